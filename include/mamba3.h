@@ -1,0 +1,162 @@
+/*
+ * mamba3.h -- C ABI of the MI355X (gfx950) Mamba-3 SSM scan library.
+ *
+ * The library evaluates the Mamba-3 state-space recurrence: exponential-
+ * trapezoid (second-order) discretisation with a data-dependent rotating
+ * ("complex", RoPE-trick) state, in SISO (rank 1) and MIMO (rank R) form,
+ * as a chunked parallel prefill over a prompt and as a single-token decode
+ * step.  Sources (web pages on Mamba-3, which print no equations):
+ *   lilting.ch, "Together AIがMamba-3を発表、長文推論でTransformer比約7倍の速度と
+ *   複素数値SSM", section "アーキテクチャ改善":
+ *     "1. 指数台形離散化"  -- second-order rule mixing current and previous input;
+ *     "2. 複素数値状態"    -- N real state dims = N/2 complex pairs, realised as
+ *                            block-diagonal 2x2 rotations of real vectors;
+ *     "3. MIMO SSM"        -- rank-r input/output coupling (r = 4 on the page);
+ *   same article, section "カーネル実装の多層構成": a prefill kernel and a
+ *   separate latency-oriented decode kernel.
+ *
+ * Definition computed (per batch row b and head h, for each token t):
+ *     alpha = exp(dt_t * A_h),  beta = (1 - lam_t) dt_t,  gamma = lam_t dt_t
+ *     G     = alpha h + beta sum_r x_prev[r] (x) B_prev[r]          (P x N)
+ *     h     = RotPairs(G, theta_t) + gamma sum_r x_t[r] (x) B_t[r]
+ *     y_t[r]= h C_t[r] + D_h x_t[r]
+ *     (B_prev, x_prev) = (B_t, x_t)
+ * RotPairs rotates state columns (2j, 2j+1) by theta_t[j]:
+ *     (a, b) -> (a cos - b sin, a sin + b cos).
+ * theta is the per-token angle (already scaled by dt), shared by the P rows
+ * and the R ranks; dt, lam, theta, A and D are shared by the R ranks.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP device memory of the
+ *     current device); every call is asynchronous on `stream` (a hipStream_t
+ *     passed as void*; NULL = the default stream).  Nothing synchronises.
+ *   - The caller owns every buffer.  The library allocates no device memory.
+ *   - Tensors are dense, row-major, in the layouts given below, with base
+ *     pointers aligned to 16 bytes.
+ *   - I/O dtype (x, B, C, y, B_prev, x_prev) is fp32 or bf16 as dims.io_dtype
+ *     says; dt, lam, theta, A, D and the state h are always fp32.
+ *   - Errors detectable on the host (NULL pointer, bad shape, unsupported
+ *     size, misalignment, short workspace) return a negative m3_status BEFORE
+ *     any HIP call; m3_last_error() then describes the problem.  A failed
+ *     launch returns M3_ERR_HIP.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.  No NaN/Inf checks are made.
+ */
+#ifndef MAMBA3_H
+#define MAMBA3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define M3_ABI_VERSION 1
+
+typedef enum {
+  M3_OK = 0,
+  M3_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  M3_ERR_SHAPE = -2,       /* a size is negative or zero where it must be > 0    */
+  M3_ERR_DTYPE = -3,       /* io_dtype is not one of m3_dtype                    */
+  M3_ERR_ALIGN = -4,       /* a tensor base pointer is not 16-byte aligned       */
+  M3_ERR_UNSUPPORTED = -5, /* sizes valid but outside the compiled set (below)   */
+  M3_ERR_WORKSPACE = -6,   /* workspace smaller than the required size           */
+  M3_ERR_HIP = -7          /* a HIP launch or runtime call failed                */
+} m3_status;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
+
+/* Problem sizes.  Supported set:
+ *   batch >= 1, heads >= 1 (batch*heads < 2^31 / 1024),
+ *   headdim P in {16, 32, 64, 128},
+ *   dstate  N in {16, 32, 64, 128}  (N/2 complex pairs),
+ *   rank    R in {1, 2, 4}          (1 = SISO, >1 = MIMO),
+ *   chunk   Q in {16, 32, 64}       (prefill block length; Q*R <= 256),
+ *   io_dtype in m3_dtype.
+ * Anything else returns M3_ERR_UNSUPPORTED (or M3_ERR_SHAPE for values <= 0). */
+typedef struct {
+  int32_t batch, heads, headdim, dstate, rank, chunk;
+  int32_t io_dtype;
+} m3_dims;
+
+/* Recurrent state of every (batch, head), in the LAB frame (the frame of the
+ * definition above; no accumulated rotation is folded in):
+ *   h       fp32      (batch, heads, P, N)
+ *   B_prev  io dtype  (batch, heads, R, N)   last token's B  (pending input)
+ *   x_prev  io dtype  (batch, heads, R, P)   last token's x
+ * A fresh sequence is all zeros (m3_state_zero). */
+typedef struct {
+  float* h;
+  void* B_prev;
+  void* x_prev;
+} m3_state;
+
+/* ABI version (M3_ABI_VERSION). */
+int m3_abi_version(void);
+
+/* Thread-local, NUL-terminated description of the last non-OK status returned
+ * on this thread (empty string if none).  Owned by the library. */
+const char* m3_last_error(void);
+
+/* Host only.  Byte sizes of the three state buffers for `dims`.  Any output
+ * pointer may be NULL. */
+int m3_state_bytes(const m3_dims* dims, size_t* h_bytes, size_t* bprev_bytes,
+                   size_t* xprev_bytes);
+
+/* Zero the whole state (h, B_prev, x_prev): the start of a fresh sequence.
+ * Uses a fill kernel (no memset node), so it may be captured in a HIP graph. */
+int m3_state_zero(const m3_dims* dims, m3_state* state, void* stream);
+
+/* Copy a state from caller buffers (same layouts as m3_state) into `dst`.
+ * Source and destination must not overlap. */
+int m3_state_load(const m3_dims* dims, m3_state* dst, const float* h,
+                  const void* B_prev, const void* x_prev, void* stream);
+
+/* Copy `src` out into caller buffers (same layouts).  Must not overlap. */
+int m3_state_readout(const m3_dims* dims, const m3_state* src, float* h,
+                     void* B_prev, void* x_prev, void* stream);
+
+/* Host only.  Workspace bytes that mamba3_prefill needs for (dims, seqlen).
+ * 0 when the prompt is processed by one fused pass; >0 when the library
+ * splits long prompts of few (batch, head) chains into segments whose start
+ * states are found by a scan over segment summaries. */
+int mamba3_prefill_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* bytes);
+
+/* Chunked parallel prefill of `seqlen` tokens for every (batch, head).
+ *   x      io    (batch, seqlen, heads, R, P)
+ *   B, C   io    (batch, seqlen, heads, R, N)
+ *   dt     fp32  (batch, seqlen, heads)
+ *   lam    fp32  (batch, seqlen, heads)
+ *   theta  fp32  (batch, seqlen, heads, N/2)   per-token angles (scaled by dt)
+ *   A, D   fp32  (heads)
+ *   state  in: the state before the prompt; out: the state after it (in place)
+ *   y      io    (batch, seqlen, heads, R, P)   output; must not alias inputs
+ *   workspace / workspace_bytes: device scratch of at least
+ *     mamba3_prefill_workspace_bytes(dims, seqlen) bytes (may be NULL if 0).
+ * seqlen == 0 is a no-op that returns M3_OK.  Results match the sequential
+ * definition up to rounding: fp32 state and accumulation; with bf16 I/O the
+ * rotated B/C, the masked score tile and the carried state are rounded to
+ * bf16 as matrix-core operands. */
+int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const void* B,
+                   const void* C, const float* dt, const float* lam, const float* theta,
+                   const float* A, const float* D, m3_state* state, void* y,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* One recurrent step: one new token for every (batch, head).
+ *   x      io    (batch, heads, R, P)
+ *   B, C   io    (batch, heads, R, N)
+ *   dt, lam fp32 (batch, heads);  theta fp32 (batch, heads, N/2)
+ *   A, D   fp32  (heads)
+ *   state  updated in place (h streamed once: read once, written once)
+ *   y      io    (batch, heads, R, P); must not alias inputs or state.
+ * dims.chunk is ignored. */
+int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const void* C,
+                       const float* dt, const float* lam, const float* theta,
+                       const float* A, const float* D, m3_state* state, void* y,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA3_H */

@@ -1,0 +1,260 @@
+"""Python binding of libmamba3.so (ctypes).  Argument marshalling only.
+
+Every function has the name of the C entry point it calls (include/mamba3.h)
+and takes torch tensors on the GPU; it checks dtype, device, contiguity and
+shape, passes raw device pointers plus the current HIP stream, and raises
+M3Error on a non-zero status.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback of any kind: if the library is
+missing, importing the functions raises.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmamba3.so")
+
+M3_OK = 0
+M3_ERR_NULL = -1
+M3_ERR_SHAPE = -2
+M3_ERR_DTYPE = -3
+M3_ERR_ALIGN = -4
+M3_ERR_UNSUPPORTED = -5
+M3_ERR_WORKSPACE = -6
+M3_ERR_HIP = -7
+M3_F32 = 0
+M3_BF16 = 1
+
+STATUS_NAMES = {
+    M3_OK: "M3_OK", M3_ERR_NULL: "M3_ERR_NULL", M3_ERR_SHAPE: "M3_ERR_SHAPE",
+    M3_ERR_DTYPE: "M3_ERR_DTYPE", M3_ERR_ALIGN: "M3_ERR_ALIGN",
+    M3_ERR_UNSUPPORTED: "M3_ERR_UNSUPPORTED", M3_ERR_WORKSPACE: "M3_ERR_WORKSPACE",
+    M3_ERR_HIP: "M3_ERR_HIP",
+}
+
+EXPORTED = (
+    "m3_abi_version", "m3_last_error", "m3_state_bytes", "m3_state_zero", "m3_state_load",
+    "m3_state_readout", "mamba3_prefill_workspace_bytes", "mamba3_prefill", "mamba3_decode_step",
+)
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class m3_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32)]
+
+
+class m3_state(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("B_prev", ctypes.c_void_p), ("x_prev", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmamba3.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m state_space_sequence_prefill_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D, S = ctypes.POINTER(m3_dims), ctypes.POINTER(m3_state)
+        L.m3_abi_version.restype = ctypes.c_int
+        L.m3_abi_version.argtypes = []
+        L.m3_last_error.restype = ctypes.c_char_p
+        L.m3_last_error.argtypes = []
+        L.m3_state_bytes.restype = ctypes.c_int
+        L.m3_state_bytes.argtypes = [D, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.m3_state_zero.restype = ctypes.c_int
+        L.m3_state_zero.argtypes = [D, S, vp]
+        L.m3_state_load.restype = ctypes.c_int
+        L.m3_state_load.argtypes = [D, S, vp, vp, vp, vp]
+        L.m3_state_readout.restype = ctypes.c_int
+        L.m3_state_readout.argtypes = [D, S, vp, vp, vp, vp]
+        L.mamba3_prefill_workspace_bytes.restype = ctypes.c_int
+        L.mamba3_prefill_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(sz)]
+        L.mamba3_prefill.restype = ctypes.c_int
+        L.mamba3_prefill.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp, sz, vp]
+        L.mamba3_decode_step.restype = ctypes.c_int
+        L.mamba3_decode_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != M3_OK:
+        raise M3Error(status, lib().m3_last_error().decode(errors="replace"))
+
+
+def make_dims(batch, heads, headdim, dstate, rank=1, chunk=64, io_dtype="bf16"):
+    code = {"bf16": M3_BF16, "f32": M3_F32}.get(io_dtype, io_dtype)
+    return m3_dims(batch, heads, headdim, dstate, rank, chunk, code)
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_torch_dtype(dims):
+    torch = _torch()
+    return torch.bfloat16 if dims.io_dtype == M3_BF16 else torch.float32
+
+
+def _ptr(t, name, shape, dtype):
+    """Device pointer of tensor t after checking dtype, device, layout, shape."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+class State:
+    """Device state of every (batch, head): h fp32 (b,H,P,N), B_prev io (b,H,R,N),
+    x_prev io (b,H,R,P), all in the lab frame.  Plain torch tensors; ``c_struct``
+    gives the m3_state the C calls take."""
+
+    def __init__(self, dims, h, B_prev, x_prev):
+        self.dims = dims
+        self.h, self.B_prev, self.x_prev = h, B_prev, x_prev
+        d = dims
+        _ptr(h, "h", (d.batch, d.heads, d.headdim, d.dstate), _torch().float32)
+        _ptr(B_prev, "B_prev", (d.batch, d.heads, d.rank, d.dstate), _io_torch_dtype(d))
+        _ptr(x_prev, "x_prev", (d.batch, d.heads, d.rank, d.headdim), _io_torch_dtype(d))
+
+    @classmethod
+    def empty(cls, dims, device="cuda"):
+        torch = _torch()
+        d = dims
+        io = _io_torch_dtype(d)
+        return cls(d,
+                   torch.empty((d.batch, d.heads, d.headdim, d.dstate), dtype=torch.float32, device=device),
+                   torch.empty((d.batch, d.heads, d.rank, d.dstate), dtype=io, device=device),
+                   torch.empty((d.batch, d.heads, d.rank, d.headdim), dtype=io, device=device))
+
+    def c_struct(self):
+        return m3_state(self.h.data_ptr(), self.B_prev.data_ptr(), self.x_prev.data_ptr())
+
+
+def m3_abi_version():
+    return lib().m3_abi_version()
+
+
+def m3_last_error():
+    return lib().m3_last_error().decode(errors="replace")
+
+
+def m3_state_bytes(dims):
+    hb, bb, xb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().m3_state_bytes(ctypes.byref(dims), ctypes.byref(hb), ctypes.byref(bb), ctypes.byref(xb)))
+    return hb.value, bb.value, xb.value
+
+
+def m3_state_zero(dims, state, stream=None):
+    cs = state.c_struct()
+    _check(lib().m3_state_zero(ctypes.byref(dims), ctypes.byref(cs), _stream(stream)))
+
+
+def m3_state_load(dims, dst, h, B_prev, x_prev, stream=None):
+    d = dims
+    io = _io_torch_dtype(d)
+    ph = _ptr(h, "h", (d.batch, d.heads, d.headdim, d.dstate), _torch().float32)
+    pb = _ptr(B_prev, "B_prev", (d.batch, d.heads, d.rank, d.dstate), io)
+    px = _ptr(x_prev, "x_prev", (d.batch, d.heads, d.rank, d.headdim), io)
+    cs = dst.c_struct()
+    _check(lib().m3_state_load(ctypes.byref(d), ctypes.byref(cs), ph, pb, px, _stream(stream)))
+
+
+def m3_state_readout(dims, src, h, B_prev, x_prev, stream=None):
+    d = dims
+    io = _io_torch_dtype(d)
+    ph = _ptr(h, "h", (d.batch, d.heads, d.headdim, d.dstate), _torch().float32)
+    pb = _ptr(B_prev, "B_prev", (d.batch, d.heads, d.rank, d.dstate), io)
+    px = _ptr(x_prev, "x_prev", (d.batch, d.heads, d.rank, d.headdim), io)
+    cs = src.c_struct()
+    _check(lib().m3_state_readout(ctypes.byref(d), ctypes.byref(cs), ph, pb, px, _stream(stream)))
+
+
+def mamba3_prefill_workspace_bytes(dims, seqlen):
+    n = ctypes.c_size_t()
+    _check(lib().mamba3_prefill_workspace_bytes(ctypes.byref(dims), int(seqlen), ctypes.byref(n)))
+    return n.value
+
+
+def mamba3_prefill(dims, seqlen, x, B, C, dt, lam, theta, A, D, state, y, workspace=None, stream=None):
+    """Chunked prefill of `seqlen` tokens; `state` (State) is updated in place,
+    `y` receives the outputs.  `workspace` is a uint8 GPU tensor of at least
+    mamba3_prefill_workspace_bytes(dims, seqlen) bytes (or None when that is 0)."""
+    torch = _torch()
+    d = dims
+    io = _io_torch_dtype(d)
+    T, Hh, R, P, N = int(seqlen), d.heads, d.rank, d.headdim, d.dstate
+    f32 = torch.float32
+    args = [
+        _ptr(x, "x", (d.batch, T, Hh, R, P), io),
+        _ptr(B, "B", (d.batch, T, Hh, R, N), io),
+        _ptr(C, "C", (d.batch, T, Hh, R, N), io),
+        _ptr(dt, "dt", (d.batch, T, Hh), f32),
+        _ptr(lam, "lam", (d.batch, T, Hh), f32),
+        _ptr(theta, "theta", (d.batch, T, Hh, N // 2), f32),
+        _ptr(A, "A", (Hh,), f32),
+        _ptr(D, "D", (Hh,), f32),
+    ]
+    py = _ptr(y, "y", (d.batch, T, Hh, R, P), io)
+    ws, wsb = None, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    cs = state.c_struct()
+    _check(lib().mamba3_prefill(ctypes.byref(d), T, *args, ctypes.byref(cs), py, ws, wsb, _stream(stream)))
+
+
+def mamba3_decode_step(dims, x, B, C, dt, lam, theta, A, D, state, y, stream=None):
+    """One decode step for every (batch, head); `state` is updated in place."""
+    torch = _torch()
+    d = dims
+    io = _io_torch_dtype(d)
+    Hh, R, P, N = d.heads, d.rank, d.headdim, d.dstate
+    f32 = torch.float32
+    args = [
+        _ptr(x, "x", (d.batch, Hh, R, P), io),
+        _ptr(B, "B", (d.batch, Hh, R, N), io),
+        _ptr(C, "C", (d.batch, Hh, R, N), io),
+        _ptr(dt, "dt", (d.batch, Hh), f32),
+        _ptr(lam, "lam", (d.batch, Hh), f32),
+        _ptr(theta, "theta", (d.batch, Hh, N // 2), f32),
+        _ptr(A, "A", (Hh,), f32),
+        _ptr(D, "D", (Hh,), f32),
+    ]
+    py = _ptr(y, "y", (d.batch, Hh, R, P), io)
+    cs = state.c_struct()
+    _check(lib().mamba3_decode_step(ctypes.byref(d), *args, ctypes.byref(cs), py, _stream(stream)))

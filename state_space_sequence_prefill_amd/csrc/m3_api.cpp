@@ -1,0 +1,298 @@
+// C ABI of the Mamba-3 scan library: argument validation and dispatch.
+//
+// Every host-detectable problem is reported with a negative m3_status before
+// any HIP call is made, so the whole validation layer runs (and is tested)
+// on machines without a GPU.  See include/mamba3.h for the contract.
+#include "../../include/mamba3.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "m3_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return M3_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t io_size(const m3_dims* d) { return d->io_dtype == M3_BF16 ? 2 : 4; }
+
+// Shape / dtype / support checks shared by every entry point.  `need_chunk`
+// is false for the decode step (which ignores dims.chunk).
+int check_dims(const m3_dims* d, bool need_chunk, m3::Dims* out) {
+  if (!d) return fail(M3_ERR_NULL, "dims is NULL");
+  if (d->batch <= 0 || d->heads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->rank <= 0)
+    return fail(M3_ERR_SHAPE, "batch, heads, headdim, dstate and rank must be > 0 (got %d %d %d %d %d)",
+                d->batch, d->heads, d->headdim, d->dstate, d->rank);
+  if (need_chunk && d->chunk <= 0) return fail(M3_ERR_SHAPE, "chunk must be > 0 (got %d)", d->chunk);
+  if (d->io_dtype != M3_F32 && d->io_dtype != M3_BF16)
+    return fail(M3_ERR_DTYPE, "io_dtype %d is neither M3_F32 nor M3_BF16", d->io_dtype);
+  if ((int64_t)d->batch * d->heads > (int64_t)(1 << 21))
+    return fail(M3_ERR_UNSUPPORTED, "batch*heads = %lld exceeds 2^21",
+                (long long)((int64_t)d->batch * d->heads));
+  if (d->dstate % 2) return fail(M3_ERR_UNSUPPORTED, "dstate %d is odd (N/2 complex pairs)", d->dstate);
+  m3::Dims m;
+  m.batch = d->batch;
+  m.heads = d->heads;
+  m.P = d->headdim;
+  m.N = d->dstate;
+  m.R = d->rank;
+  m.Q = need_chunk ? d->chunk : 64;
+  m.bf16 = d->io_dtype == M3_BF16;
+  const bool supported = need_chunk ? m3::prefill_supported(m) : m3::decode_supported(m);
+  if (!supported)
+    return fail(M3_ERR_UNSUPPORTED,
+                "unsupported sizes headdim=%d dstate=%d rank=%d chunk=%d (supported: headdim in "
+                "{16,32,64,128}, dstate in {16,32,64,128}, rank in {1,2,4}, chunk in {16,32,64}, "
+                "chunk*rank <= 256)",
+                d->headdim, d->dstate, d->rank, d->chunk);
+  *out = m;
+  return M3_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(M3_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(M3_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return M3_OK;
+}
+
+int check_state(const m3_state* s, const char* what) {
+  if (!s) return fail(M3_ERR_NULL, "%s is NULL", what);
+  int st;
+  if ((st = check_ptr(s->h, "state.h")) != M3_OK) return st;
+  if ((st = check_ptr(s->B_prev, "state.B_prev")) != M3_OK) return st;
+  if ((st = check_ptr(s->x_prev, "state.x_prev")) != M3_OK) return st;
+  return M3_OK;
+}
+
+void state_sizes(const m3_dims* d, size_t* hb, size_t* bb, size_t* xb) {
+  const size_t chains = (size_t)d->batch * d->heads;
+  *hb = chains * d->headdim * d->dstate * sizeof(float);
+  *bb = chains * d->rank * d->dstate * io_size(d);
+  *xb = chains * d->rank * d->headdim * io_size(d);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(M3_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Segment plan for the prefill.  Chains (batch*heads) that already fill the
+// chip run one fused pass.  Few long chains are split into nseg segments so
+// that about 256 workgroups (one per MI355X compute unit) run at once; each
+// segment keeps at least 4 chunks.  Deterministic in (dims, seqlen) only.
+constexpr int kTargetWorkgroups = 256;
+constexpr int kMinSegChunks = 4;
+constexpr int kMaxSegments = 64;
+
+void plan_segments(const m3::Dims& m, int seqlen, int* nseg, int* seg_chunks) {
+  const int nchunks = (seqlen + m.Q - 1) / m.Q;
+  const int chains = m.batch * m.heads;
+  int g = 1;
+  if (chains < kTargetWorkgroups / 2) {
+    g = (kTargetWorkgroups + chains - 1) / chains;
+    if (g > kMaxSegments) g = kMaxSegments;
+    const int gmax = nchunks / kMinSegChunks;
+    if (g > gmax) g = gmax;
+    if (g < 1) g = 1;
+  }
+  if (g == 1) {
+    *nseg = 1;
+    *seg_chunks = nchunks;
+    return;
+  }
+  const int sc = (nchunks + g - 1) / g;
+  *seg_chunks = sc;
+  *nseg = (nchunks + sc - 1) / sc;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace layout for the segment path: seg_state | seg_decay | seg_angle.
+size_t workspace_for(const m3::Dims& m, int nseg) {
+  if (nseg <= 1) return 0;
+  const size_t cs = (size_t)nseg * m.batch * m.heads;
+  return align256(cs * m.P * m.N * sizeof(float)) + align256(cs * sizeof(float)) +
+         align256(cs * (m.N / 2) * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int m3_abi_version(void) { return M3_ABI_VERSION; }
+
+const char* m3_last_error(void) { return g_err; }
+
+int m3_state_bytes(const m3_dims* dims, size_t* h_bytes, size_t* bprev_bytes, size_t* xprev_bytes) {
+  m3::Dims m;
+  int st = check_dims(dims, false, &m);
+  if (st != M3_OK) return st;
+  size_t hb, bb, xb;
+  state_sizes(dims, &hb, &bb, &xb);
+  if (h_bytes) *h_bytes = hb;
+  if (bprev_bytes) *bprev_bytes = bb;
+  if (xprev_bytes) *xprev_bytes = xb;
+  return ok();
+}
+
+int m3_state_zero(const m3_dims* dims, m3_state* state, void* stream) {
+  m3::Dims m;
+  int st = check_dims(dims, false, &m);
+  if (st != M3_OK) return st;
+  if ((st = check_state(state, "state")) != M3_OK) return st;
+  size_t hb, bb, xb;
+  state_sizes(dims, &hb, &bb, &xb);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = m3::launch_fill_zero(state->h, hb, s);
+  if (e == hipSuccess) e = m3::launch_fill_zero(state->B_prev, bb, s);
+  if (e == hipSuccess) e = m3::launch_fill_zero(state->x_prev, xb, s);
+  return hip_status(e, "m3_state_zero");
+}
+
+int m3_state_load(const m3_dims* dims, m3_state* dst, const float* h, const void* B_prev,
+                  const void* x_prev, void* stream) {
+  m3::Dims m;
+  int st = check_dims(dims, false, &m);
+  if (st != M3_OK) return st;
+  if ((st = check_state(dst, "dst")) != M3_OK) return st;
+  if ((st = check_ptr(h, "h")) != M3_OK) return st;
+  if ((st = check_ptr(B_prev, "B_prev")) != M3_OK) return st;
+  if ((st = check_ptr(x_prev, "x_prev")) != M3_OK) return st;
+  size_t hb, bb, xb;
+  state_sizes(dims, &hb, &bb, &xb);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = m3::launch_copy(dst->h, h, hb, s);
+  if (e == hipSuccess) e = m3::launch_copy(dst->B_prev, B_prev, bb, s);
+  if (e == hipSuccess) e = m3::launch_copy(dst->x_prev, x_prev, xb, s);
+  return hip_status(e, "m3_state_load");
+}
+
+int m3_state_readout(const m3_dims* dims, const m3_state* src, float* h, void* B_prev, void* x_prev,
+                     void* stream) {
+  m3::Dims m;
+  int st = check_dims(dims, false, &m);
+  if (st != M3_OK) return st;
+  if ((st = check_state(src, "src")) != M3_OK) return st;
+  if ((st = check_ptr(h, "h")) != M3_OK) return st;
+  if ((st = check_ptr(B_prev, "B_prev")) != M3_OK) return st;
+  if ((st = check_ptr(x_prev, "x_prev")) != M3_OK) return st;
+  size_t hb, bb, xb;
+  state_sizes(dims, &hb, &bb, &xb);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = m3::launch_copy(h, src->h, hb, s);
+  if (e == hipSuccess) e = m3::launch_copy(B_prev, src->B_prev, bb, s);
+  if (e == hipSuccess) e = m3::launch_copy(x_prev, src->x_prev, xb, s);
+  return hip_status(e, "m3_state_readout");
+}
+
+int mamba3_prefill_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* bytes) {
+  m3::Dims m;
+  int st = check_dims(dims, true, &m);
+  if (st != M3_OK) return st;
+  if (!bytes) return fail(M3_ERR_NULL, "bytes is NULL");
+  if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
+  int nseg = 1, sc = 0;
+  if (seqlen > 0) plan_segments(m, seqlen, &nseg, &sc);
+  *bytes = workspace_for(m, nseg);
+  return ok();
+}
+
+int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                   const float* dt, const float* lam, const float* theta, const float* A,
+                   const float* D, m3_state* state, void* y, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  m3::Dims m;
+  int st = check_dims(dims, true, &m);
+  if (st != M3_OK) return st;
+  if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
+  if ((st = check_state(state, "state")) != M3_OK) return st;
+  if (seqlen == 0) return ok();
+  if ((int64_t)seqlen * m.batch * m.heads * m.R * (m.N > m.P ? m.N : m.P) > ((int64_t)1 << 40))
+    return fail(M3_ERR_UNSUPPORTED, "problem too large for 40-bit element offsets");
+  const void* ptrs[] = {x, B, C, dt, lam, theta, A, D, y};
+  const char* names[] = {"x", "B", "C", "dt", "lam", "theta", "A", "D", "y"};
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_ptr(ptrs[i], names[i])) != M3_OK) return st;
+  int nseg = 1, sc = 0;
+  plan_segments(m, seqlen, &nseg, &sc);
+  const size_t need = workspace_for(m, nseg);
+  if (need > 0) {
+    if (workspace_bytes < need)
+      return fail(M3_ERR_WORKSPACE, "workspace of %zu bytes < required %zu", workspace_bytes, need);
+    if ((st = check_ptr(workspace, "workspace")) != M3_OK) return st;
+  }
+  m3::PrefillArgs a;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt = dt;
+  a.lam = lam;
+  a.theta = theta;
+  a.A = A;
+  a.D = D;
+  a.h = state->h;
+  a.B_prev = state->B_prev;
+  a.x_prev = state->x_prev;
+  a.y = y;
+  a.seqlen = seqlen;
+  a.nseg = nseg;
+  a.seg_chunks = sc;
+  a.seg_state = nullptr;
+  a.seg_decay = nullptr;
+  a.seg_angle = nullptr;
+  if (nseg > 1) {
+    const size_t cs = (size_t)nseg * m.batch * m.heads;
+    char* w = static_cast<char*>(workspace);
+    a.seg_state = reinterpret_cast<float*>(w);
+    w += align256(cs * m.P * m.N * sizeof(float));
+    a.seg_decay = reinterpret_cast<float*>(w);
+    w += align256(cs * sizeof(float));
+    a.seg_angle = reinterpret_cast<float*>(w);
+  }
+  return hip_status(m3::launch_prefill(m, a, static_cast<hipStream_t>(stream)), "mamba3_prefill");
+}
+
+int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const void* C,
+                       const float* dt, const float* lam, const float* theta, const float* A,
+                       const float* D, m3_state* state, void* y, void* stream) {
+  m3::Dims m;
+  int st = check_dims(dims, false, &m);
+  if (st != M3_OK) return st;
+  if ((st = check_state(state, "state")) != M3_OK) return st;
+  const void* ptrs[] = {x, B, C, dt, lam, theta, A, D, y};
+  const char* names[] = {"x", "B", "C", "dt", "lam", "theta", "A", "D", "y"};
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_ptr(ptrs[i], names[i])) != M3_OK) return st;
+  m3::DecodeArgs a;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt = dt;
+  a.lam = lam;
+  a.theta = theta;
+  a.A = A;
+  a.D = D;
+  a.h = state->h;
+  a.B_prev = state->B_prev;
+  a.x_prev = state->x_prev;
+  a.y = y;
+  return hip_status(m3::launch_decode(m, a, static_cast<hipStream_t>(stream)), "mamba3_decode_step");
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side helpers shared by the gfx950 kernels of the Mamba-3 scan library.
+//
+// Storage types: I/O tensors are either fp32 (float) or bf16 (__bf16, bit
+// pattern of the upper half of an fp32).  All arithmetic is fp32; conversions
+// to bf16 round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// Load 4 consecutive I/O elements (16 B for fp32, 8 B for bf16) as fp32.
+__device__ __forceinline__ void load4(const float* p, float (&o)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float (&o)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+// Store 4 fp32 values as 4 consecutive I/O elements.
+__device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16* p, const float (&v)[4]) {
+  bf16x4 o;
+  o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+
+// Pair rotation by (c, s): (a, b) -> (a c - b s, a s + b c).
+__device__ __forceinline__ void rot2(float& a, float& b, float c, float s) {
+  const float na = a * c - b * s;
+  const float nb = a * s + b * c;
+  a = na;
+  b = nb;
+}
+
+// Lane-crossing helpers (wave64).
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+__device__ __forceinline__ float shfl_up(float v, int d) { return __shfl_up(v, d, kWave); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const float u = shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+}  // namespace m3

@@ -1,0 +1,63 @@
+// Internal launch interface between the C ABI (m3_api.cpp) and the gfx950
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3 {
+
+struct Dims {
+  int batch, heads, P, N, R, Q;
+  bool bf16;
+};
+
+// Arguments of one decode step (see mamba3_decode_step in include/mamba3.h).
+struct DecodeArgs {
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* theta;
+  const float* A;
+  const float* D;
+  float* h;
+  void* B_prev;
+  void* x_prev;
+  void* y;
+};
+
+// Arguments of one prefill pass over tokens [0, seqlen) of every chain.
+struct PrefillArgs {
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* theta;
+  const float* A;
+  const float* D;
+  float* h;       // lab-frame state (batch, heads, P, N), in/out
+  void* B_prev;   // pending B (batch, heads, R, N), in/out
+  void* x_prev;   // pending x (batch, heads, R, P), in/out
+  void* y;
+  int seqlen;
+  // Segment path (long prompts, few chains).  nseg == 1: plain fused pass.
+  int nseg;        // number of segments the sequence is split into
+  int seg_chunks;  // chunks per segment (the last segment may be shorter)
+  float* seg_state;   // (nseg, batch, heads, P, N) fp32: per-segment summaries / start states
+  float* seg_decay;   // (nseg, batch, heads) fp32: log of the segment's total decay
+  float* seg_angle;   // (nseg, batch, heads, N/2) fp32: the segment's total angle
+};
+
+hipError_t launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prefill(const Dims& d, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+bool decode_supported(const Dims& d);
+bool prefill_supported(const Dims& d);
+
+}  // namespace m3

@@ -1,0 +1,182 @@
+"""C-ABI tests that run without a GPU.
+
+The library must load, export every function that include/mamba3.h
+declares, and reject every host-detectable problem with the documented
+status before it makes any HIP call (so these tests never touch a device).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from state_space_sequence_prefill_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba3.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libmamba3.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:m3|mamba3)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version():
+    assert B.m3_abi_version() == 1
+
+
+def dims(**kw):
+    base = dict(batch=2, heads=3, headdim=64, dstate=64, rank=1, chunk=64, io_dtype="bf16")
+    base.update(kw)
+    return B.make_dims(**base)
+
+
+FAKE = 0x10000  # a 16-byte aligned non-NULL address; never dereferenced on the host
+
+
+def fake_state():
+    return B.m3_state(FAKE, FAKE, FAKE)
+
+
+def call_prefill(d, seqlen=16, ptrs=None, state=None, ws=None, wsb=0):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    st = fake_state() if state is None else state
+    return B.lib().mamba3_prefill(ctypes.byref(d), seqlen, *p[:8], ctypes.byref(st), p[8], ws, wsb, None)
+
+
+def call_decode(d, ptrs=None, state=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    st = fake_state() if state is None else state
+    return B.lib().mamba3_decode_step(ctypes.byref(d), *p[:8], ctypes.byref(st), p[8], None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, B.M3_ERR_SHAPE), ("heads", -1, B.M3_ERR_SHAPE), ("headdim", 0, B.M3_ERR_SHAPE),
+    ("dstate", 0, B.M3_ERR_SHAPE), ("rank", 0, B.M3_ERR_SHAPE), ("chunk", 0, B.M3_ERR_SHAPE),
+    ("io_dtype", 7, B.M3_ERR_DTYPE), ("dstate", 15, B.M3_ERR_UNSUPPORTED),
+    ("dstate", 256, B.M3_ERR_UNSUPPORTED), ("headdim", 48, B.M3_ERR_UNSUPPORTED),
+    ("rank", 3, B.M3_ERR_UNSUPPORTED), ("rank", 8, B.M3_ERR_UNSUPPORTED),
+    ("chunk", 128, B.M3_ERR_UNSUPPORTED), ("chunk", 24, B.M3_ERR_UNSUPPORTED),
+])
+def test_prefill_rejects_bad_dims(field, value, status):
+    d = dims(**{field: value})
+    assert call_prefill(d) == status
+    assert B.m3_last_error()
+
+
+def test_prefill_lds_limit_is_unsupported():
+    # fp32 I/O with N = 128 and a 64-token chunk does not fit 160 KiB of LDS
+    assert call_prefill(dims(io_dtype="f32", dstate=128, chunk=64)) == B.M3_ERR_UNSUPPORTED
+    assert call_prefill(dims(rank=4, chunk=64, dstate=128)) == B.M3_ERR_UNSUPPORTED
+
+
+def test_decode_checks_dims():
+    assert call_decode(dims(dstate=15)) == B.M3_ERR_UNSUPPORTED
+    assert call_decode(dims(rank=3)) == B.M3_ERR_UNSUPPORTED
+    assert call_decode(dims(io_dtype=5)) == B.M3_ERR_DTYPE
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_prefill_rejects_null_pointer(i):
+    p = [FAKE] * 9
+    p[i] = None
+    assert call_prefill(dims(), ptrs=p) == B.M3_ERR_NULL
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_decode_rejects_null_pointer(i):
+    p = [FAKE] * 9
+    p[i] = None
+    assert call_decode(dims(), ptrs=p) == B.M3_ERR_NULL
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_prefill_rejects_misaligned_pointer(i):
+    p = [FAKE] * 9
+    p[i] = FAKE + 4
+    assert call_prefill(dims(), ptrs=p) == B.M3_ERR_ALIGN
+
+
+@pytest.mark.parametrize("which", ["h", "B_prev", "x_prev"])
+def test_state_pointer_checks(which):
+    st = fake_state()
+    setattr(st, which, None)
+    assert call_prefill(dims(), state=st) == B.M3_ERR_NULL
+    assert call_decode(dims(), state=st) == B.M3_ERR_NULL
+    st = fake_state()
+    setattr(st, which, FAKE + 8)
+    assert call_prefill(dims(), state=st) == B.M3_ERR_ALIGN
+
+
+def test_null_state_and_dims():
+    d = dims()
+    p = [FAKE] * 9
+    assert B.lib().mamba3_prefill(None, 4, *p[:8], ctypes.byref(fake_state()), p[8], None, 0, None) == B.M3_ERR_NULL
+    assert B.lib().mamba3_prefill(ctypes.byref(d), 4, *p[:8], None, p[8], None, 0, None) == B.M3_ERR_NULL
+
+
+def test_negative_seqlen():
+    assert call_prefill(dims(), seqlen=-1) == B.M3_ERR_SHAPE
+
+
+def test_zero_seqlen_is_a_noop_before_any_hip_call():
+    # no kernel is launched for an empty prompt; input pointers may be NULL
+    assert call_prefill(dims(), seqlen=0, ptrs=[None] * 9) == B.M3_OK
+
+
+def test_state_bytes():
+    d = dims(batch=8, heads=32, headdim=64, dstate=128, rank=1)
+    assert B.m3_state_bytes(d) == (8 * 32 * 64 * 128 * 4, 8 * 32 * 128 * 2, 8 * 32 * 64 * 2)
+    d = dims(batch=256, heads=32, headdim=64, dstate=64, rank=4, io_dtype="f32")
+    assert B.m3_state_bytes(d) == (256 * 32 * 64 * 64 * 4, 256 * 32 * 4 * 64 * 4, 256 * 32 * 4 * 64 * 4)
+
+
+def test_workspace_plan():
+    # many chains: one fused pass, no workspace
+    assert B.mamba3_prefill_workspace_bytes(dims(batch=8, heads=32, dstate=128), 4096) == 0
+    # few long chains: segment summaries
+    n = B.mamba3_prefill_workspace_bytes(dims(batch=1, heads=32, dstate=128), 16384)
+    assert n >= 8 * 32 * 64 * 128 * 4
+    # short prompt of few chains: not worth splitting
+    assert B.mamba3_prefill_workspace_bytes(dims(batch=1, heads=2), 64 * 3) == 0
+    assert B.mamba3_prefill_workspace_bytes(dims(batch=1, heads=2), 0) == 0
+
+
+def test_short_workspace_is_rejected():
+    d = dims(batch=1, heads=32, dstate=128)
+    need = B.mamba3_prefill_workspace_bytes(d, 16384)
+    assert call_prefill(d, seqlen=16384, ws=FAKE, wsb=need - 1) == B.M3_ERR_WORKSPACE
+    assert call_prefill(d, seqlen=16384, ws=None, wsb=need) == B.M3_ERR_NULL
+    assert call_prefill(d, seqlen=16384, ws=FAKE + 4, wsb=need) == B.M3_ERR_ALIGN
+
+
+def test_state_ops_validate():
+    d = dims()
+    st = fake_state()
+    assert B.lib().m3_state_zero(ctypes.byref(d), None, None) == B.M3_ERR_NULL
+    assert B.lib().m3_state_load(ctypes.byref(d), ctypes.byref(st), None, FAKE, FAKE, None) == B.M3_ERR_NULL
+    assert B.lib().m3_state_readout(ctypes.byref(d), ctypes.byref(st), FAKE, FAKE + 2, FAKE, None) == B.M3_ERR_ALIGN
+    bad = dims(dstate=7)
+    assert B.lib().m3_state_zero(ctypes.byref(bad), ctypes.byref(st), None) == B.M3_ERR_UNSUPPORTED
+
+
+def test_last_error_is_cleared_by_success():
+    call_prefill(dims(dstate=15))
+    assert "odd" in B.m3_last_error()
+    B.m3_state_bytes(dims())
+    assert B.m3_last_error() == ""

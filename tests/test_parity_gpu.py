@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: relative L2 error <= 2e-2 for bf16 I/O and <= 1e-5 for fp32 I/O, on y
+and on the final state h; the pending pair (B_prev, x_prev) is a raw copy and
+must be bit-exact.  Small cases compare whole tensors; the full-size
+workloads compare a seeded sample of (batch, head) chains that the oracle
+recomputes sequentially.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from state_space_sequence_prefill_amd import synthetic as syn
+
+from m3_testlib import (exact_state, inputs_on_gpu, oracle_args, relerr, state_slice, state_to_gpu,
+                        to_np, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import state_space_sequence_prefill_amd as m3  # noqa: E402
+
+
+def W(name, **kw):
+    return syn.WORKLOADS[name].with_(**kw)
+
+
+def dims_of(w):
+    return m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype)
+
+
+def run_prefill(w, tt, state, seqlen=None):
+    d = dims_of(w)
+    T = w.seqlen if seqlen is None else seqlen
+    y = torch.empty((w.batch, T, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
+    nws = m3.mamba3_prefill_workspace_bytes(d, T)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+    m3.mamba3_prefill(d, T, tt["x"], tt["B"], tt["C"], tt["dt"], tt["lam"], tt["theta"], tt["A"], tt["D"],
+                      state, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def make_state(w, st=None):
+    d = dims_of(w)
+    s = m3.State.empty(d)
+    if st is None:
+        m3.m3_state_zero(d, s)
+    else:
+        h, Bp, xp = state_to_gpu(st, w.io_dtype)
+        m3.m3_state_load(d, s, h, Bp, xp)
+    return s
+
+
+def check_prefill(w, seed, pairs=None, st=None, long_memory=False, zero_D=False, tol=None):
+    ex, tt = inputs_on_gpu(w, seed, long_memory=long_memory, zero_D=zero_D)
+    s = make_state(w, st)
+    y = run_prefill(w, tt, s)
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    st_ex = exact_state(st, w.io_dtype) if st is not None else oracle.zero_state(
+        w.batch, w.heads, w.headdim, w.dstate, w.rank)
+    args = oracle_args(ex, pairs)
+    y_ref, (h_ref, bp_ref, xp_ref) = oracle.prefill(**args, state=state_slice(st_ex, pairs))
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    y_gpu = np.moveaxis(to_np(y)[bs, :, hs], 0, 1)[None]
+    tol = tol_for(w.io_dtype) if tol is None else tol
+    ey = relerr(y_gpu, y_ref)
+    eh = relerr(to_np(s.h)[bs, hs][None], h_ref)
+    print(f"[{w.name} seed={seed} T={w.seqlen} Q={w.chunk}] rel-L2 y={ey:.3e} h={eh:.3e}", flush=True)
+    assert ey <= tol, ey
+    assert eh <= tol, eh
+    assert np.array_equal(to_np(s.B_prev)[bs, hs][None], bp_ref)
+    assert np.array_equal(to_np(s.x_prev)[bs, hs][None], xp_ref)
+    return ey, eh
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def check_decode(w, seed, steps=3, pairs=None, tol=None):
+    d = dims_of(w)
+    rng_state = syn.draw_state(w, seed + 500)
+    s = make_state(w, rng_state)
+    cur = exact_state(rng_state, w.io_dtype)
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    cur = state_slice(cur, pairs)
+    tol = tol_for(w.io_dtype) if tol is None else tol
+    ex, tt = inputs_on_gpu(w, seed, seqlen=steps)
+    for k in range(steps):
+        tok = {key: (v[:, k].contiguous() if v.dim() >= 3 else v) for key, v in tt.items()}
+        y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
+        m3.mamba3_decode_step(d, tok["x"], tok["B"], tok["C"], tok["dt"], tok["lam"], tok["theta"], tok["A"],
+                              tok["D"], s, y)
+        torch.cuda.synchronize()
+        args = oracle_args(ex, pairs)
+        y_ref, cur = oracle.decode_step(args["x"][:, k], args["Bm"][:, k], args["Cm"][:, k], args["dt"][:, k],
+                                        args["lam"][:, k], args["theta"][:, k], args["A"], args["D"], cur)
+        ey = relerr(to_np(y)[bs, hs][None], y_ref)
+        eh = relerr(to_np(s.h)[bs, hs][None], cur[0])
+        print(f"[decode {w.name} step {k}] rel-L2 y={ey:.3e} h={eh:.3e}", flush=True)
+        assert ey <= tol and eh <= tol, (ey, eh)
+        assert np.array_equal(to_np(s.B_prev)[bs, hs][None], cur[1])
+        assert np.array_equal(to_np(s.x_prev)[bs, hs][None], cur[2])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("P,N,R", [(16, 16, 1), (64, 64, 4), (64, 128, 1), (32, 32, 2), (128, 128, 1),
+                                   (16, 64, 4)])
+def test_decode_small(io, P, N, R):
+    w = W("tiny_siso_f32", batch=3, heads=5, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=1)
+    check_decode(w, seed=10 + P + N + R)
+
+
+@pytest.mark.parametrize("name", ["decode_mimo_r4_n64", "decode_siso_n128"])
+def test_decode_full_size_sampled(name):
+    w = syn.WORKLOADS[name]
+    rng = np.random.default_rng(7)
+    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(24)]
+    check_decode(w, seed=4, steps=2, pairs=pairs)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def test_prefill_tiny_siso_f32():
+    """The 1 x 1 x 16 x 16, T=64, Q=16 fp32 case, whole tensor, 1e-5."""
+    check_prefill(syn.WORKLOADS["tiny_siso_f32"], seed=1000)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 100])
+def test_prefill_ragged_lengths(io, T):
+    w = W("tiny_siso_f32", batch=2, heads=3, headdim=16, dstate=16, seqlen=T, chunk=16, io_dtype=io)
+    check_prefill(w, seed=2000 + T)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("P,N,R,Q", [(64, 128, 1, 64), (64, 64, 4, 64), (32, 32, 2, 32), (16, 64, 4, 16),
+                                     (128, 32, 1, 64), (64, 16, 1, 32), (32, 128, 2, 16)])
+def test_prefill_shapes(io, P, N, R, Q):
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=P, dstate=N, rank=R, seqlen=3 * Q + 5, chunk=Q,
+          io_dtype=io)
+    d = dims_of(w)
+    try:
+        m3.mamba3_prefill_workspace_bytes(d, w.seqlen)
+    except m3.M3Error as e:
+        assert e.status == m3.binding.M3_ERR_UNSUPPORTED
+        pytest.skip(f"not in the compiled set: {e}")
+    check_prefill(w, seed=3000 + P + N + R + Q)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_nonzero_initial_state(io):
+    w = W("tiny_siso_f32", batch=2, heads=3, headdim=32, dstate=32, rank=2, seqlen=70, chunk=32, io_dtype=io)
+    check_prefill(w, seed=41, st=syn.draw_state(w, 42))
+
+
+def test_prefill_long_memory_and_zero_skip():
+    w = W("tiny_siso_f32", batch=1, heads=4, headdim=64, dstate=64, rank=1, seqlen=300, chunk=64,
+          io_dtype="bf16")
+    check_prefill(w, seed=51, long_memory=True, zero_D=True)
+
+
+def test_prefill_segment_path_small():
+    """Few chains and many chunks take the three-pass segment path."""
+    w = W("tiny_siso_f32", batch=1, heads=2, headdim=32, dstate=32, rank=1, seqlen=64 * 40 + 7, chunk=64,
+          io_dtype="bf16")
+    d = dims_of(w)
+    assert m3.mamba3_prefill_workspace_bytes(d, w.seqlen) > 0
+    check_prefill(w, seed=61, st=syn.draw_state(w, 62))
+
+
+def test_prefill_segment_path_f32():
+    w = W("tiny_siso_f32", batch=1, heads=3, headdim=16, dstate=16, rank=2, seqlen=16 * 50 + 3, chunk=16,
+          io_dtype="f32")
+    d = dims_of(w)
+    assert m3.mamba3_prefill_workspace_bytes(d, w.seqlen) > 0
+    check_prefill(w, seed=63, st=syn.draw_state(w, 64))
+
+
+def test_split_prefill_handoff_and_decode_continuation():
+    """prefill(T1) -> readout -> load -> prefill(T2) -> 3 decode steps equals
+    the oracle run over T1 + T2 + 3 tokens."""
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=32, dstate=64, rank=2, seqlen=150, chunk=32,
+          io_dtype="bf16")
+    d = dims_of(w)
+    ex, tt = inputs_on_gpu(w, seed=71)
+    T1, T2 = 70, 77
+    s = make_state(w)
+    sl = lambda lo, hi: {k: (v[:, lo:hi].contiguous() if v.dim() >= 3 else v) for k, v in tt.items()}  # noqa
+    y1 = run_prefill(w, sl(0, T1), s, seqlen=T1)
+    h_out = torch.empty_like(s.h)
+    b_out = torch.empty_like(s.B_prev)
+    x_out = torch.empty_like(s.x_prev)
+    m3.m3_state_readout(d, s, h_out, b_out, x_out)
+    s2 = m3.State.empty(d)
+    m3.m3_state_load(d, s2, h_out, b_out, x_out)
+    y2 = run_prefill(w, sl(T1, T1 + T2), s2, seqlen=T2)
+    ys = [y1, y2]
+    for t in range(T1 + T2, T1 + T2 + 3):
+        tok = {k: (v[:, t].contiguous() if v.dim() >= 3 else v) for k, v in tt.items()}
+        y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
+        m3.mamba3_decode_step(d, tok["x"], tok["B"], tok["C"], tok["dt"], tok["lam"], tok["theta"], tok["A"],
+                              tok["D"], s2, y)
+        ys.append(y[:, None])
+    torch.cuda.synchronize()
+    y_all = np.concatenate([to_np(v) for v in ys], axis=1)
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    args = oracle_args({k: (v[:, :T1 + T2 + 3] if v.ndim >= 3 else v) for k, v in ex.items()}, pairs)
+    y_ref, (h_ref, _, _) = oracle.prefill(**args)
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    ey = relerr(np.moveaxis(y_all[bs, :, hs], 0, 1)[None], y_ref)
+    eh = relerr(to_np(s2.h)[bs, hs][None], h_ref)
+    print(f"[handoff] rel-L2 y={ey:.3e} h={eh:.3e}", flush=True)
+    assert ey <= 2e-2 and eh <= 2e-2
+
+
+def test_zero_length_prefill_is_noop():
+    w = W("tiny_siso_f32", batch=1, heads=2, headdim=16, dstate=16, seqlen=0, io_dtype="f32")
+    d = dims_of(w)
+    st = syn.draw_state(w, 5)
+    s = make_state(w, st)
+    before = to_np(s.h).copy()
+    ex, tt = inputs_on_gpu(w, seed=5)
+    run_prefill(w, tt, s, seqlen=0)
+    assert np.array_equal(to_np(s.h), before)
+
+
+def test_prefill_deterministic():
+    w = W("tiny_siso_f32", batch=2, heads=4, headdim=64, dstate=128, rank=1, seqlen=333, chunk=64,
+          io_dtype="bf16")
+    ex, tt = inputs_on_gpu(w, seed=81)
+    outs = []
+    for _ in range(3):
+        s = make_state(w)
+        y = run_prefill(w, tt, s)
+        outs.append((to_np(y), to_np(s.h)))
+    for o in outs[1:]:
+        assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1])
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the benchmark's launch configuration), sampled chains
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["siso_1p5b_t4096", "mimo_r4_t4096", "long_siso_t16384"])
+def test_prefill_full_size_sampled(name):
+    w = syn.WORKLOADS[name]
+    rng = np.random.default_rng(99)
+    chains = sorted({(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(6)})
+    check_prefill(w, seed=1000 + list(syn.WORKLOADS).index(name), pairs=chains)
