@@ -120,3 +120,35 @@ def as_exact(inputs: dict, io_dtype: str) -> dict:
     for k, v in inputs.items():
         out[k] = round_io(v, io_dtype) if k in IO_KEYS else round_io(v, "f32")
     return out
+
+
+def draw_torch(w: Workload, seed: int, device="cuda", seqlen=None, long_memory: bool = False):
+    """Same distributions and layouts as ``draw``, drawn directly on the device
+    with torch's generator (for timing runs, where the values do not matter
+    but their distribution and size do).  x, B, C are cast to the I/O dtype
+    (round-to-nearest-even); dt, lam, theta, A, D are fp32."""
+    import torch
+
+    T = w.seqlen if seqlen is None else seqlen
+    b, H, R, P, N = w.batch, w.heads, w.rank, w.headdim, w.dstate
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    f32 = torch.float32
+
+    def normal(shape, mean=0.0, std=1.0):
+        return torch.randn(shape, generator=g, device=device, dtype=f32) * std + mean
+
+    def uniform(shape, lo, hi):
+        return torch.rand(shape, generator=g, device=device, dtype=f32) * (hi - lo) + lo
+
+    x = normal((b, T, H, R, P)).to(io)
+    Bm = normal((b, T, H, R, N)).to(io)
+    Cm = normal((b, T, H, R, N)).to(io)
+    dt = torch.nn.functional.softplus(normal((b, T, H), -2.0, 0.5))
+    lam = torch.sigmoid(normal((b, T, H)))
+    theta = uniform((b, T, H, N // 2), -torch.pi, torch.pi) * dt[..., None]
+    A = -torch.exp(uniform((H,), -5.0, -3.0) if long_memory else uniform((H,), -1.0, 1.0))
+    D = normal((H,))
+    return {"x": x, "B": Bm, "C": Cm, "dt": dt.contiguous(), "lam": lam.contiguous(),
+            "theta": theta.contiguous(), "A": A, "D": D}
