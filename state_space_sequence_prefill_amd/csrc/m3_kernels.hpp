@@ -60,4 +60,9 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 bool decode_supported(const Dims& d);
 bool prefill_supported(const Dims& d);
 
+// Producer/consumer prefill (m3_prefill_pc.hip): used for every pass whose
+// double-buffered tiles fit; `mode` 0 fused, 1 segment summaries, 2 segments.
+bool prefill_pc_supported(const Dims& d);
+hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
+
 }  // namespace m3

@@ -46,6 +46,7 @@
 // its true entry value).
 #include "m3_device.hpp"
 #include "m3_kernels.hpp"
+#include "m3_mfma.hpp"
 
 namespace m3 {
 namespace {
@@ -55,93 +56,6 @@ constexpr int kWaves = kThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode : int { kFused = 0, kSummary = 1, kSegment = 2 };
-
-// ----------------------------------------------------------------------------
-// MFMA fragments: 8 K-values per lane for a 16 x 32 (A) or 32 x 16 (B) slab.
-// bf16: one v_mfma_f32_16x16x32_bf16.  f32: eight v_mfma_f32_16x16x4_f32, the
-// kk-th using element kk of every lane (any K order works as long as the A and
-// B fragments agree, which every caller guarantees).
-// ----------------------------------------------------------------------------
-template <typename IO> struct Frag;
-template <> struct Frag<bf16> {
-  bf16x8 v;
-  __device__ __forceinline__ void set(int k, float f) { v[k] = (bf16)f; }
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = (bf16)0.0f;
-  }
-  __device__ __forceinline__ void load8(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
-  __device__ __forceinline__ void load44(const bf16* p0, const bf16* p1) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
-    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-  }
-};
-template <> struct Frag<float> {
-  float v[8];
-  __device__ __forceinline__ void set(int k, float f) { v[k] = f; }
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = 0.0f;
-  }
-  __device__ __forceinline__ void load8(const float* p) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-  __device__ __forceinline__ void load44(const float* p0, const float* p1) {
-    const float4 a = *reinterpret_cast<const float4*>(p0);
-    const float4 b = *reinterpret_cast<const float4*>(p1);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
-
-__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
-}
-__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[k], b.v[k], acc, 0, 0, 0);
-}
-
-// 8 consecutive I/O elements <-> fp32.
-__device__ __forceinline__ void load8f(const float* p, float (&o)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-}
-__device__ __forceinline__ void load8f(const bf16* p, float (&o)[8]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[2 * k] = __uint_as_float(w[k] << 16);
-    o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
-}
-__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
-  bf16x8 o;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = (bf16)v[k];
-  *reinterpret_cast<bf16x8*>(p) = o;
-}
-
-// Trig of the chunk-local angles.  bf16 I/O rounds the rotated operands to
-// bf16 anyway, so the hardware sin/cos is ample; fp32 I/O uses sincosf.
-template <typename IO> __device__ __forceinline__ void trig(float a, float& s, float& c) {
-  sincosf(a, &s, &c);
-}
-template <> __device__ __forceinline__ void trig<bf16>(float a, float& s, float& c) {
-  __sincosf(a, &s, &c);
-}
 
 // ----------------------------------------------------------------------------
 // LDS layout (dynamic).  rows = Q*R rounded up to 32; all pitches add 16 B.
@@ -160,8 +74,9 @@ struct Lds {
   float* sW;     // [Q] state-update weights w_s
   float* sMisc;  // [0] l_E (natural log), [1] l_E*log2e
   float* sSeg;   // [N/2] running angle total (segment summaries)
+  float2* sEnd;  // [N/2] (cos, sin) of the chunk's last local angle
 
-  __host__ __device__ static size_t bytes(int rows_pad, int Q) {
+  __host__ __device__ static constexpr size_t bytes(int rows_pad, int Q) {
     const int ldr = rows_pad + PAD;
     size_t b = 0;
     b += (size_t)rows_pad * LDN * E * 2;  // sB, sC
@@ -174,6 +89,7 @@ struct Lds {
     b += (size_t)Q * 4;                   // sW
     b += 16;                              // sMisc
     b += (size_t)(N / 2) * 4;             // sSeg
+    b += (size_t)(N / 2) * 8;             // sEnd
     return b;
   }
   __device__ void carve(char* base, int rows_pad, int Q) {
@@ -190,8 +106,23 @@ struct Lds {
     sTok = reinterpret_cast<float4*>(p); p += (size_t)Q * 16;
     sW = reinterpret_cast<float*>(p); p += (size_t)Q * 4;
     sMisc = reinterpret_cast<float*>(p); p += 16;
-    sSeg = reinterpret_cast<float*>(p);
+    sSeg = reinterpret_cast<float*>(p); p += (size_t)(N / 2) * 4;
+    sEnd = reinterpret_cast<float2*>(p);
   }
+};
+
+// Largest padded row count (Q*R rounded up to 32) a <IO, N, P> instance
+// supports: the LDS tiles must fit 160 KiB and every thread prefetches at
+// most two 4-row x 8-column slices of B, C and x.
+template <typename IO, int N, int P>
+struct Limits {
+  static constexpr size_t kLds = 160 * 1024;
+  static constexpr bool fits(int r) {
+    return Lds<IO, N, P>::bytes(r, r < 64 ? r : 64) <= kLds && r * N <= 16384 && r * P <= 16384;
+  }
+  static constexpr int kMaxRows = fits(256) ? 256 : fits(128) ? 128 : fits(64) ? 64 : fits(32) ? 32 : 0;
+  static constexpr int kMaxB = (kMaxRows / 4) * (N / 8) > kThreads ? 2 : 1;  // B/C slices per thread
+  static constexpr int kMaxX = (kMaxRows / 4) * (P / 8) > kThreads ? 2 : 1;  // x slices per thread
 };
 
 struct KParams {
@@ -310,30 +241,93 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
   }
   float lsum = 0.f;  // running log-decay of a segment summary (thread 0)
 
+  // ---------------- register prefetch of one chunk's inputs ----------------
+  // Issued for chunk c+1 right after chunk c's tiles are built, so the HBM
+  // latency overlaps chunk c's matrix-core phases.
+  constexpr int MB = Limits<IO, N, P>::kMaxB, MX = Limits<IO, N, P>::kMaxX;
+  const int npg = N / 8;                        // pair groups of 4 pairs (8 columns)
+  const int nth = (Q / 4) * npg;                // angle items (4 tokens x 4 pairs), <= 256
+  const int nbitems = (rows_pad / 4) * npg;     // B/C items (4 rows x 8 columns)
+  const int npx = P / 8;
+  const int nxitems = (rows_pad / 4) * npx;     // x items (4 rows x 8 columns)
+  float pf_dt = 0.f, pf_lm = 0.f, pf_dtn = 0.f, pf_lmn = 0.f;
+  float4 pf_th[4];
+  Raw8<IO> pf_b[MB][4], pf_c[MB][4], pf_x[MX][4];
+
+  // Loads are unconditional from clamped (always valid) addresses; rows and
+  // tokens past the end are zeroed where the values are consumed.  A load
+  // into a register that was zeroed on another path would make the compiler
+  // wait for every outstanding load before the next one.
+  auto issue_loads = [&](int ck) {
+    const int c0 = ck * Q;
+    const int Lc = (T - c0 < Q) ? (T - c0) : Q;
+    if (wave == 0) {
+      const int t = lane < Lc ? lane : Lc - 1;
+      pf_dt = DTg[(size_t)(c0 + t) * H];
+      pf_lm = LMg[(size_t)(c0 + t) * H];
+      const int tn = (c0 + Lc < T) ? c0 + Lc : c0 + Lc - 1;
+      pf_dtn = DTg[(size_t)tn * H];
+      pf_lmn = LMg[(size_t)tn * H];
+    }
+    if (tid < nth) {
+      const int tg = tid / npg, pg = tid % npg;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = (4 * tg + k < Lc) ? 4 * tg + k : 0;
+        pf_th[k] = *reinterpret_cast<const float4*>(THg + (size_t)(c0 + t) * tokTh + 4 * pg);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int it = tid + m * kThreads;
+      if (it < nbitems) {
+        const int rg = it / npg, cg = it % npg;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int rho = 4 * rg + k;
+          const bool valid = rho < rows && (rho >> lgR) < Lc;
+          const int t = valid ? (rho >> lgR) : 0, r = valid ? (rho & (R - 1)) : 0;
+          pf_b[m][k].load(Bg + (size_t)(c0 + t) * tokBC + r * N + 8 * cg);
+          if (has_y) pf_c[m][k].load(Cg + (size_t)(c0 + t) * tokBC + r * N + 8 * cg);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MX; ++m) {
+      const int it = tid + m * kThreads;
+      if (it < nxitems) {
+        const int rg = it / npx, xg = it % npx;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int rho = 4 * rg + k;
+          const bool valid = rho < rows && (rho >> lgR) < Lc;
+          const int t = valid ? (rho >> lgR) : 0, r = valid ? (rho & (R - 1)) : 0;
+          pf_x[m][k].load(Xg + (size_t)(c0 + t) * tokX + r * P + 8 * xg);
+        }
+      }
+    }
+  };
+
+  if (ck0 < ck1) issue_loads(ck0);
+
   for (int ck = ck0; ck < ck1; ++ck) {
     const int c0 = ck * Q;
     const int Lc = (T - c0 < Q) ? (T - c0) : Q;  // valid tokens in this chunk
     const bool fold_next = (c0 + Lc) < T;        // a token follows this chunk
+    const int te = Lc - 1;
     __syncthreads();  // previous chunk fully consumed (LDS reuse)
 
     // ---------------- A1: decay scan and per-token coefficients ----------------
     if (wave == 0) {
       const int t = lane;
       const bool valid = t < Lc;
-      float dtv = 0.f, lmv = 0.f;
-      if (valid) {
-        dtv = DTg[(size_t)(c0 + t) * H];
-        lmv = LMg[(size_t)(c0 + t) * H];
-      }
+      const float dtv = valid ? pf_dt : 0.f, lmv = valid ? pf_lm : 0.f;
       const float av = (valid && t > 0) ? dtv * Ah : 0.f;
       const float ell = wave_inclusive_scan(av);   // l_t (first token's decay is in E)
       const float gam = lmv * dtv;
       const float bet = (1.0f - lmv) * dtv;
-      float dtn = 0.f, lmn = 0.f;
-      if (fold_next) {
-        dtn = DTg[(size_t)(c0 + Lc) * H];
-        lmn = LMg[(size_t)(c0 + Lc) * H];
-      }
+      const float dtn = fold_next ? pf_dtn : 0.f;
+      const float lmn = fold_next ? pf_lmn : 0.f;
       const float ell_last = __shfl(ell, Lc - 1, kWave);
       const float ellE = ell_last + dtn * Ah;
       const float bet_next_tok = (1.0f - lmn) * dtn;
@@ -364,18 +358,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
     }
 
     // ---------------- A2: angle prefix over the chunk ----------------
-    const int ngrp = Q / 4;          // token groups of 4
-    const int npg = N / 8;           // pair groups of 4
-    const int nitems = ngrp * npg;   // <= 256
     float ph[4][4];
     const int tg = tid / npg, pg = tid % npg;
-    if (tid < nitems) {
+    if (tid < nth) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int t = 4 * tg + k;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < Lc) v = *reinterpret_cast<const float4*>(THg + (size_t)(c0 + t) * tokTh + 4 * pg);
-        ph[k][0] = v.x; ph[k][1] = v.y; ph[k][2] = v.z; ph[k][3] = v.w;
+        const bool tv = 4 * tg + k < Lc;
+        ph[k][0] = tv ? pf_th[k].x : 0.f;
+        ph[k][1] = tv ? pf_th[k].y : 0.f;
+        ph[k][2] = tv ? pf_th[k].z : 0.f;
+        ph[k][3] = tv ? pf_th[k].w : 0.f;
         if (k > 0) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) ph[k][j] += ph[k - 1][j];
@@ -385,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
           make_float4(ph[3][0], ph[3][1], ph[3][2], ph[3][3]);
     }
     __syncthreads();
-    if (tid < nitems) {
+    if (tid < nth) {
       float off[4] = {0.f, 0.f, 0.f, 0.f};
       for (int q = 0; q < tg; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(s.sTot + q * (N / 2) + 4 * pg);
@@ -393,30 +385,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ph[k][j] += off[j];
         *reinterpret_cast<float4*>(s.sPhi + (4 * tg + k) * (N / 2) + 4 * pg) =
-            make_float4(ph[k][0] + off[0], ph[k][1] + off[1], ph[k][2] + off[2], ph[k][3] + off[3]);
+            make_float4(ph[k][0], ph[k][1], ph[k][2], ph[k][3]);
+        if (4 * tg + k == te) {
+          // rotation of the carried state into the next chunk's frame (fp32 trig)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float sn, cs;
+            sincosf(ph[k][j], &sn, &cs);
+            s.sEnd[4 * pg + j] = make_float2(cs, sn);
+          }
+        }
       }
     }
     __syncthreads();
 
     // ---------------- A3: rotate B, C; build the LDS tiles ----------------
-    {
-      const int ncg = N / 8;                 // 8-column groups
-      const int nbitems = (rows_pad / 4) * ncg;
-      for (int it = tid; it < nbitems; it += kThreads) {
-        const int rg = it / ncg, cg = it % ncg;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int it = tid + m * kThreads;
+      if (it < nbitems) {
+        const int rg = it / npg, cg = it % npg;
         float bt[4][8];
+#pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int rho = 4 * rg + k;
-          const int t = rho >> lgR, r = rho & (R - 1);
+          const int t = rho >> lgR;
           const bool valid = (rho < rows) && (t < Lc);
           float bv[8], cv[8];
+          pf_b[m][k].unpack(bv);
+          if (has_y) pf_c[m][k].unpack(cv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) { bv[e] = 0.f; cv[e] = 0.f; }
+          for (int e = 0; e < 8; ++e) {
+            bv[e] = valid ? bv[e] : 0.f;
+            cv[e] = (valid && has_y) ? cv[e] : 0.f;
+          }
           float wt = 0.f;
           if (valid) {
-            load8f(Bg + (size_t)(c0 + t) * tokBC + r * N + 8 * cg, bv);
-            if (has_y) load8f(Cg + (size_t)(c0 + t) * tokBC + r * N + 8 * cg, cv);
             const float4 pv = *reinterpret_cast<const float4*>(s.sPhi + t * (N / 2) + 4 * cg);
             const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
@@ -440,18 +447,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
           store4(s.sBt + (8 * cg + e) * ldr + 4 * rg, col);
         }
       }
-      const int npx = P / 8;
-      const int nxitems = (rows_pad / 4) * npx;
-      for (int it = tid; it < nxitems; it += kThreads) {
+    }
+#pragma unroll
+    for (int m = 0; m < MX; ++m) {
+      const int it = tid + m * kThreads;
+      if (it < nxitems) {
         const int rg = it / npx, xg = it % npx;
         float xv[4][8];
+#pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int rho = 4 * rg + k;
-          const int t = rho >> lgR, r = rho & (R - 1);
-          const bool valid = (rho < rows) && (t < Lc);
+          const bool valid = rho < rows && (rho >> lgR) < Lc;
+          pf_x[m][k].unpack(xv[k]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xv[k][e] = 0.f;
-          if (valid) load8f(Xg + (size_t)(c0 + t) * tokX + r * P + 8 * xg, xv[k]);
+          for (int e = 0; e < 8; ++e) xv[k][e] = valid ? xv[k][e] : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -460,6 +469,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
         }
       }
     }
+    // next chunk's inputs: in flight during this chunk's matrix-core phases
+    if (ck + 1 < ck1) issue_loads(ck + 1);
     __syncthreads();
 
     // ---------------- B: outputs of this chunk ----------------
@@ -483,12 +494,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
             mma(Y[pb], fa, fb);
           }
         }
-        float lq[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tq = (16 * rb + 4 * g + i) >> lgR;
-          lq[i] = s.sTok[tq < Q ? tq : Q - 1].y;
-          const float sc = exp2f(lq[i]);
+          const float sc = exp2f(s.sTok[tq < Q ? tq : Q - 1].y);
 #pragma unroll
           for (int pb = 0; pb < PB; ++pb) Y[pb][i] *= sc;
         }
@@ -551,7 +560,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
     {
       const float decE = expf(s.sMisc[0]);
       const int nks = rows_pad / 32;
-      const int te = Lc - 1;
       const bool last_chunk = (ck == ck1 - 1);
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
@@ -566,13 +574,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
             mma(acc, fa, fb);
           }
           // rows n = 16nb + 4g + i: pairs (8nb + 2g) and (8nb + 2g + 1) -> lane-local rotation
-          const float2 pe = *reinterpret_cast<const float2*>(s.sPhi + te * (N / 2) + 8 * nb + 2 * g);
-          float s0, c0r, s1, c1r;
-          sincosf(pe.x, &s0, &c0r);
-          sincosf(pe.y, &s1, &c1r);
+          const float2 r0 = s.sEnd[8 * nb + 2 * g];
+          const float2 r1 = s.sEnd[8 * nb + 2 * g + 1];
           float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-          rot2(v[0], v[1], c0r, s0);
-          rot2(v[2], v[3], c1r, s1);
+          rot2(v[0], v[1], r0.x, r0.y);
+          rot2(v[2], v[3], r1.x, r1.y);
           Hreg[k] = f32x4{v[0], v[1], v[2], v[3]};
           const int p = 16 * pb + c, n0 = 16 * nb + 4 * g;
           store4(s.sH + p * LDN + n0, v);
@@ -728,17 +734,17 @@ hipError_t launch_fused_t(const Dims& d, const PrefillArgs& a, hipStream_t st) {
   kp.lgR = d.R == 1 ? 0 : (d.R == 2 ? 1 : 2);
   kp.Q = d.Q;
   const int chains = d.batch * d.heads;
-  if (a.nseg <= 1) {
-    kp.mode = kFused;
-    kp.nblocks = chains;
-    hipLaunchKernelGGL((prefill_kernel<IO, N, P>), dim3(kp.nblocks), dim3(kThreads), lds, st, kp);
+  const bool pc = prefill_pc_supported(d);
+  auto pass = [&](int mode, int nblocks) -> hipError_t {
+    if (pc) return launch_prefill_pc(d, a, st, mode, nblocks);
+    kp.mode = mode;
+    kp.nblocks = nblocks;
+    hipLaunchKernelGGL((prefill_kernel<IO, N, P>), dim3(nblocks), dim3(kThreads), lds, st, kp);
     return hipGetLastError();
-  }
+  };
+  if (a.nseg <= 1) return pass(kFused, chains);
   // pass 1: summaries of segments 0 .. nseg-2 from a zero entry value
-  kp.mode = kSummary;
-  kp.nblocks = chains * (a.nseg - 1);
-  hipLaunchKernelGGL((prefill_kernel<IO, N, P>), dim3(kp.nblocks), dim3(kThreads), lds, st, kp);
-  hipError_t e = hipGetLastError();
+  hipError_t e = pass(kSummary, chains * (a.nseg - 1));
   if (e != hipSuccess) return e;
   // pass 2: scan over segments -> entry values
   int G2 = 1;
@@ -751,10 +757,7 @@ hipError_t launch_fused_t(const Dims& d, const PrefillArgs& a, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // pass 3: every segment from its entry value
-  kp.mode = kSegment;
-  kp.nblocks = chains * a.nseg;
-  hipLaunchKernelGGL((prefill_kernel<IO, N, P>), dim3(kp.nblocks), dim3(kThreads), lds, st, kp);
-  return hipGetLastError();
+  return pass(kSegment, chains * a.nseg);
 }
 
 template <typename IO, int N>
@@ -778,17 +781,16 @@ hipError_t launch_n(const Dims& d, const PrefillArgs& a, hipStream_t s) {
 }
 
 template <typename IO>
-size_t lds_need(const Dims& d) {
-  const int rows_pad = ((d.Q * d.R) + 31) & ~31;
+int max_rows(const Dims& d) {
   switch (d.N * 1000 + d.P) {
 #define M3_CASE(NN, PP) \
-  case NN * 1000 + PP: return Lds<IO, NN, PP>::bytes(rows_pad, d.Q);
+  case NN * 1000 + PP: return Limits<IO, NN, PP>::kMaxRows;
     M3_CASE(16, 16) M3_CASE(16, 32) M3_CASE(16, 64) M3_CASE(16, 128)
     M3_CASE(32, 16) M3_CASE(32, 32) M3_CASE(32, 64) M3_CASE(32, 128)
     M3_CASE(64, 16) M3_CASE(64, 32) M3_CASE(64, 64) M3_CASE(64, 128)
     M3_CASE(128, 16) M3_CASE(128, 32) M3_CASE(128, 64) M3_CASE(128, 128)
 #undef M3_CASE
-    default: return (size_t)1 << 40;
+    default: return 0;
   }
 }
 
@@ -801,8 +803,8 @@ bool prefill_supported(const Dims& d) {
   const bool q_ok = d.Q == 16 || d.Q == 32 || d.Q == 64;
   if (!(n_ok && p_ok && r_ok && q_ok)) return false;
   if (d.Q * d.R > 256) return false;
-  const size_t lds = d.bf16 ? lds_need<bf16>(d) : lds_need<float>(d);
-  return lds <= 160 * 1024;
+  const int rows_pad = ((d.Q * d.R) + 31) & ~31;
+  return prefill_pc_supported(d) || rows_pad <= (d.bf16 ? max_rows<bf16>(d) : max_rows<float>(d));
 }
 
 hipError_t launch_prefill(const Dims& d, const PrefillArgs& a, hipStream_t s) {
