@@ -225,6 +225,8 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
   if (seqlen == 0) return ok();
   if ((int64_t)seqlen * m.batch * m.heads * m.R * (m.N > m.P ? m.N : m.P) > ((int64_t)1 << 40))
     return fail(M3_ERR_UNSUPPORTED, "problem too large for 40-bit element offsets");
+  if ((int64_t)m.Q * m.heads * m.R * (m.N > m.P ? m.N : m.P) >= ((int64_t)1 << 31))
+    return fail(M3_ERR_UNSUPPORTED, "chunk * heads * rank * max(headdim, dstate) must stay below 2^31");
   const void* ptrs[] = {x, B, C, dt, lam, theta, A, D, y};
   const char* names[] = {"x", "B", "C", "dt", "lam", "theta", "A", "D", "y"};
   for (int i = 0; i < 9; ++i)

@@ -61,13 +61,47 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
 }
 __device__ __forceinline__ float shfl_up(float v, int d) { return __shfl_up(v, d, kWave); }
 
+// DPP move with zero fill: lanes whose source is outside the row (or in a
+// disabled row) read 0.  ctrl: 0x110 | n = row_shr:n, 0x142 = row_bcast:15,
+// 0x143 = row_bcast:31.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sum within each row of 16 lanes (4 DPP adds, no LDS).
+__device__ __forceinline__ float row16_inclusive_scan(float v) {
+  v += dpp_zero<0x111, 0xf>(v);
+  v += dpp_zero<0x112, 0xf>(v);
+  v += dpp_zero<0x114, 0xf>(v);
+  v += dpp_zero<0x118, 0xf>(v);
+  return v;
+}
+
+// Inclusive prefix sum within each half-wave of 32 lanes.
+__device__ __forceinline__ float row32_inclusive_scan(float v) {
+  v = row16_inclusive_scan(v);
+  v += dpp_zero<0x142, 0xa>(v);  // rows 1 and 3 add the last lane of rows 0 and 2
+  return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const float u = shfl_up(v, d);
-    if (lane >= d) v += u;
+  v = row32_inclusive_scan(v);
+  v += dpp_zero<0x143, 0xc>(v);  // rows 2 and 3 add lane 31
+  return v;
+}
+
+// Inclusive prefix sum within aligned segments of `width` lanes (power of two
+// <= 64): DPP for 16, 32 and 64, shuffles otherwise.
+__device__ __forceinline__ float segment_inclusive_scan(float v, int width) {
+  if (width == 16) return row16_inclusive_scan(v);
+  if (width == 32) return row32_inclusive_scan(v);
+  if (width == 64) return wave_inclusive_scan(v);
+  const int sub = threadIdx.x & (width - 1);
+  for (int d = 1; d < width; d <<= 1) {
+    const float u = __shfl_up(v, d, width);
+    if (sub >= d) v += u;
   }
   return v;
 }

@@ -53,7 +53,7 @@ __device__ __forceinline__ int pc_remap_block(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
-// LDS layout for <IO, N, P> at runtime rows_pad (= Q*R rounded up to 32).
+// LDS layout for <IO, N, P> with tiles of `rows` (token, rank) rows.
 template <typename IO, int N, int P>
 struct PcLds {
   static constexpr int E = sizeof(IO);
@@ -61,15 +61,15 @@ struct PcLds {
   static constexpr int NK = N < 32 ? 32 : N;
   static constexpr int LDN = NK + PAD;
   // one tile buffer
-  __host__ __device__ static constexpr size_t buf_bytes(int rows_pad) {
-    return (size_t)rows_pad * LDN * E * 2            // sB, sC
-           + (size_t)N * (rows_pad + PAD) * E        // sBt
-           + (size_t)P * (rows_pad + PAD) * E        // sXt
-           + (size_t)(N / 2) * 16;                   // sEnd {cos, sin, phi, 0}
+  __host__ __device__ static constexpr size_t buf_bytes(int rows) {
+    return (size_t)rows * LDN * E * 2            // sB, sC
+           + (size_t)N * (rows + PAD) * E        // sBt
+           + (size_t)P * (rows + PAD) * E        // sXt
+           + (size_t)(N / 2) * 16;               // sEnd {cos, sin, phi, 0}
   }
-  __host__ __device__ static constexpr size_t coef_bytes(int Q) { return (size_t)Q * 20 + 16; }
-  __host__ __device__ static constexpr size_t bytes(int rows_pad, int Q) {
-    return 2 * buf_bytes(rows_pad) + 3 * coef_bytes(Q) + (N / 2) * 4;
+  static constexpr size_t kCoefBytes = 64 * 20 + 16;  // one coefficient slot (Q <= 64)
+  __host__ __device__ static constexpr size_t bytes(int rows) {
+    return 2 * buf_bytes(rows) + 3 * kCoefBytes + (N / 2) * 4;
   }
 };
 
@@ -89,7 +89,7 @@ template <typename IO, int N, int P>
 struct PcLimits {
   static constexpr int NK = PcLds<IO, N, P>::NK;
   static constexpr bool fits(int r) {
-    return PcLds<IO, N, P>::bytes(r, r < 64 ? r : 64) <= 160 * 1024 && r * NK * (int)sizeof(IO) <= 16384 &&
+    return PcLds<IO, N, P>::bytes(r) <= 160 * 1024 && r * NK * (int)sizeof(IO) <= 16384 &&
            (r / 4) * (N / 8) <= 2 * kProdThreads && (r / 4) * (P / 8) <= 2 * kProdThreads;
   }
   static constexpr int kMaxRows = fits(128) ? 128 : fits(64) ? 64 : fits(32) ? 32 : 0;
@@ -97,6 +97,13 @@ struct PcLimits {
   static constexpr int kMI = (kMaxRows / 4) * (N / 8) > kProdThreads ? 2 : 1;     // B/C items per thread
   static constexpr int kMX = (kMaxRows / 4) * (P / 8) > kProdThreads ? 2 : 1;     // x items per thread
   static constexpr int kPBW = (P / 16 + kConsWaves - 1) / kConsWaves;            // p-blocks per consumer
+};
+
+// One chunk's raw inputs as a producer thread holds them in registers.
+template <typename IO, int MI, int MX>
+struct PcRaw {
+  Raw8<IO> b[MI][4], c[MI][4], x[MX][4];
+  float4 th[MI][4];
 };
 
 template <typename IO, int N, int P>
@@ -107,6 +114,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   constexpr int NK = L::NK, LDN = L::LDN, PAD = L::PAD;
   constexpr int NS = NK / 32;
   constexpr int MI = Lim::kMI, MX = Lim::kMX, PBW = Lim::kPBW, RBM = Lim::kMaxRB;
+  // Tiles always hold RMAX rows; rows past Q*R stay zero, so every consumer
+  // loop has compile-time bounds.
+  constexpr int RMAX = Lim::kMaxRows, KSM = RMAX / 32;
+  constexpr int ldr = RMAX + PAD;
   extern __shared__ __align__(16) char smem[];
 
   const PrefillArgs& a = kp.a;
@@ -129,14 +140,13 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   const bool producer = wave < 4;
   const int rows = Q * R;
   const int rows_pad = (rows + 31) & ~31;
-  const int ldr = rows_pad + PAD;
 
   // ---- LDS: [tile buffer 0 | tile buffer 1 | coefs x3 | sSeg] ----
-  const size_t bufB = (size_t)rows_pad * LDN * sizeof(IO);           // sB, sC
-  const size_t bufBt = (size_t)N * ldr * sizeof(IO);
-  const size_t bufXt = (size_t)P * ldr * sizeof(IO);
-  const size_t bufStride = 2 * bufB + bufBt + bufXt + (size_t)(N / 2) * 16;
-  const size_t coefStride = (size_t)Q * 20 + 16;
+  constexpr size_t bufB = (size_t)RMAX * LDN * sizeof(IO);  // sB, sC
+  constexpr size_t bufBt = (size_t)N * ldr * sizeof(IO);
+  constexpr size_t bufXt = (size_t)P * ldr * sizeof(IO);
+  constexpr size_t bufStride = L::buf_bytes(RMAX);
+  constexpr size_t coefStride = L::kCoefBytes;
   char* const coefBase = smem + 2 * bufStride;
   float* const sSeg = reinterpret_cast<float*>(coefBase + 3 * coefStride);
   auto getbuf = [&](int ck) {
@@ -157,16 +167,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     r.sMisc = reinterpret_cast<float*>(p + (size_t)Q * 20);
     return r;
   };
-  if (NK != N) {
-    // columns N .. NK-1 of sB and sC are never written: keep them zero
-    for (int k = 0; k < 2; ++k) {
-      const PcBuf<IO, N, P> bk = getbuf(k);
-      for (int e = tid; e < rows_pad * LDN; e += kPcThreads) {
-        bk.sB[e] = from_f32<IO>(0.f);
-        bk.sC[e] = from_f32<IO>(0.f);
-      }
-    }
-  }
+  // Zero both tile buffers once: padding rows and columns are never written.
+  for (size_t e = tid; e < 2 * bufStride / 16; e += kPcThreads)
+    reinterpret_cast<uint4*>(smem)[e] = make_uint4(0u, 0u, 0u, 0u);
   if (mode == kPcSummary)
     for (int j = tid; j < N / 2; j += kPcThreads) sSeg[j] = 0.f;
 
@@ -191,6 +194,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // 4 state pairs = 8 columns).  Items are laid out row-group-fastest, so the
     // RG = rows_pad/4 row groups of one pair group are RG consecutive lanes of
     // one wave and the angle prefix over the chunk is an in-wave segmented scan.
+    // Inside the chunk loop every load and every use of a loaded register is
+    // unconditional (threads past the item count work on a clamped duplicate
+    // item and skip only their LDS stores): a load or use behind a branch
+    // would make the compiler wait for all outstanding loads.
     const int pt = tid;
     const int RG = rows_pad / 4;
     const int npg = N / 8;
@@ -198,51 +205,88 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     const int npx = P / 8;
     const int nxitems = RG * npx;
     const int ntok = 4 >> lgR;  // tokens per row group (R <= 4)
-    Raw8<IO> rb_[MI][4], rc_[MI][4], rx_[MX][4];  // raw B, C, x of the next chunk
-    float4 rth[MI][4];                            // raw theta of the next chunk
-    float rdt = 0.f, rlm = 0.f, rdtn = 0.f, rlmn = 0.f;  // raw dt/lam (wave 0), chunk after next
+    const IO* const Csrc = has_y ? Cg : Bg;  // segment summaries never read C
+    // Two register sets: chunk i is built from one while chunk i+1's loads
+    // land in the other, and chunk i+2's loads are issued into the first
+    // right after it is consumed (two chunks of HBM latency hidden).
+    PcRaw<IO, MI, MX> rsA, rsB;
+    float rdt, rlm, rdtn, rlmn;  // raw dt/lam of the chunk after next
 
-    auto load_chunk = [&](int ck) {  // B, C, x, theta of chunk ck
+    // Per item: row group, column group, and 32-bit element offsets of its
+    // rows relative to the chunk's first token (the host keeps
+    // chunk * heads * rank * max(N, P) below 2^31).
+    int irg[MI], ipg[MI], rtok[MI][4];
+    bool ist[MI];
+    uint32_t ob[MI][4], oth[MI][4], obs[MI], oths[MI];
+    int xrg[MX], xxg[MX], xtok[MX][4];
+    bool xst[MX];
+    uint32_t ox[MX][4], oxs[MX];
+#pragma unroll
+    for (int m = 0; m < MI; ++m) {
+      const int it0 = pt + m * kProdThreads;
+      ist[m] = it0 < nbitems;
+      const int it = ist[m] ? it0 : it0 % nbitems;
+      const int rg = it % RG, pg = it / RG;
+      irg[m] = rg;
+      ipg[m] = pg;
+      const int t0 = (4 * rg) >> lgR;
+      obs[m] = 8u * pg;
+      oths[m] = 4u * pg;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rho = 4 * rg + k;
+        rtok[m][k] = rho < rows ? (rho >> lgR) : Q;
+        ob[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokBC + (uint32_t)(rho & (R - 1)) * N + 8 * pg;
+        oth[m][k] = (uint32_t)(t0 + (k < ntok ? k : ntok - 1)) * (uint32_t)tokTh + 4 * pg;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MX; ++m) {
+      const int it0 = pt + m * kProdThreads;
+      xst[m] = it0 < nxitems;
+      const int it = xst[m] ? it0 : it0 % nxitems;
+      const int rg = it % RG, xg = it / RG;
+      xrg[m] = rg;
+      xxg[m] = xg;
+      oxs[m] = 8u * xg;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rho = 4 * rg + k;
+        xtok[m][k] = rho < rows ? (rho >> lgR) : Q;
+        ox[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokX + (uint32_t)(rho & (R - 1)) * P + 8 * xg;
+      }
+    }
+
+    auto load_chunk = [&](int ck, PcRaw<IO, MI, MX>& rs) {  // B, C, x, theta of chunk ck (rows past the chunk read token 0)
       const int c0 = ck * Q, Lc = chunk_len(ck);
+      const IO* Bc = Bg + (size_t)c0 * tokBC;
+      const IO* Cc = Csrc + (size_t)c0 * tokBC;
+      const IO* Xc = Xg + (size_t)c0 * tokX;
+      const float* Tc = THg + (size_t)c0 * tokTh;
 #pragma unroll
       for (int m = 0; m < MI; ++m) {
-        const int it = pt + m * kProdThreads;
-        if (it < nbitems) {
-          const int rg = it % RG, pg = it / RG;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int rho = 4 * rg + k;
-            const bool valid = rho < rows && (rho >> lgR) < Lc;
-            const int t = valid ? (rho >> lgR) : 0, r = valid ? (rho & (R - 1)) : 0;
-            rb_[m][k].load(Bg + (size_t)(c0 + t) * tokBC + r * N + 8 * pg);
-            if (has_y) rc_[m][k].load(Cg + (size_t)(c0 + t) * tokBC + r * N + 8 * pg);
-          }
-          const int t0 = (4 * rg) >> lgR;
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t o = rtok[m][k] < Lc ? ob[m][k] : obs[m];
+          rs.b[m][k].load(Bc + o);
+          rs.c[m][k].load(Cc + o);
+        }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            int t = t0 + (q < ntok ? q : ntok - 1);
-            t = t < Lc ? t : 0;
-            rth[m][q] = *reinterpret_cast<const float4*>(THg + (size_t)(c0 + t) * tokTh + 4 * pg);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t o = rtok[m][0] + (q < ntok ? q : ntok - 1) < Lc ? oth[m][q] : oths[m];
+          rs.th[m][q] = *reinterpret_cast<const float4*>(Tc + o);
         }
       }
 #pragma unroll
       for (int m = 0; m < MX; ++m) {
-        const int it = pt + m * kProdThreads;
-        if (it < nxitems) {
-          const int rg = it % RG, xg = it / RG;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int rho = 4 * rg + k;
-            const bool valid = rho < rows && (rho >> lgR) < Lc;
-            const int t = valid ? (rho >> lgR) : 0, r = valid ? (rho & (R - 1)) : 0;
-            rx_[m][k].load(Xg + (size_t)(c0 + t) * tokX + r * P + 8 * xg);
-          }
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t o = xtok[m][k] < Lc ? ox[m][k] : oxs[m];
+          rs.x[m][k].load(Xc + o);
         }
       }
     };
-    auto load_dt = [&](int ck) {  // dt, lam of chunk ck and of the token after it (wave 0)
-      if (wave != 0) return;
+    auto load_dt = [&](int ck) {  // dt, lam of chunk ck (lane = token) and of the token after it
       const int c0 = ck * Q, Lc = chunk_len(ck);
       const int t = lane < Lc ? lane : Lc - 1;
       rdt = DTg[(size_t)(c0 + t) * H];
@@ -251,12 +295,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       rdtn = DTg[(size_t)tn * H];
       rlmn = LMg[(size_t)tn * H];
     };
-    // In-chunk decay scan and per-token coefficients of chunk ck -> coef slot ck % 3.
+    // In-chunk decay scan and per-token coefficients of chunk ck -> coef slot
+    // ck % 3 (computed by every producer wave, stored by wave 0).
     // sTok[t] = {A_t, B_t, L_t, 0} with L_t = l_t log2(e) and the mask weights
     // gamma_t 2^{L_q - L_t} = 2^{L_q - A_t},  beta_{t+1} 2^{L_q - L_{t+1}} = 2^{L_q - B_t}
     // (a zero weight gives an infinite exponent and an exact zero).
-    auto decay_coefs = [&](int ck) {
-      if (wave != 0) return;
+    auto decay_coefs = [&](int ck, bool store) {
       const int c0 = ck * Q, Lc = chunk_len(ck);
       const bool fold_next = c0 + Lc < T;
       const PcCoef co = getcoef(ck);
@@ -272,108 +316,94 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const float ellE = ell_last + dtn * Ah;
       const float bet_up = __shfl_down(bet, 1, kWave);
       const float ell_up = __shfl_down(ell, 1, kWave);
-      float betn, elln;
-      if (t < Lc - 1) {
-        betn = bet_up;
-        elln = ell_up;
-      } else if (t == Lc - 1) {
-        betn = (1.0f - lmn) * dtn;
-        elln = ellE;
-      } else {
-        betn = 0.f;
-        elln = ellE;
-      }
+      const bool inner = t < Lc - 1, lastv = t == Lc - 1;
+      const float betn = inner ? bet_up : (lastv ? (1.0f - lmn) * dtn : 0.f);
+      const float elln = inner ? ell_up : ellE;
       const float ellv = valid ? ell : ell_last;
       const float w = valid ? (gam * expf(ellE - ellv) + betn * expf(ellE - elln)) : 0.f;
       const float inf = __builtin_huge_valf();
       const float L2 = ellv * kLog2ePc;
       const float Ak = (valid && gam > 0.f) ? L2 - __log2f(gam) : inf;
       const float Bk = (valid && betn > 0.f) ? elln * kLog2ePc - __log2f(betn) : inf;
-      if (t < Q) {
+      if (store && wave == 0 && t < Q) {
         co.sTok[t] = make_float4(Ak, Bk, L2, 0.f);
         co.sW[t] = w;
-      }
-      if (t == 0) {
-        co.sMisc[0] = ellE;
-        co.sMisc[1] = ellE * kLog2ePc;
+        if (t == 0) {
+          co.sMisc[0] = ellE;
+          co.sMisc[1] = ellE * kLog2ePc;
+        }
       }
     };
     // Angles (in-wave scan), rotation, and the tiles of chunk ck -> tile buffer ck % 2.
-    auto build_tiles = [&](int ck) {
+    auto build_tiles = [&](int ck, const PcRaw<IO, MI, MX>& rs) {
       const int Lc = chunk_len(ck);
       const int te = Lc - 1;
       const PcBuf<IO, N, P> bf = getbuf(ck);
       const float* sW = getcoef(ck).sW;
 #pragma unroll
       for (int m = 0; m < MI; ++m) {
-        const int it = pt + m * kProdThreads;
-        if (it < nbitems) {
-          const int rg = it % RG, pg = it / RG;
-          const int t0 = (4 * rg) >> lgR;
-          float th[4][4];
+        const int rg = irg[m], pg = ipg[m];
+        const int t0 = rtok[m][0];
+        float th[4][4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool tv = q < ntok && t0 + q < Lc;
-            th[q][0] = tv ? rth[m][q].x : 0.f;
-            th[q][1] = tv ? rth[m][q].y : 0.f;
-            th[q][2] = tv ? rth[m][q].z : 0.f;
-            th[q][3] = tv ? rth[m][q].w : 0.f;
-          }
-          // exclusive prefix of the row groups' totals within the pair group
-          float base[4];
+        for (int q = 0; q < 4; ++q) {
+          const float tv = (q < ntok && t0 + q < Lc) ? 1.f : 0.f;
+          th[q][0] = tv * rs.th[m][q].x;
+          th[q][1] = tv * rs.th[m][q].y;
+          th[q][2] = tv * rs.th[m][q].z;
+          th[q][3] = tv * rs.th[m][q].w;
+        }
+        // exclusive prefix of the row groups' totals within the pair group
+        float base[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float tot = th[0][j] + th[1][j] + th[2][j] + th[3][j];
+          base[j] = segment_inclusive_scan(tot, RG) - tot;
+        }
+        // per-row angles: rows of one token share its prefix
+        float ph[4][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int kq = R == 1 ? k : (k >> lgR);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            ph[k][j] = base[j] + th[0][j] + (kq >= 1 ? th[1][j] : 0.f) + (kq >= 2 ? th[2][j] : 0.f) +
+                       (kq >= 3 ? th[3][j] : 0.f);
+        }
+        float bt[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int rho = 4 * rg + k;
+          const int t = rtok[m][k];
+          const bool valid = t < Lc;
+          const float vm = valid ? 1.f : 0.f;  // zero padding rows through the rotation
+          float bv[8], cv[8];
+          rs.b[m][k].unpack(bv);
+          rs.c[m][k].unpack(cv);
+          float cs4[4], sn4[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float tot = th[0][j] + th[1][j] + th[2][j] + th[3][j];
-            float inc = tot;
-            for (int d = 1; d < RG; d <<= 1) {
-              const float u = __shfl_up(inc, d, RG);
-              if (rg >= d) inc += u;
-            }
-            base[j] = inc - tot;
+            float sn, cs;
+            trig<IO>(ph[k][j], sn, cs);
+            cs4[j] = cs * vm;
+            sn4[j] = sn * vm;
+            rot2(bv[2 * j], bv[2 * j + 1], cs4[j], -sn4[j]);
+            rot2(cv[2 * j], cv[2 * j + 1], cs4[j], -sn4[j]);
           }
-          float bt[4][8];
+          const float wt = valid ? sW[t < Q ? t : 0] : 0.f;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int rho = 4 * rg + k;
-            const int t = rho >> lgR;
-            const int kq = t - t0;  // token of this row within the row group
-            const bool valid = rho < rows && t < Lc;
-            float ph[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float acc = base[j];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc += (q <= kq) ? th[q][j] : 0.f;
-              ph[j] = acc;
-            }
-            float bv[8], cv[8];
-            rb_[m][k].unpack(bv);
-            if (has_y) rc_[m][k].unpack(cv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float sn, cs;
-              trig<IO>(ph[j], sn, cs);
-              rot2(bv[2 * j], bv[2 * j + 1], cs, -sn);
-              if (has_y) rot2(cv[2 * j], cv[2 * j + 1], cs, -sn);
-            }
-            const float wt = valid ? sW[t] : 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              bv[e] = valid ? bv[e] : 0.f;
-              cv[e] = (valid && has_y) ? cv[e] : 0.f;
-              bt[k][e] = bv[e] * wt;
-            }
+          for (int e = 0; e < 8; ++e) bt[k][e] = bv[e] * wt;
+          if (ist[m]) {
             store8(bf.sB + rho * LDN + 8 * pg, bv);
             if (has_y) store8(bf.sC + rho * LDN + 8 * pg, cv);
             if (valid && t == te && (rho & (R - 1)) == 0) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                float sn, cs;
-                sincosf(ph[j], &sn, &cs);
-                bf.sEnd[4 * pg + j] = make_float4(cs, sn, ph[j], 0.f);
-              }
+              for (int j = 0; j < 4; ++j)
+                bf.sEnd[4 * pg + j] = make_float4(cs4[j], sn4[j], ph[k][j], 0.f);
             }
           }
+        }
+        if (ist[m]) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float col[4] = {bt[0][e], bt[1][e], bt[2][e], bt[3][e]};
@@ -383,45 +413,73 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
 #pragma unroll
       for (int m = 0; m < MX; ++m) {
-        const int it = pt + m * kProdThreads;
-        if (it < nxitems) {
-          const int rg = it % RG, xg = it / RG;
+        const int rg = xrg[m], xg = xxg[m];
+        if constexpr (sizeof(IO) == 2) {
+          // transpose 4 rows x 8 bf16 columns with byte permutes (no unpack)
+          uint32_t w[4][4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t keep = xtok[m][k] < Lc ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[k][q] = rs.x[m][k].w[q] & keep;
+          }
+          uint2 v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            v[e].x = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
+            v[e].y = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
+          }
+          if (xst[m]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2*>(bf.sXt + (8 * xg + e) * ldr + 4 * rg) = v[e];
+          }
+        } else {
           float xv[4][8];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const int rho = 4 * rg + k;
-            const bool valid = rho < rows && (rho >> lgR) < Lc;
-            rx_[m][k].unpack(xv[k]);
+            const float vm = xtok[m][k] < Lc ? 1.f : 0.f;
+            rs.x[m][k].unpack(xv[k]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xv[k][e] = valid ? xv[k][e] : 0.f;
+            for (int e = 0; e < 8; ++e) xv[k][e] *= vm;
           }
+          if (xst[m]) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float col[4] = {xv[0][e], xv[1][e], xv[2][e], xv[3][e]};
-            store4(bf.sXt + (8 * xg + e) * ldr + 4 * rg, col);
+            for (int e = 0; e < 8; ++e) {
+              const float col[4] = {xv[0][e], xv[1][e], xv[2][e], xv[3][e]};
+              store4(bf.sXt + (8 * xg + e) * ldr + 4 * rg, col);
+            }
           }
         }
       }
     };
 
+    // One pipeline step = one chunk and one barrier (the consumers count the
+    // same number of barriers).
+    auto step = [&](int i, PcRaw<IO, MI, MX>& rs) {
+      if (i < ck1) {
+        build_tiles(i, rs);
+        const int n1 = i + 1 < ck1 ? i + 1 : i;  // clamped: past the end the data is reloaded, not used
+        const int n2 = i + 2 < ck1 ? i + 2 : n1;
+        decay_coefs(n1, n1 != i);
+        load_chunk(n2, rs);
+        load_dt(n2);
+      }
+      __syncthreads();
+    };
     if (ck0 < ck1) {
       // prologue: coefficients of the first chunk, then the first prefetches
       load_dt(ck0);
-      decay_coefs(ck0);
-      load_chunk(ck0);
-      if (ck0 + 1 < ck1) load_dt(ck0 + 1);
+      decay_coefs(ck0, true);
+      const int n1 = ck0 + 1 < ck1 ? ck0 + 1 : ck0;
+      load_chunk(ck0, rsA);
+      load_chunk(n1, rsB);
+      load_dt(n1);
     }
     __syncthreads();
-    for (int i = ck0; i <= ck1; ++i) {
-      if (i < ck1) {
-        build_tiles(i);
-        if (i + 1 < ck1) {
-          decay_coefs(i + 1);
-          load_chunk(i + 1);
-          if (i + 2 < ck1) load_dt(i + 2);
-        }
-      }
-      __syncthreads();
+    for (int i = ck0; i <= ck1; i += 2) {
+      step(i, rsA);
+      if (i + 1 <= ck1) step(i + 1, rsB);
     }
   } else {
     // ======================= consumers (waves 4-7) =======================
@@ -479,8 +537,8 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         const PcBuf<IO, N, P> bf = getbuf(j);
         const PcCoef co = getcoef(j);
         const bool last_chunk = j == ck1 - 1;
-        const int nks = rows_pad / 32;
-        const int nrb = rows_pad / 16;  // row blocks (padding rows are zero)
+        constexpr int nks = KSM;  // tiles hold RMAX rows; padding rows are zero
+        constexpr int nrb = RBM;
 #pragma unroll
         for (int u = 0; u < PBW; ++u) {
           const int pb = cw + kConsWaves * u;
@@ -591,26 +649,29 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           }
           // state update and rotation into the next chunk's frame
           const float decE = expf(co.sMisc[0]);
-          Frag<IO> Xs[RBM / 2];
+          // all operands first (independent LDS reads), then the MFMA chains
+          Frag<IO> Xs[KSM];
+          Frag<IO> Bs[NB][KSM];
+          float2 r0[NB], r1[NB];
 #pragma unroll
-          for (int ks = 0; ks < RBM / 2; ++ks)
-            if (ks < nks) Xs[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
+          for (int ks = 0; ks < KSM; ++ks) Xs[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int ks = 0; ks < KSM; ++ks) Bs[nb][ks].load8(bf.sBt + (16 * nb + c) * ldr + 32 * ks + 8 * g);
+            const float4 e0 = bf.sEnd[8 * nb + 2 * g];
+            const float4 e1 = bf.sEnd[8 * nb + 2 * g + 1];
+            r0[nb] = make_float2(e0.x, e0.y);
+            r1[nb] = make_float2(e1.x, e1.y);
+          }
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             f32x4 hacc = Hreg[u][nb] * decE;
 #pragma unroll
-            for (int ks = 0; ks < RBM / 2; ++ks) {
-              if (ks < nks) {
-                Frag<IO> fa;
-                fa.load8(bf.sBt + (16 * nb + c) * ldr + 32 * ks + 8 * g);
-                mma(hacc, fa, Xs[ks]);
-              }
-            }
-            const float4 r0 = bf.sEnd[8 * nb + 2 * g];
-            const float4 r1 = bf.sEnd[8 * nb + 2 * g + 1];
+            for (int ks = 0; ks < KSM; ++ks) mma(hacc, Bs[nb][ks], Xs[ks]);
             float v[4] = {hacc[0], hacc[1], hacc[2], hacc[3]};
-            rot2(v[0], v[1], r0.x, r0.y);
-            rot2(v[2], v[3], r1.x, r1.y);
+            rot2(v[0], v[1], r0[nb].x, r0[nb].y);
+            rot2(v[2], v[3], r1[nb].x, r1[nb].y);
             Hreg[u][nb] = f32x4{v[0], v[1], v[2], v[3]};
             if (last_chunk) {
               const int p = 16 * pb + c, n0 = 16 * nb + 4 * g;
@@ -650,8 +711,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 
 template <typename IO, int N, int P>
 hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int mode, int nblocks) {
-  const int rows_pad = ((d.Q * d.R) + 31) & ~31;
-  const size_t lds = PcLds<IO, N, P>::bytes(rows_pad, d.Q);
+  const size_t lds = PcLds<IO, N, P>::bytes(PcLimits<IO, N, P>::kMaxRows);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P>),
