@@ -455,16 +455,16 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     };
 
     // One pipeline step = one chunk and one barrier (the consumers count the
-    // same number of barriers).
+    // same number of barriers: one per chunk plus a last one).
     auto step = [&](int i, PcRaw<IO, MI, MX>& rs) {
-      if (i < ck1) {
-        build_tiles(i, rs);
-        const int n1 = i + 1 < ck1 ? i + 1 : i;  // clamped: past the end the data is reloaded, not used
-        const int n2 = i + 2 < ck1 ? i + 2 : n1;
-        decay_coefs(n1, n1 != i);
-        load_chunk(n2, rs);
-        load_dt(n2);
-      }
+      build_tiles(i, rs);
+      const int n1 = i + 1 < ck1 ? i + 1 : i;  // clamped: past the end the data is reloaded, not used
+      const int n2 = i + 2 < ck1 ? i + 2 : n1;
+      decay_coefs(n1, n1 != i);
+      // dt first: the vmcnt counter is in order, so consuming dt next step
+      // then leaves this step's chunk batch in flight
+      load_dt(n2);
+      load_chunk(n2, rs);
       __syncthreads();
     };
     if (ck0 < ck1) {
@@ -473,14 +473,19 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       decay_coefs(ck0, true);
       const int n1 = ck0 + 1 < ck1 ? ck0 + 1 : ck0;
       load_chunk(ck0, rsA);
-      load_chunk(n1, rsB);
       load_dt(n1);
+      load_chunk(n1, rsB);
     }
     __syncthreads();
-    for (int i = ck0; i <= ck1; i += 2) {
+    // the pair loop has no conditional loads, so the wait counts the compiler
+    // derives around its back edge stay exact (only the batch consumed waits)
+    int i = ck0;
+    for (; i + 1 < ck1; i += 2) {
       step(i, rsA);
-      if (i + 1 <= ck1) step(i + 1, rsB);
+      step(i + 1, rsB);
     }
+    if (i < ck1) step(i, rsA);
+    __syncthreads();
   } else {
     // ======================= consumers (waves 4-7) =======================
     const int cw = wave - 4;
