@@ -33,7 +33,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
-PREFILL_SRC = os.path.join(ROOT, "state_space_sequence_prefill_amd", "csrc", "m3_prefill.hip")
+CSRC = os.path.join(ROOT, "state_space_sequence_prefill_amd", "csrc")
+# sources whose code the fused prefill launch runs (kernel, device helpers)
+PREFILL_SRCS = ("m3_prefill_pc.hip", "m3_mfma.hpp", "m3_device.hpp")
+HEADLINE = "siso_1p5b_t4096"
+METRIC = "Mamba-3 scan prefill Mtokens/s + decode \u00b5s/step; % of MFMA / HBM peak"
 
 
 def log(msg):
@@ -69,20 +73,24 @@ def decode_bytes(w):
     return 2 * h + 2 * pend + tok + y
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha():
+    h = hashlib.sha256()
+    for name in PREFILL_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic(workload_name):
-    """Per-launch HBM bytes measured with rocprofv3 counters, if recorded for
-    the current kernel source (profiles/<kernel>_<workload>_traffic.json)."""
-    p = os.path.join(PROFILES, f"prefill_{workload_name}_traffic.json")
+    """Per-launch HBM bytes measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters (scaled by the copy-kernel calibration), if they were recorded
+    for the current kernel sources (profiles/prefill_pc_<workload>_traffic.json)."""
+    p = os.path.join(PROFILES, f"prefill_pc_{workload_name}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != source_sha(PREFILL_SRC):
+    if rec.get("kernel_source_sha") != source_sha():
         return None
     return rec.get("bytes_per_launch")
 
@@ -194,27 +202,32 @@ def time_decode(w, seed, steps=1000, flush_steps=20):
     }
 
 
-def cpu_baseline(w):
-    """The fp64 oracle, unchanged, on the host: batch row 0 of the workload
-    (all heads, all tokens), single-threaded numpy."""
+def cpu_baseline(w, min_seconds=10.0):
+    """The fp64 oracle, unchanged, on the host, single-threaded numpy: whole
+    batch rows of the workload (all heads, all tokens), one at a time, until
+    at least `min_seconds` of CPU time have been spent (at most all rows)."""
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
+    import contextlib
     import oracle
     from state_space_sequence_prefill_amd import synthetic as syn
     ws = w.with_(batch=1)
-    ex = syn.as_exact(syn.draw(ws, 1001), w.io_dtype)
-    import contextlib
     ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    rows, spent = 0, 0.0
     with ctx:
-        t0 = time.perf_counter()
-        oracle.prefill(ex["x"], ex["B"], ex["C"], ex["dt"], ex["lam"], ex["theta"], ex["A"], ex["D"])
-        dt = time.perf_counter() - t0
-    toks = ws.batch * ws.seqlen
-    return {"value": round(toks / dt / 1e6, 8), "unit": "Mtokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch row 0 of {w.batch} ({w.heads} heads x {w.seqlen} tokens), numpy fp64, "
-                      f"{dt:.1f} s", "seconds": round(dt, 2), "cpu": _cpu_model(), "host_cpus": os.cpu_count()}
+        while rows < w.batch and spent < min_seconds:
+            ex = syn.as_exact(syn.draw(ws, 1001 + rows), w.io_dtype)
+            t0 = time.perf_counter()
+            oracle.prefill(ex["x"], ex["B"], ex["C"], ex["dt"], ex["lam"], ex["theta"], ex["A"], ex["D"])
+            spent += time.perf_counter() - t0
+            rows += 1
+    toks = rows * ws.seqlen
+    return {"value": round(toks / spent / 1e6, 8), "unit": "Mtokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {w.batch} batch rows ({w.heads} heads x {w.seqlen} tokens each), "
+                      f"numpy fp64 sequential, one thread, {spent:.1f} s",
+            "seconds": round(spent, 2), "cpu": _cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def _cpu_model():
@@ -228,6 +241,77 @@ def _cpu_model():
     return "unknown"
 
 
+def profile_prefill(steps):
+    """A few untimed prefill launches of the headline workload (for rocprofv3)."""
+    import torch
+    from state_space_sequence_prefill_amd import synthetic as syn
+    pf = Prefill(syn.WORKLOADS[HEADLINE], seed=1001)
+    for _ in range(steps):
+        pf.step()
+    torch.cuda.synchronize()
+    log(f"bench: {steps} prefill launches of {HEADLINE} done")
+
+
+def profile_copy(steps):
+    """Copies of a known size through the library's copy kernel (m3_state_load
+    of a 256 x 32 x 64 x 128 fp32 state, 256 MiB read + 256 MiB written per
+    launch): the calibration for rocprofv3's FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    import state_space_sequence_prefill_amd as m3
+    d = m3.make_dims(256, 32, 64, 128, 1, 64, "bf16")
+    dst = m3.State.empty(d)
+    src = m3.State.empty(d)
+    src.h.fill_(1.0)
+    src.B_prev.zero_()
+    src.x_prev.zero_()
+    for _ in range(steps):
+        m3.m3_state_load(d, dst, src.h, src.B_prev, src.x_prev)
+    torch.cuda.synchronize()
+    log(f"bench: {steps} state copies of {dst.h.numel() * 4} bytes done")
+
+
+def _counter_per_dispatch(run_dir, counter, kernel_substr, largest=False):
+    """Mean (or, with largest, the maximum) value per dispatch of a counter
+    from a rocprofv3 counter_collection.csv under run_dir."""
+    import csv
+    import glob
+    tot = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    key = (f, r["Dispatch_Id"])
+                    tot[key] = tot.get(key, 0.0) + float(r["Counter_Value"])
+    if not tot:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} under {run_dir}")
+    vals = list(tot.values())
+    return max(vals) if largest else sum(vals) / len(vals)
+
+
+def record_traffic(base):
+    """Write profiles/prefill_pc_<workload>_traffic.json from four rocprofv3
+    counter runs under `base`: prefill_fetch, prefill_write (FETCH_SIZE /
+    WRITE_SIZE of the prefill launches) and copy_fetch, copy_write (the same
+    counters for the 256 MiB copy).  Counters are KiB per dispatch; each is
+    scaled by known copy bytes / counter reading of the copy."""
+    copy_bytes = 256 * 32 * 64 * 128 * 4
+    cf = _counter_per_dispatch(os.path.join(base, "copy_fetch"), "FETCH_SIZE", "copy_kernel", largest=True) * 1024
+    cw = _counter_per_dispatch(os.path.join(base, "copy_write"), "WRITE_SIZE", "copy_kernel", largest=True) * 1024
+    pf = _counter_per_dispatch(os.path.join(base, "prefill_fetch"), "FETCH_SIZE", "prefill_pc_kernel") * 1024
+    pw = _counter_per_dispatch(os.path.join(base, "prefill_write"), "WRITE_SIZE", "prefill_pc_kernel") * 1024
+    kf, kw = copy_bytes / cf, copy_bytes / cw
+    from state_space_sequence_prefill_amd import synthetic as syn
+    w = syn.WORKLOADS[HEADLINE]
+    rec = {"workload": HEADLINE, "kernel": "prefill_pc_kernel", "kernel_source_sha": source_sha(),
+           "fetch_bytes_raw": pf, "write_bytes_raw": pw, "copy_fetch_scale": kf, "copy_write_scale": kw,
+           "bytes_per_launch": round(pf * kf + pw * kw), "algorithmic_bytes_per_launch": prefill_bytes(w)}
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"prefill_pc_{HEADLINE}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,10 +319,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile-prefill", type=int, default=0, metavar="K",
+                    help="only run K untimed prefill launches (for rocprofv3)")
+    ap.add_argument("--profile-copy", type=int, default=0, metavar="K",
+                    help="only run K 256 MiB copies (counter calibration)")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write the traffic record from rocprofv3 counter runs under DIR (no GPU)")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every (batch, head) chain of the scan is independent, so "
-              "N GPUs run the same kernel on batch/N (see the sharding notes in DESIGN.md); run with --gpus 1.",
+              "N GPUs would run the same kernel on batch/N with no communication; run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -247,7 +340,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
-    w = syn.WORKLOADS["siso_1p5b_t4096"]
+    if args.profile_prefill or args.profile_copy:
+        if args.profile_prefill:
+            profile_prefill(args.profile_prefill)
+        if args.profile_copy:
+            profile_copy(args.profile_copy)
+        return
+
+    w = syn.WORKLOADS[HEADLINE]
     log(f"bench: prefill {w.name} warmup={args.warmup} steps={args.steps}")
     pf = Prefill(w, seed=1001)
     ms_step, kern_ms = pf.time(args.steps, args.warmup)
@@ -257,7 +357,7 @@ def main():
     achieved = nbytes / (kern_ms / 1e3) / 1e9
     flops = prefill_flops(w)
     line = {
-        "metric": "Mamba-3 scan prefill Mtokens/s + decode us/step; % of MFMA / HBM peak",
+        "metric": METRIC,
         "value": round(value, 3),
         "unit": "Mtokens/s",
         "n_gpus": 1,
@@ -274,7 +374,7 @@ def main():
                    "io_dtype": w.io_dtype, "state_dtype": "f32", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(w.name),
-                     "kernel": "prefill_kernel (fused pass)", "algorithmic_bytes_per_launch": nbytes,
+                     "kernel": "prefill_pc_kernel (fused pass)", "algorithmic_bytes_per_launch": nbytes,
                      "kernel_ms": round(kern_ms, 4),
                      "mfma_frac_at_measured_time": round(flops / (kern_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
