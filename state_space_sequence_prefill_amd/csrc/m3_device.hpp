@@ -106,4 +106,28 @@ __device__ __forceinline__ float segment_inclusive_scan(float v, int width) {
   return v;
 }
 
+// Inclusive prefix sums over strided lanes, K independent values at once (so
+// each step's K lane reads are in flight together): within each aligned group
+// of count*stride lanes (a power of two <= 64), lane base + k*stride adds the
+// values of lanes base + k'*stride for k' <= k (stride, count powers of two,
+// count <= 32).
+template <int K>
+__device__ __forceinline__ void strided_inclusive_scan(float (&v)[K], int stride, int count) {
+  const int k = ((int)threadIdx.x / stride) & (count - 1);
+  const int lane = (int)threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int s = 0; s < 5; ++s) {
+    const int d = 1 << s;
+    if (d < count) {
+      const int src = (lane - d * stride) & (kWave - 1);
+      float u[K];
+#pragma unroll
+      for (int q = 0; q < K; ++q)
+        u[q] = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v[q])));
+#pragma unroll
+      for (int q = 0; q < K; ++q) v[q] += (k >= d) ? u[q] : 0.f;
+    }
+  }
+}
+
 }  // namespace m3

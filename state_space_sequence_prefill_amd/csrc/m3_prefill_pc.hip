@@ -67,9 +67,14 @@ struct PcLds {
            + (size_t)P * (rows + PAD) * E        // sXt
            + (size_t)(N / 2) * 16;               // sEnd {cos, sin, phi, 0}
   }
+  // masked score tile (S.M) shared by the consumer waves: rows = queries,
+  // columns = keys
+  __host__ __device__ static constexpr size_t sm_bytes(int rows) { return (size_t)rows * (rows + PAD) * E; }
+  // output tile: the consumer waves' y slices meet here and leave as whole rows
+  __host__ __device__ static constexpr size_t y_bytes(int rows) { return (size_t)rows * (P + PAD) * E; }
   static constexpr size_t kCoefBytes = 64 * 20 + 16;  // one coefficient slot (Q <= 64)
   __host__ __device__ static constexpr size_t bytes(int rows) {
-    return 2 * buf_bytes(rows) + 3 * kCoefBytes + (N / 2) * 4;
+    return 2 * buf_bytes(rows) + sm_bytes(rows) + y_bytes(rows) + 3 * kCoefBytes + (N / 2) * 4;
   }
 };
 
@@ -113,10 +118,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   constexpr int NB = N / 16, PB = P / 16;
   constexpr int NK = L::NK, LDN = L::LDN, PAD = L::PAD;
   constexpr int NS = NK / 32;
-  constexpr int MI = Lim::kMI, MX = Lim::kMX, PBW = Lim::kPBW, RBM = Lim::kMaxRB;
+  constexpr int MI = Lim::kMI, MX = Lim::kMX, PBW = Lim::kPBW;
   // Tiles always hold RMAX rows; rows past Q*R stay zero, so every consumer
   // loop has compile-time bounds.
-  constexpr int RMAX = Lim::kMaxRows, KSM = RMAX / 32;
+  // (instances whose tiles do not fit at all are never launched; they compile
+  // with the smallest tile height)
+  constexpr int RMAX = Lim::kMaxRows > 0 ? Lim::kMaxRows : 32, KSM = RMAX / 32, RBM = RMAX / 16;
   constexpr int ldr = RMAX + PAD;
   extern __shared__ __align__(16) char smem[];
 
@@ -141,13 +148,18 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   const int rows = Q * R;
   const int rows_pad = (rows + 31) & ~31;
 
-  // ---- LDS: [tile buffer 0 | tile buffer 1 | coefs x3 | sSeg] ----
+  // ---- LDS: [tile buffer 0 | tile buffer 1 | sSM | sY | coefs x3 | sSeg] ----
   constexpr size_t bufB = (size_t)RMAX * LDN * sizeof(IO);  // sB, sC
   constexpr size_t bufBt = (size_t)N * ldr * sizeof(IO);
   constexpr size_t bufXt = (size_t)P * ldr * sizeof(IO);
   constexpr size_t bufStride = L::buf_bytes(RMAX);
   constexpr size_t coefStride = L::kCoefBytes;
-  char* const coefBase = smem + 2 * bufStride;
+  constexpr size_t smStride = L::sm_bytes(RMAX);
+  constexpr size_t yStride = L::y_bytes(RMAX);
+  constexpr int ldy = P + PAD;
+  IO* const sSM = reinterpret_cast<IO*>(smem + 2 * bufStride);
+  IO* const sY = reinterpret_cast<IO*>(smem + 2 * bufStride + smStride);
+  char* const coefBase = smem + 2 * bufStride + smStride + yStride;
   float* const sSeg = reinterpret_cast<float*>(coefBase + 3 * coefStride);
   auto getbuf = [&](int ck) {
     char* p = smem + (size_t)(ck & 1) * bufStride;
@@ -167,8 +179,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     r.sMisc = reinterpret_cast<float*>(p + (size_t)Q * 20);
     return r;
   };
-  // Zero both tile buffers once: padding rows and columns are never written.
-  for (size_t e = tid; e < 2 * bufStride / 16; e += kPcThreads)
+  // Zero both tile buffers and the score tile once: padding rows and
+  // columns, and score blocks above the diagonal, are never written.
+  for (size_t e = tid; e < (2 * bufStride + smStride) / 16; e += kPcThreads)
     reinterpret_cast<uint4*>(smem)[e] = make_uint4(0u, 0u, 0u, 0u);
   if (mode == kPcSummary)
     for (int j = tid; j < N / 2; j += kPcThreads) sSeg[j] = 0.f;
@@ -191,18 +204,23 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   if (producer) {
     // ======================= producers (waves 0-3) =======================
     // Item = (row group rg: 4 consecutive (token, rank) rows, pair group pg:
-    // 4 state pairs = 8 columns).  Items are laid out row-group-fastest, so the
-    // RG = rows_pad/4 row groups of one pair group are RG consecutive lanes of
-    // one wave and the angle prefix over the chunk is an in-wave segmented scan.
+    // 4 state pairs = 8 columns).  Lanes run over GW adjacent pair groups
+    // first, then over the RG = rows_pad/4 row groups, so 16 lanes read GW*16
+    // contiguous bytes of 16/GW rows (few cache lines per load instruction),
+    // and the RG row groups of one pair group stay inside one wave (GW*RG <=
+    // 64): the angle prefix over the chunk is an in-wave strided scan.
     // Inside the chunk loop every load and every use of a loaded register is
     // unconditional (threads past the item count work on a clamped duplicate
     // item and skip only their LDS stores): a load or use behind a branch
     // would make the compiler wait for all outstanding loads.
     const int pt = tid;
+    const int pw = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform producer index
     const int RG = rows_pad / 4;
     const int npg = N / 8;
-    const int nbitems = RG * npg;
+    const int GW = npg < 64 / RG ? npg : 64 / RG;  // pair groups per lane group
     const int npx = P / 8;
+    const int GX = npx < 64 / RG ? npx : 64 / RG;  // x column groups per lane group
+    const int nbitems = RG * npg;
     const int nxitems = RG * npx;
     const int ntok = 4 >> lgR;  // tokens per row group (R <= 4)
     const IO* const Csrc = has_y ? Cg : Bg;  // segment summaries never read C
@@ -226,7 +244,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const int it0 = pt + m * kProdThreads;
       ist[m] = it0 < nbitems;
       const int it = ist[m] ? it0 : it0 % nbitems;
-      const int rg = it % RG, pg = it / RG;
+      const int rg = (it / GW) % RG, pg = (it / (GW * RG)) * GW + it % GW;
       irg[m] = rg;
       ipg[m] = pg;
       const int t0 = (4 * rg) >> lgR;
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const int it0 = pt + m * kProdThreads;
       xst[m] = it0 < nxitems;
       const int it = xst[m] ? it0 : it0 % nxitems;
-      const int rg = it % RG, xg = it / RG;
+      const int rg = (it / GX) % RG, xg = (it / (GX * RG)) * GX + it % GX;
       xrg[m] = rg;
       xxg[m] = xg;
       oxs[m] = 8u * xg;
@@ -296,7 +314,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       rlmn = LMg[(size_t)tn * H];
     };
     // In-chunk decay scan and per-token coefficients of chunk ck -> coef slot
-    // ck % 3 (computed by every producer wave, stored by wave 0).
+    // ck % 3 (producer wave 0 only, which alone loads dt and lam).
     // sTok[t] = {A_t, B_t, L_t, 0} with L_t = l_t log2(e) and the mask weights
     // gamma_t 2^{L_q - L_t} = 2^{L_q - A_t},  beta_{t+1} 2^{L_q - L_{t+1}} = 2^{L_q - B_t}
     // (a zero weight gives an infinite exponent and an exact zero).
@@ -325,7 +343,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const float L2 = ellv * kLog2ePc;
       const float Ak = (valid && gam > 0.f) ? L2 - __log2f(gam) : inf;
       const float Bk = (valid && betn > 0.f) ? elln * kLog2ePc - __log2f(betn) : inf;
-      if (store && wave == 0 && t < Q) {
+      if (store && t < Q) {
         co.sTok[t] = make_float4(Ak, Bk, L2, 0.f);
         co.sW[t] = w;
         if (t == 0) {
@@ -354,12 +372,15 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           th[q][3] = tv * rs.th[m][q].w;
         }
         // exclusive prefix of the row groups' totals within the pair group
-        float base[4];
+        float base[4], tot[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float tot = th[0][j] + th[1][j] + th[2][j] + th[3][j];
-          base[j] = segment_inclusive_scan(tot, RG) - tot;
+          tot[j] = th[0][j] + th[1][j] + th[2][j] + th[3][j];
+          base[j] = tot[j];
         }
+        strided_inclusive_scan(base, GW, RG);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) base[j] -= tot[j];
         // per-row angles: rows of one token share its prefix
         float ph[4][4];
 #pragma unroll
@@ -454,26 +475,34 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
     };
 
-    // One pipeline step = one chunk and one barrier (the consumers count the
-    // same number of barriers: one per chunk plus a last one).
+    // One pipeline step = one chunk and two barriers (the consumers count the
+    // same: two per chunk plus a last pair).  Building chunk i overlaps the
+    // consumers' shared score tile of chunk i-1 (other buffers); the first
+    // barrier ends both, and the coefficient work and the next loads then
+    // overlap the consumers' outputs and state update.
     auto step = [&](int i, PcRaw<IO, MI, MX>& rs) {
       build_tiles(i, rs);
+      __syncthreads();
       const int n1 = i + 1 < ck1 ? i + 1 : i;  // clamped: past the end the data is reloaded, not used
       const int n2 = i + 2 < ck1 ? i + 2 : n1;
-      decay_coefs(n1, n1 != i);
-      // dt first: the vmcnt counter is in order, so consuming dt next step
-      // then leaves this step's chunk batch in flight
-      load_dt(n2);
+      if (pw == 0) {
+        decay_coefs(n1, n1 != i);
+        // dt first: the vmcnt counter is in order, so consuming dt next step
+        // then leaves this step's chunk batch in flight
+        load_dt(n2);
+      }
       load_chunk(n2, rs);
       __syncthreads();
     };
     if (ck0 < ck1) {
       // prologue: coefficients of the first chunk, then the first prefetches
-      load_dt(ck0);
-      decay_coefs(ck0, true);
       const int n1 = ck0 + 1 < ck1 ? ck0 + 1 : ck0;
+      if (pw == 0) {
+        load_dt(ck0);
+        decay_coefs(ck0, true);
+      }
       load_chunk(ck0, rsA);
-      load_dt(n1);
+      if (pw == 0) load_dt(n1);
       load_chunk(n1, rsB);
     }
     __syncthreads();
@@ -486,9 +515,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     }
     if (i < ck1) step(i, rsA);
     __syncthreads();
+    __syncthreads();
   } else {
     // ======================= consumers (waves 4-7) =======================
-    const int cw = wave - 4;
+    const int cw = __builtin_amdgcn_readfirstlane(wave - 4);  // wave-uniform
     f32x4 Hreg[PBW][NB];  // E^T tiles: rows n = 16nb + 4g + i, column p = 16pb + c
     float lsum = 0.f;
 #pragma unroll
@@ -535,15 +565,96 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
     }
     __syncthreads();
+    // y of chunk jy leaves the LDS output tile as whole 16-byte runs of its
+    // rows (each (token, rank) row is P contiguous elements in HBM)
+    auto store_y = [&](int jy) {
+      const int c0 = jy * Q, nrow = chunk_len(jy) * R;
+      constexpr int G16 = P * (int)sizeof(IO) / 16;  // 16-byte granules per row
+      for (int e = tid - kProdThreads; e < nrow * G16; e += kConsWaves * kWave) {
+        const int row = e / G16, gq = e % G16;
+        const uint4 v = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * (16 / sizeof(IO)));
+        *reinterpret_cast<uint4*>(Yg + (size_t)(c0 + (row >> lgR)) * tokX + (row & (R - 1)) * P +
+                                  gq * (16 / sizeof(IO))) = v;
+      }
+    };
     for (int i = ck0; i <= ck1; ++i) {
+      if (has_y && i >= ck0 + 2) store_y(i - 2);
+      // ---- phase 1: this wave's 16x16 blocks of S.M for chunk i-1 ----
+      // Blocks (rb, kb), kb <= rb, are dealt round-robin to the 4 consumer
+      // waves.  S^T = Bt Ct^T leaves the accumulator with 4 consecutive keys
+      // per lane for one query, masked by the trapezoid decay and stored as
+      // one 4-element run of row `query` of sSM (D x on the diagonal).
+      if (i > ck0 && has_y) {
+        const int j = i - 1;
+        const PcBuf<IO, N, P> bf = getbuf(j);
+        const PcCoef co = getcoef(j);
+        const int rbn = (rows + 15) >> 4;
+        const int nblk = rbn * (rbn + 1) / 2;
+        // groups of up to kGrp blocks in straight-line code, so the LDS reads
+        // of a group are all in flight before its first product
+        constexpr int NBLK = RBM * (RBM + 1) / 2, NQ = (NBLK + kConsWaves - 1) / kConsWaves;
+        constexpr int kGrp = NQ < 3 ? NQ : 3;
+        for (int q0 = 0; q0 < NQ; q0 += kGrp) {
+          int rbq[kGrp], kbq[kGrp];
+          bool okq[kGrp];
+#pragma unroll
+          for (int q = 0; q < kGrp; ++q) {
+            const int bi = cw + kConsWaves * (q0 + q);
+            okq[q] = bi < nblk;
+            int rem = okq[q] ? bi : 0, rb = 0;
+            while (rem > rb) {  // block index -> (row block, key block), kb <= rb
+              rem -= rb + 1;
+              ++rb;
+            }
+            rbq[q] = rb;
+            kbq[q] = rem;
+          }
+          Frag<IO> Bf[kGrp][NS], Cf[kGrp][NS];
+          float4 kt[kGrp][4];
+          float lq[kGrp];
+#pragma unroll
+          for (int q = 0; q < kGrp; ++q) {
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+              const IO* br = bf.sB + (16 * kbq[q] + c) * LDN + 32 * ns + 4 * g;
+              const IO* cr = bf.sC + (16 * rbq[q] + c) * LDN + 32 * ns + 4 * g;
+              Bf[q][ns].load44(br, br + 16);
+              Cf[q][ns].load44(cr, cr + 16);
+            }
+            const int tq = (16 * rbq[q] + c) >> lgR;
+            lq[q] = co.sTok[tq < Q ? tq : Q - 1].z;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int tk = (16 * kbq[q] + 4 * g + i4) >> lgR;
+              kt[q][i4] = co.sTok[tk < Q ? tk : Q - 1];
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < kGrp; ++q) {
+            f32x4 St = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) mma(St, Bf[q][ns], Cf[q][ns]);
+            const int rq = 16 * rbq[q] + c, tq = rq >> lgR;
+            float v[4];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int rk = 16 * kbq[q] + 4 * g + i4, tk = rk >> lgR;
+              float m = (tk <= tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].x) : 0.f;
+              m += (tk < tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].y) : 0.f;
+              v[i4] = St[i4] * m + ((rk == rq) ? Dh : 0.f);
+            }
+            if (okq[q]) store4(sSM + rq * ldr + 16 * kbq[q] + 4 * g, v);
+          }
+        }
+      }
+      __syncthreads();
+      // ---- phase 2: outputs and state update for this wave's p-blocks ----
       if (i > ck0) {
         const int j = i - 1;
         const int c0 = j * Q, Lc = chunk_len(j);
         const PcBuf<IO, N, P> bf = getbuf(j);
         const PcCoef co = getcoef(j);
         const bool last_chunk = j == ck1 - 1;
-        constexpr int nks = KSM;  // tiles hold RMAX rows; padding rows are zero
-        constexpr int nrb = RBM;
 #pragma unroll
         for (int u = 0; u < PBW; ++u) {
           const int pb = cw + kConsWaves * u;
@@ -558,98 +669,40 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
                 Hf[ns].set(i4, Hreg[u][2 * ns][i4]);
                 Hf[ns].set(4 + i4, (2 * ns + 1 < NB) ? Hreg[u][(2 * ns + 1 < NB) ? 2 * ns + 1 : 0][i4] : 0.f);
               }
-            f32x4 acc[RBM];
-            float lq[RBM];
+            Frag<IO> Xf[KSM];
 #pragma unroll
-            for (int rb = 0; rb < RBM; ++rb) {
-              acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-              const int tq = (16 * rb + c) >> lgR;
-              lq[rb] = co.sTok[tq < Q ? tq : Q - 1].z;
+            for (int ks = 0; ks < KSM; ++ks) {
+              const IO* xr = bf.sXt + (16 * pb + c) * ldr + 32 * ks + 4 * g;
+              Xf[ks].load44(xr, xr + 16);
             }
-            // key slabs ks (rows 32ks .. 32ks+31), query row blocks rb >= 2ks;
-            // loop bounds are compile-time so causal skipping costs nothing
-#pragma unroll
-            for (int ks = 0; ks < RBM / 2; ++ks) {
-              if (ks < nks) {
-                Frag<IO> Bf[2][NS];
-                float kA[2][4], kB[2][4];
-                int tk[2][4];
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                  const int kb = 2 * ks + h2;
-#pragma unroll
-                  for (int ns = 0; ns < NS; ++ns) {
-                    const IO* br = bf.sB + (16 * kb + c) * LDN + 32 * ns + 4 * g;
-                    Bf[h2][ns].load44(br, br + 16);
-                  }
-#pragma unroll
-                  for (int i4 = 0; i4 < 4; ++i4) {
-                    tk[h2][i4] = (16 * kb + 4 * g + i4) >> lgR;
-                    const float4 kt = co.sTok[tk[h2][i4] < Q ? tk[h2][i4] : Q - 1];
-                    kA[h2][i4] = kt.x;
-                    kB[h2][i4] = kt.y;
-                  }
-                }
-                Frag<IO> Xf;
-                {
-                  const IO* xr = bf.sXt + (16 * pb + c) * ldr + 32 * ks + 4 * g;
-                  Xf.load44(xr, xr + 16);
-                }
-#pragma unroll
-                for (int rb = 2 * ks; rb < RBM; ++rb) {
-                  if (rb < nrb) {
-                    Frag<IO> Cf[NS];
-#pragma unroll
-                    for (int ns = 0; ns < NS; ++ns) {
-                      const IO* cr = bf.sC + (16 * rb + c) * LDN + 32 * ns + 4 * g;
-                      Cf[ns].load44(cr, cr + 16);
-                    }
-                    if (ks == 0) {
-#pragma unroll
-                      for (int ns = 0; ns < NS; ++ns) mma(acc[rb], Hf[ns], Cf[ns]);
-                      acc[rb] = acc[rb] * __builtin_amdgcn_exp2f(lq[rb]);
-                    }
-                    const int tq = (16 * rb + c) >> lgR;
-                    f32x4 St[2];
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                      St[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-                      if (2 * ks + h2 <= rb) {
-#pragma unroll
-                        for (int ns = 0; ns < NS; ++ns) mma(St[h2], Bf[h2][ns], Cf[ns]);
-                      }
-                    }
-                    Frag<IO> SM;
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                      const int kb = 2 * ks + h2;
-#pragma unroll
-                      for (int i4 = 0; i4 < 4; ++i4) {
-                        float v = 0.f;
-                        if (kb <= rb) {
-                          const int tkv = tk[h2][i4];
-                          float m = (tkv <= tq) ? __builtin_amdgcn_exp2f(lq[rb] - kA[h2][i4]) : 0.f;
-                          m += (tkv < tq) ? __builtin_amdgcn_exp2f(lq[rb] - kB[h2][i4]) : 0.f;
-                          v = St[h2][i4] * m;
-                          if (kb == rb) v += (4 * g + i4 == c) ? Dh : 0.f;  // skip term D x
-                        }
-                        SM.set(4 * h2 + i4, v);
-                      }
-                    }
-                    mma(acc[rb], Xf, SM);
-                  }
-                }
-              }
-            }
-            // store y (token t = row 16rb + c, columns 16pb + 4g .. +3)
 #pragma unroll
             for (int rb = 0; rb < RBM; ++rb) {
               const int rho = 16 * rb + c;
-              const int t = rho >> lgR, r = rho & (R - 1);
-              if (rb < nrb && rho < rows && t < Lc) {
-                const float v[4] = {acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]};
-                store4(Yg + (size_t)(c0 + t) * tokX + r * P + 16 * pb + 4 * g, v);
+              f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+              {
+                Frag<IO> Cf[NS];
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) {
+                  const IO* cr = bf.sC + rho * LDN + 32 * ns + 4 * g;
+                  Cf[ns].load44(cr, cr + 16);
+                }
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) mma(acc, Hf[ns], Cf[ns]);
+                const int tq = rho >> lgR;
+                acc = acc * __builtin_amdgcn_exp2f(co.sTok[tq < Q ? tq : Q - 1].z);
               }
+#pragma unroll
+              for (int ks = 0; ks < KSM; ++ks) {
+                if (2 * ks <= rb) {
+                  Frag<IO> SMf;
+                  const IO* sr = sSM + rho * ldr + 32 * ks + 4 * g;
+                  SMf.load44(sr, sr + 16);
+                  mma(acc, Xf[ks], SMf);
+                }
+              }
+              // y (row rho, columns 16pb + 4g .. +3) into the output tile
+              const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+              store4(sY + rho * ldy + 16 * pb + 4 * g, v);
             }
           }
           // state update and rotation into the next chunk's frame
@@ -702,6 +755,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
       __syncthreads();
     }
+    if (has_y && ck1 > ck0) store_y(ck1 - 1);
   }
 
   if (writes_final) {
