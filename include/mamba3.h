@@ -71,7 +71,10 @@ typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
  *   headdim P in {16, 32, 64, 128},
  *   dstate  N in {16, 32, 64, 128}  (N/2 complex pairs),
  *   rank    R in {1, 2, 4}          (1 = SISO, >1 = MIMO),
- *   chunk   Q in {16, 32, 64}       (prefill block length; Q*R <= 256),
+ *   chunk   Q in {16, 32, 64}       (prefill block length; Q*R <= 256; the
+ *                                    result does not depend on it, and the
+ *                                    library may tile with Q/2 or Q/4 when
+ *                                    Q*R rows do not fit its tiles),
  *   io_dtype in m3_dtype.
  * Anything else returns M3_ERR_UNSUPPORTED (or M3_ERR_SHAPE for values <= 0). */
 typedef struct {

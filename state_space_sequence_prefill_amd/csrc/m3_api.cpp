@@ -207,6 +207,7 @@ int mamba3_prefill_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* 
   if (st != M3_OK) return st;
   if (!bytes) return fail(M3_ERR_NULL, "bytes is NULL");
   if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
+  m.Q = m3::prefill_tile_chunk(m);
   int nseg = 1, sc = 0;
   if (seqlen > 0) plan_segments(m, seqlen, &nseg, &sc);
   *bytes = workspace_for(m, nseg);
@@ -223,6 +224,7 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
   if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
   if ((st = check_state(state, "state")) != M3_OK) return st;
   if (seqlen == 0) return ok();
+  m.Q = m3::prefill_tile_chunk(m);
   if ((int64_t)seqlen * m.batch * m.heads * m.R * (m.N > m.P ? m.N : m.P) > ((int64_t)1 << 40))
     return fail(M3_ERR_UNSUPPORTED, "problem too large for 40-bit element offsets");
   if ((int64_t)m.Q * m.heads * m.R * (m.N > m.P ? m.N : m.P) >= ((int64_t)1 << 31))

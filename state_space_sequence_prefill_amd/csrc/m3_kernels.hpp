@@ -63,6 +63,8 @@ bool prefill_supported(const Dims& d);
 // Producer/consumer prefill (m3_prefill_pc.hip): used for every pass whose
 // double-buffered tiles fit; `mode` 0 fused, 1 segment summaries, 2 segments.
 bool prefill_pc_supported(const Dims& d);
+// Chunk length the prefill kernels tile with (<= d.Q; see m3_prefill.hip).
+int prefill_tile_chunk(const Dims& d);
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
 
 }  // namespace m3

@@ -807,6 +807,20 @@ bool prefill_supported(const Dims& d) {
   return prefill_pc_supported(d) || rows_pad <= (d.bf16 ? max_rows<bf16>(d) : max_rows<float>(d));
 }
 
+int prefill_tile_chunk(const Dims& d) {
+  // The chunk length is a tile height: the chunked form gives the same result
+  // for any chunk length.  When Q*R rows do not fit the producer/consumer
+  // kernel's tiles, halve the chunk (down to 16 tokens) rather than fall back
+  // to the single-role kernel.
+  if (prefill_pc_supported(d)) return d.Q;
+  for (int q = d.Q / 2; q >= 16; q /= 2) {
+    Dims e = d;
+    e.Q = q;
+    if (prefill_pc_supported(e)) return q;
+  }
+  return d.Q;
+}
+
 hipError_t launch_prefill(const Dims& d, const PrefillArgs& a, hipStream_t s) {
   return d.bf16 ? launch_n<bf16>(d, a, s) : launch_n<float>(d, a, s);
 }
