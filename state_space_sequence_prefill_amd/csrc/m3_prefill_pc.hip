@@ -343,8 +343,15 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const float L2 = ellv * kLog2ePc;
       const float Ak = (valid && gam > 0.f) ? L2 - __log2f(gam) : inf;
       const float Bk = (valid && betn > 0.f) ? elln * kLog2ePc - __log2f(betn) : inf;
+      // key factor for score blocks below the diagonal: with e the last token
+      // of the key's 16-row block, M[q][k] = 2^{L_q - L_e} * Kf_k for every
+      // query q after that block (both factors <= 1 except Kf's beta term at
+      // k = e, which is 1/alpha of the next token)
+      const int te = t | ((16 >> lgR) - 1);
+      const float Le = __shfl(L2, te < Lc ? te : Lc - 1, kWave);
+      const float Kf = valid ? gam * exp2f(Le - L2) + betn * exp2f(Le - elln * kLog2ePc) : 0.f;
       if (store && t < Q) {
-        co.sTok[t] = make_float4(Ak, Bk, L2, 0.f);
+        co.sTok[t] = make_float4(Ak, Bk, L2, Kf);
         co.sW[t] = w;
         if (t == 0) {
           co.sMisc[0] = ellE;
@@ -396,8 +403,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         for (int k = 0; k < 4; ++k) {
           const int rho = 4 * rg + k;
           const int t = rtok[m][k];
+          // rows past the chunk hold finite duplicates (clamped loads); every
+          // use of them is weighted by an exact zero (mask, w) or never stored
           const bool valid = t < Lc;
-          const float vm = valid ? 1.f : 0.f;  // zero padding rows through the rotation
           float bv[8], cv[8];
           rs.b[m][k].unpack(bv);
           rs.c[m][k].unpack(cv);
@@ -406,8 +414,8 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           for (int j = 0; j < 4; ++j) {
             float sn, cs;
             trig<IO>(ph[k][j], sn, cs);
-            cs4[j] = cs * vm;
-            sn4[j] = sn * vm;
+            cs4[j] = cs;
+            sn4[j] = sn;
             rot2(bv[2 * j], bv[2 * j + 1], cs4[j], -sn4[j]);
             rot2(cv[2 * j], cv[2 * j + 1], cs4[j], -sn4[j]);
           }
@@ -439,11 +447,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           // transpose 4 rows x 8 bf16 columns with byte permutes (no unpack)
           uint32_t w[4][4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t keep = xtok[m][k] < Lc ? 0xffffffffu : 0u;
+          for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w[k][q] = rs.x[m][k].w[q] & keep;
-          }
+            for (int q = 0; q < 4; ++q) w[k][q] = rs.x[m][k].w[q];
           uint2 v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -458,12 +464,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         } else {
           float xv[4][8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float vm = xtok[m][k] < Lc ? 1.f : 0.f;
-            rs.x[m][k].unpack(xv[k]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xv[k][e] *= vm;
-          }
+          for (int k = 0; k < 4; ++k) rs.x[m][k].unpack(xv[k]);
           if (xst[m]) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -611,7 +612,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           }
           Frag<IO> Bf[kGrp][NS], Cf[kGrp][NS];
           float4 kt[kGrp][4];
-          float lq[kGrp];
+          float lq[kGrp], le[kGrp];
 #pragma unroll
           for (int q = 0; q < kGrp; ++q) {
 #pragma unroll
@@ -623,6 +624,8 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             }
             const int tq = (16 * rbq[q] + c) >> lgR;
             lq[q] = co.sTok[tq < Q ? tq : Q - 1].z;
+            const int tkl = (16 * kbq[q] + 15) >> lgR;  // last token of the key block
+            le[q] = co.sTok[tkl < Q ? tkl : Q - 1].z;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               const int tk = (16 * kbq[q] + 4 * g + i4) >> lgR;
@@ -636,12 +639,20 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             for (int ns = 0; ns < NS; ++ns) mma(St, Bf[q][ns], Cf[q][ns]);
             const int rq = 16 * rbq[q] + c, tq = rq >> lgR;
             float v[4];
+            if (kbq[q] < rbq[q]) {
+              // below the diagonal every key precedes every query: one row
+              // factor 2^{L_q - L_e} times the key factors
+              const float rf = __builtin_amdgcn_exp2f(lq[q] - le[q]);
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              const int rk = 16 * kbq[q] + 4 * g + i4, tk = rk >> lgR;
-              float m = (tk <= tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].x) : 0.f;
-              m += (tk < tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].y) : 0.f;
-              v[i4] = St[i4] * m + ((rk == rq) ? Dh : 0.f);
+              for (int i4 = 0; i4 < 4; ++i4) v[i4] = St[i4] * (rf * kt[q][i4].w);
+            } else {
+#pragma unroll
+              for (int i4 = 0; i4 < 4; ++i4) {
+                const int rk = 16 * kbq[q] + 4 * g + i4, tk = rk >> lgR;
+                float m = (tk <= tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].x) : 0.f;
+                m += (tk < tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].y) : 0.f;
+                v[i4] = St[i4] * m + ((rk == rq) ? Dh : 0.f);
+              }
             }
             if (okq[q]) store4(sSM + rq * ldr + 16 * kbq[q] + 4 * g, v);
           }
