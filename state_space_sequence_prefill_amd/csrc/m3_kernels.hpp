@@ -58,6 +58,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 bool decode_supported(const Dims& d);
+// Rank >= 2 decode on the matrix cores (m3_decode_mimo.hip).
+bool decode_mimo_supported(const Dims& d);
+hipError_t launch_decode_mimo(const Dims& d, const DecodeArgs& a, hipStream_t s);
 bool prefill_supported(const Dims& d);
 
 // Producer/consumer prefill (m3_prefill_pc.hip): used for every pass whose
