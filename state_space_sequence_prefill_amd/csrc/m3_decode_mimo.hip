@@ -221,6 +221,8 @@ hipError_t launch_mimo_n(const Dims& d, const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 bool decode_mimo_supported(const Dims& d) {
+  // rank 1 stays on the VALU kernel (measured faster: its readout would use
+  // one row of sixteen in the matrix product)
   if (!(d.R == 2 || d.R == 4)) return false;
   if (!(d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128)) return false;
   if (!(d.P == 16 || d.P == 32 || d.P == 64 || d.P == 128)) return false;
