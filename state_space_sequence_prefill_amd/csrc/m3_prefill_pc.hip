@@ -616,11 +616,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 #pragma unroll
           for (int q = 0; q < kGrp; ++q) {
 #pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-              const IO* br = bf.sB + (16 * kbq[q] + c) * LDN + 32 * ns + 4 * g;
-              const IO* cr = bf.sC + (16 * rbq[q] + c) * LDN + 32 * ns + 4 * g;
-              Bf[q][ns].load44(br, br + 16);
-              Cf[q][ns].load44(cr, cr + 16);
+            for (int ns = 0; ns < NS; ++ns) {  // K = n in natural order (one 16-byte read each)
+              Bf[q][ns].load8(bf.sB + (16 * kbq[q] + c) * LDN + 32 * ns + 8 * g);
+              Cf[q][ns].load8(bf.sC + (16 * rbq[q] + c) * LDN + 32 * ns + 8 * g);
             }
             const int tq = (16 * rbq[q] + c) >> lgR;
             lq[q] = co.sTok[tq < Q ? tq : Q - 1].z;
@@ -680,12 +678,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
                 Hf[ns].set(i4, Hreg[u][2 * ns][i4]);
                 Hf[ns].set(4 + i4, (2 * ns + 1 < NB) ? Hreg[u][(2 * ns + 1 < NB) ? 2 * ns + 1 : 0][i4] : 0.f);
               }
-            Frag<IO> Xf[KSM];
+            Frag<IO> Xf[KSM];  // K = keys in natural order, as the score rows below
 #pragma unroll
-            for (int ks = 0; ks < KSM; ++ks) {
-              const IO* xr = bf.sXt + (16 * pb + c) * ldr + 32 * ks + 4 * g;
-              Xf[ks].load44(xr, xr + 16);
-            }
+            for (int ks = 0; ks < KSM; ++ks) Xf[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
 #pragma unroll
             for (int rb = 0; rb < RBM; ++rb) {
               const int rho = 16 * rb + c;
@@ -706,8 +701,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
               for (int ks = 0; ks < KSM; ++ks) {
                 if (2 * ks <= rb) {
                   Frag<IO> SMf;
-                  const IO* sr = sSM + rho * ldr + 32 * ks + 4 * g;
-                  SMf.load44(sr, sr + 16);
+                  SMf.load8(sSM + rho * ldr + 32 * ks + 8 * g);
                   mma(acc, Xf[ks], SMf);
                 }
               }
