@@ -26,11 +26,17 @@ def to_gpu(arr, io_dtype, key):
     return t.cuda().contiguous()
 
 
-def inputs_on_gpu(w, seed, long_memory=False, seqlen=None, zero_D=False):
-    """Returns (exact fp64 dict, torch dict) for workload w."""
+def inputs_on_gpu(w, seed, long_memory=False, seqlen=None, zero_D=False, dt_scale=1.0, a_scale=1.0):
+    """Returns (exact fp64 dict, torch dict) for workload w.  dt_scale and
+    a_scale stretch dt (and the dt-scaled angles) and A, e.g. for strong decay."""
     raw = syn.draw(w, seed, long_memory=long_memory, seqlen=seqlen)
     if zero_D:
         raw["D"] = np.zeros_like(raw["D"])
+    if dt_scale != 1.0:
+        raw["dt"] = raw["dt"] * dt_scale
+        raw["theta"] = raw["theta"] * dt_scale
+    if a_scale != 1.0:
+        raw["A"] = raw["A"] * a_scale
     ex = syn.as_exact(raw, w.io_dtype)
     tt = {k: to_gpu(v, w.io_dtype, k) for k, v in ex.items()}
     return ex, tt

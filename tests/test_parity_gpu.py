@@ -56,8 +56,9 @@ def make_state(w, st=None):
     return s
 
 
-def check_prefill(w, seed, pairs=None, st=None, long_memory=False, zero_D=False, tol=None):
-    ex, tt = inputs_on_gpu(w, seed, long_memory=long_memory, zero_D=zero_D)
+def check_prefill(w, seed, pairs=None, st=None, long_memory=False, zero_D=False, tol=None, dt_scale=1.0,
+                  a_scale=1.0):
+    ex, tt = inputs_on_gpu(w, seed, long_memory=long_memory, zero_D=zero_D, dt_scale=dt_scale, a_scale=a_scale)
     s = make_state(w, st)
     y = run_prefill(w, tt, s)
     if pairs is None:
@@ -170,6 +171,16 @@ def test_prefill_long_memory_and_zero_skip():
     w = W("tiny_siso_f32", batch=1, heads=4, headdim=64, dstate=64, rank=1, seqlen=300, chunk=64,
           io_dtype="bf16")
     check_prefill(w, seed=51, long_memory=True, zero_D=True)
+
+
+@pytest.mark.parametrize("io,R", [("bf16", 1), ("bf16", 4), ("f32", 2)])
+def test_prefill_strong_decay(io, R):
+    """Per-token decay down to ~e^-40 (dt x 8, |A| x 8): the decay factors of
+    a chunk span hundreds of e-folds, which must underflow to exact zeros and
+    never overflow (below-diagonal score blocks use factored row/key terms)."""
+    w = W("tiny_siso_f32", batch=1, heads=3, headdim=32, dstate=32, rank=R, seqlen=200, chunk=64 // R,
+          io_dtype=io)
+    check_prefill(w, seed=71, st=syn.draw_state(w, 72), dt_scale=8.0, a_scale=8.0)
 
 
 def test_prefill_segment_path_small():
