@@ -84,18 +84,38 @@ def zero_state(batch, H, P, N, R):
     )
 
 
-def discretize(dt, lam, A):
-    """Per-token coefficients of the exponential-trapezoid update.
+# Discretisation rules (the integers are the library's m3_disc values).
+EXP_TRAPEZOID = 0      # Mamba-3's rule (the default)
+DECAYED_TRAPEZOID = 1  # textbook trapezoid: the previous input decays with the state
+EXP_EULER = 2          # Mamba-2's first-order rule
 
-    lilting.ch Mamba-3 article, "1. 指数台形離散化": the second-order rule
-    weights the current input by lam*dt and the previous input by (1-lam)*dt;
-    the state decays by exp(dt*A).  With lam = 1 this is Mamba-2's exponential
-    Euler step (same article, comparison table).
-    dt, lam: (..., H); A: (H,).  Returns alpha, beta, gamma of shape (..., H).
+
+def discretize(dt, lam, A, disc=EXP_TRAPEZOID):
+    """Per-token coefficients (alpha, beta, gamma) of the update
+    h = Rot(theta)(alpha h + beta u_prev) + gamma u.
+
+    lilting.ch Mamba-3 article, "1. 指数台形離散化" and its table of
+    discretisation methods, and the table "Mamba-2とMamba-3の比較":
+    * EXP_TRAPEZOID (Mamba-3): second order, the current input weighted by
+      lam*dt and the previous one by (1-lam)*dt; the state decays by exp(dt*A).
+    * DECAYED_TRAPEZOID: the textbook trapezoid, where the previous input is
+      carried through the transition too: beta = exp(dt*A) (1-lam) dt.
+    * EXP_EULER (Mamba-2): first order, current input only: beta = 0,
+      gamma = dt (lam is ignored).
+    dt, lam: (..., H); A: (H,).  Returns arrays of shape (..., H).
     """
     alpha = np.exp(dt * A)
-    beta = (1.0 - lam) * dt
-    gamma = lam * dt
+    if disc == EXP_TRAPEZOID:
+        beta = (1.0 - lam) * dt
+        gamma = lam * dt
+    elif disc == DECAYED_TRAPEZOID:
+        beta = alpha * (1.0 - lam) * dt
+        gamma = lam * dt
+    elif disc == EXP_EULER:
+        beta = np.zeros_like(alpha)
+        gamma = dt * np.ones_like(alpha)
+    else:
+        raise ValueError(f"unknown discretisation {disc!r}")
     return alpha, beta, gamma
 
 
@@ -139,9 +159,9 @@ def _init(state, batch, H, P, N, R):
             np.array(xp, dtype=np.float64, copy=True))
 
 
-def _step(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D):
+def _step(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D, disc=EXP_TRAPEZOID):
     """One token of the definition; all arrays carry leading (batch, H)."""
-    alpha, beta, gamma = discretize(dt_t, lam_t, A)
+    alpha, beta, gamma = discretize(dt_t, lam_t, A, disc)
     G = alpha[..., None, None] * h + beta[..., None, None] * _outer_sum(xp, Bp)
     h = rot_pairs(G, th_t[:, :, None, :])
     h = h + gamma[..., None, None] * _outer_sum(x_t, B_t)
@@ -149,7 +169,7 @@ def _step(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D):
     return h, y
 
 
-def prefill(x, Bm, Cm, dt, lam, theta, A, D, state=None):
+def prefill(x, Bm, Cm, dt, lam, theta, A, D, state=None, disc=EXP_TRAPEZOID):
     """The definition, token by token in the lab frame.
 
     Returns y (batch, T, H, R, P) and the final state (h, B_prev, x_prev).
@@ -160,12 +180,12 @@ def prefill(x, Bm, Cm, dt, lam, theta, A, D, state=None):
     y = np.zeros((batch, T, H, R, P))
     for t in range(T):
         h, y[:, t] = _step(h, Bp, xp, x[:, t], Bm[:, t], Cm[:, t],
-                           dt[:, t], lam[:, t], theta[:, t], A, D)
+                           dt[:, t], lam[:, t], theta[:, t], A, D, disc)
         Bp, xp = np.array(Bm[:, t], dtype=np.float64), np.array(x[:, t], dtype=np.float64)
     return y, (h, Bp, xp)
 
 
-def decode_step(x, Bm, Cm, dt, lam, theta, A, D, state):
+def decode_step(x, Bm, Cm, dt, lam, theta, A, D, state, disc=EXP_TRAPEZOID):
     """One recurrent step for one new token per (batch, head).
 
     x (batch, H, R, P); Bm, Cm (batch, H, R, N); dt, lam (batch, H);
@@ -174,11 +194,11 @@ def decode_step(x, Bm, Cm, dt, lam, theta, A, D, state):
     batch, H, R, P = x.shape
     N = Bm.shape[-1]
     h, Bp, xp = _init(state, batch, H, P, N, R)
-    h, y = _step(h, Bp, xp, x, Bm, Cm, dt, lam, theta, A, D)
+    h, y = _step(h, Bp, xp, x, Bm, Cm, dt, lam, theta, A, D, disc)
     return y, (h, np.array(Bm, dtype=np.float64), np.array(x, dtype=np.float64))
 
 
-def prefill_rotated_frame(x, Bm, Cm, dt, lam, theta, A, D, state=None):
+def prefill_rotated_frame(x, Bm, Cm, dt, lam, theta, A, D, state=None, disc=EXP_TRAPEZOID):
     """Same recurrence written with cumulative angles on B and C.
 
     lilting.ch Mamba-3 article, "2. 複素数値状態" (RoPE trick) and perforder.com
@@ -200,7 +220,7 @@ def prefill_rotated_frame(x, Bm, Cm, dt, lam, theta, A, D, state=None):
         Phi = Phi + theta[:, t]
         B_til = rot_pairs(Bm[:, t], -Phi[:, :, None, :])
         C_til = rot_pairs(Cm[:, t], -Phi[:, :, None, :])
-        alpha, beta, gamma = discretize(dt[:, t], lam[:, t], A)
+        alpha, beta, gamma = discretize(dt[:, t], lam[:, t], A, disc)
         g = (alpha[..., None, None] * g
              + beta[..., None, None] * _outer_sum(xp, Bp_til)
              + gamma[..., None, None] * _outer_sum(x[:, t], B_til))
@@ -211,7 +231,7 @@ def prefill_rotated_frame(x, Bm, Cm, dt, lam, theta, A, D, state=None):
     return y, (h, np.array(Bp, dtype=np.float64), xp)
 
 
-def prefill_complex(x, Bm, Cm, dt, lam, theta, A, D, state=None):
+def prefill_complex(x, Bm, Cm, dt, lam, theta, A, D, state=None, disc=EXP_TRAPEZOID):
     """Same recurrence in complex128 arithmetic.
 
     lilting.ch Mamba-3 article, "2. 複素数値状態" and its state-type table: N
@@ -231,7 +251,7 @@ def prefill_complex(x, Bm, Cm, dt, lam, theta, A, D, state=None):
     bp = cplx(Bp)                    # (b, H, R, N/2)
     y = np.zeros((batch, T, H, R, P))
     for t in range(T):
-        alpha, beta, gamma = discretize(dt[:, t], lam[:, t], A)
+        alpha, beta, gamma = discretize(dt[:, t], lam[:, t], A, disc)
         rot = np.exp(1j * theta[:, t])[:, :, None, :]          # (b, H, 1, N/2)
         bt = cplx(Bm[:, t])
         ct = cplx(Cm[:, t])
@@ -251,7 +271,7 @@ def prefill_complex(x, Bm, Cm, dt, lam, theta, A, D, state=None):
     return y, (h_out, Bp_out, xp)
 
 
-def prefill_chunked(x, Bm, Cm, dt, lam, theta, A, D, state=None, chunk=64):
+def prefill_chunked(x, Bm, Cm, dt, lam, theta, A, D, state=None, chunk=64, disc=EXP_TRAPEZOID):
     """Chunked (block) evaluation of the same recurrence.
 
     This is the "dual", matmul-shaped form that lets a parallel prefill use
@@ -290,7 +310,7 @@ def prefill_chunked(x, Bm, Cm, dt, lam, theta, A, D, state=None, chunk=64):
                 L = e - c0
                 a = dt[b, c0:e, hd] * A[hd]
                 cs = np.cumsum(a)
-                _, beta, gamma = discretize(dt[b, c0:e, hd], lam[b, c0:e, hd], A[hd])
+                _, beta, gamma = discretize(dt[b, c0:e, hd], lam[b, c0:e, hd], A[hd], disc)
                 phi = np.cumsum(theta[b, c0:e, hd], axis=0)           # (L, N/2)
                 Bt = rot_pairs(Bm[b, c0:e, hd], -phi[:, None, :])    # (L, R, N)
                 Ct = rot_pairs(Cm[b, c0:e, hd], -phi[:, None, :])

@@ -74,7 +74,19 @@ def pin_hand_worked():
     return worst
 
 
-def pin_lfilter(lam_value=None, theta_zero=False, seed=7):
+def _coefs(disc, dt0, lam0, A0):
+    """(alpha, beta, gamma) of each rule for constant parameters, written out
+    from the rule's description (lilting.ch Mamba-3 article, "1. 指数台形離散化"
+    and the table "Mamba-2とMamba-3の比較")."""
+    alpha = np.exp(dt0 * A0)
+    if disc == oracle.EXP_TRAPEZOID:      # both inputs weighted, neither decayed
+        return alpha, (1 - lam0) * dt0, lam0 * dt0
+    if disc == oracle.DECAYED_TRAPEZOID:  # previous input carried through the transition
+        return alpha, alpha * (1 - lam0) * dt0, lam0 * dt0
+    return alpha, 0.0, dt0                # exponential Euler: current input only
+
+
+def pin_lfilter(lam_value=None, theta_zero=False, seed=7, disc=0):
     """Constant dt, lam, theta and A: each complex pair of each state row is a
     first-order complex IIR filter of the (time-varying) input u_t = b_t x_t:
         z_t = a z_{t-1} + gamma u_t + beta e^{i theta} u_{t-1},  a = alpha e^{i theta}
@@ -92,11 +104,9 @@ def pin_lfilter(lam_value=None, theta_zero=False, seed=7):
     dt = np.full((1, T, 1), dt0)
     lam = np.full((1, T, 1), lam0)
     th = np.broadcast_to(th0, (1, T, 1, N // 2)).copy()
-    y, (h, _, _) = oracle.prefill(x, Bm, Cm, dt, lam, th, A, D)
+    y, (h, _, _) = oracle.prefill(x, Bm, Cm, dt, lam, th, A, D, disc=disc)
 
-    alpha = np.exp(dt0 * A[0])
-    beta = (1 - lam0) * dt0
-    gamma = lam0 * dt0
+    alpha, beta, gamma = _coefs(disc, dt0, lam0, A[0])
     b = Bm[0, :, 0, :, 0::2] + 1j * Bm[0, :, 0, :, 1::2]          # (T,R,N/2)
     c = Cm[0, :, 0, :, 0::2] + 1j * Cm[0, :, 0, :, 1::2]
     u = np.einsum("trp,trj->tpj", x[0, :, 0], b)                   # (T,P,N/2)
@@ -154,15 +164,16 @@ def pin_transition_bruteforce(seed=3):
     return worst
 
 
-def pin_mamba2_ssd(seed=11):
+def pin_mamba2_ssd(seed=11, disc=0):
     """lam = 1 and theta = 0: Mamba-2's exponential-Euler SSM (the pages'
     comparison table), whose output has the textbook structured-masked form
     y = (L o C B^T) x + D x,  L[t,s] = exp(sum_{k=s+1..t} dt_k A) dt_s, s <= t,
-    for a fresh state."""
+    for a fresh state.  The exponential-Euler rule gives that form for any lam."""
     pr, _ = rand_problem(seed, b=1, T=17, H=2, R=2, P=3, N=4, state=False)
-    pr["lam"][:] = 1.0
+    if disc != oracle.EXP_EULER:
+        pr["lam"][:] = 1.0
     pr["theta"][:] = 0.0
-    y, _ = oracle.prefill(**pr)
+    y, _ = oracle.prefill(**pr, disc=disc)
     worst = 0.0
     for hd in range(2):
         dt = pr["dt"][0, :, hd]
@@ -182,9 +193,12 @@ def pin_mamba2_ssd(seed=11):
     return worst
 
 
-def pin_geometric_series():
+def pin_geometric_series(disc=0):
     """Constant dt, lam, B, x; theta = 0; fresh state.  u = x B^T:
-    h_1 = gamma u;  h_t = alpha^{t-1} gamma u + dt u (1 - alpha^{t-1}) / (1 - alpha)."""
+    h_1 = gamma u;  h_t = alpha h_{t-1} + (beta + gamma) u, so
+    h_t = alpha^{t-1} gamma u + (beta + gamma) u (1 - alpha^{t-1}) / (1 - alpha),
+    where beta + gamma = dt for Mamba-3's rule and dt (lam + (1 - lam) alpha) for
+    the decayed (textbook) trapezoid."""
     T, P, N = 9, 2, 2
     dt0, lam0, A0 = 0.5, 0.35, -0.9
     xv = np.array([1.5, -0.5])
@@ -197,12 +211,12 @@ def pin_geometric_series():
     th = np.zeros((1, T, 1, 1))
     worst = 0.0
     alpha = np.exp(dt0 * A0)
-    gamma = lam0 * dt0
     u = np.outer(xv, bv)
     for t in range(1, T + 1):
         _, (h, _, _) = oracle.prefill(x[:, :t], Bm[:, :t], Cm[:, :t], dt[:, :t], lam[:, :t],
-                                      th[:, :t], np.array([A0]), np.array([0.0]))
-        ref = alpha ** (t - 1) * gamma * u + dt0 * u * (1 - alpha ** (t - 1)) / (1 - alpha)
+                                      th[:, :t], np.array([A0]), np.array([0.0]), disc=disc)
+        _, beta, gamma = _coefs(disc, dt0, lam0, A0)
+        ref = alpha ** (t - 1) * gamma * u + (beta + gamma) * u * (1 - alpha ** (t - 1)) / (1 - alpha)
         worst = max(worst, relerr(h[0, 0], ref))
     return worst
 
@@ -240,6 +254,11 @@ ALL_PINS = {
     "mamba2_ssd": (pin_mamba2_ssd, 1e-12),
     "geometric_series": (pin_geometric_series, 1e-12),
     "pure_rotation": (pin_pure_rotation, 1e-12),
+    # the two other discretisation rules
+    "lfilter_decayed_trapezoid": (lambda: pin_lfilter(disc=oracle.DECAYED_TRAPEZOID), 1e-12),
+    "lfilter_exp_euler": (lambda: pin_lfilter(disc=oracle.EXP_EULER), 1e-12),
+    "geometric_series_decayed_trapezoid": (lambda: pin_geometric_series(disc=oracle.DECAYED_TRAPEZOID), 1e-12),
+    "mamba2_ssd_exp_euler_any_lam": (lambda: pin_mamba2_ssd(disc=oracle.EXP_EULER), 1e-12),
 }
 
 
@@ -253,23 +272,28 @@ def test_pin(name):
 # Agreement of the formulations, chunked algebra, structure
 # ---------------------------------------------------------------------------
 
+DISCS = [0, 1, 2]  # EXP_TRAPEZOID, DECAYED_TRAPEZOID, EXP_EULER
+
+
+@pytest.mark.parametrize("disc", DISCS)
 @pytest.mark.parametrize("R,P,N", [(1, 1, 2), (1, 4, 6), (3, 2, 4), (4, 3, 8)])
-def test_formulations_agree(R, P, N):
+def test_formulations_agree(R, P, N, disc):
     pr, st = rand_problem(100 + R * 10 + N, b=2, T=21, H=2, R=R, P=P, N=N)
-    y0, s0 = oracle.prefill(**pr, state=st)
+    y0, s0 = oracle.prefill(**pr, state=st, disc=disc)
     for f in (oracle.prefill_rotated_frame, oracle.prefill_complex):
-        y1, s1 = f(**pr, state=st)
+        y1, s1 = f(**pr, state=st, disc=disc)
         assert relerr(y1, y0) < 1e-12
         for a, b in zip(s1, s0):
             assert relerr(a, b) < 1e-12
 
 
+@pytest.mark.parametrize("disc", DISCS)
 @pytest.mark.parametrize("T", [1, 7, 37, 64])
 @pytest.mark.parametrize("Q", [1, 5, 16, 64, 100])
-def test_chunked_matches_sequential(T, Q):
+def test_chunked_matches_sequential(T, Q, disc):
     pr, st = rand_problem(T * 7 + Q, b=1, T=T, H=2, R=2, P=3, N=4)
-    y0, s0 = oracle.prefill(**pr, state=st)
-    y1, s1 = oracle.prefill_chunked(**pr, state=st, chunk=Q)
+    y0, s0 = oracle.prefill(**pr, state=st, disc=disc)
+    y1, s1 = oracle.prefill_chunked(**pr, state=st, chunk=Q, disc=disc)
     assert relerr(y1, y0) < 1e-11
     for a, b in zip(s1, s0):
         assert relerr(a, b) < 1e-11
@@ -437,30 +461,30 @@ def _bad_rot_halves(v, ang):
     return out
 
 
-def _bad_disc_decayed(dt, lam, A):
-    a, b, g = OM.__dict__["_orig_disc"](dt, lam, A)
+def _bad_disc_decayed(dt, lam, A, disc=0):
+    a, b, g = OM.__dict__["_orig_disc"](dt, lam, A, disc)
     return a, b * a, g
 
 
-def _bad_disc_swapped(dt, lam, A):
-    a, b, g = OM.__dict__["_orig_disc"](dt, lam, A)
+def _bad_disc_swapped(dt, lam, A, disc=0):
+    a, b, g = OM.__dict__["_orig_disc"](dt, lam, A, disc)
     return a, g, b
 
 
-def _bad_step_unrotated_pending(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D):
-    alpha, beta, gamma = OM.discretize(dt_t, lam_t, A)
+def _bad_step_unrotated_pending(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D, disc=0):
+    alpha, beta, gamma = OM.discretize(dt_t, lam_t, A, disc)
     h = OM.rot_pairs(alpha[..., None, None] * h, th_t[:, :, None, :])
     h = h + beta[..., None, None] * OM._outer_sum(xp, Bp) + gamma[..., None, None] * OM._outer_sum(x_t, B_t)
     y = np.einsum("bhpn,bhrn->bhrp", h, C_t) + D[None, :, None, None] * x_t
     return h, y
 
 
-def _bad_step_no_skip(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D):
-    return OM.__dict__["_orig_step"](h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, 0.0 * D)
+def _bad_step_no_skip(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D, disc=0):
+    return OM.__dict__["_orig_step"](h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, 0.0 * D, disc)
 
 
-def _bad_step_transposed_readout(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D):
-    alpha, beta, gamma = OM.discretize(dt_t, lam_t, A)
+def _bad_step_transposed_readout(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A, D, disc=0):
+    alpha, beta, gamma = OM.discretize(dt_t, lam_t, A, disc)
     G = alpha[..., None, None] * h + beta[..., None, None] * OM._outer_sum(xp, Bp)
     h = OM.rot_pairs(G, th_t[:, :, None, :]) + gamma[..., None, None] * OM._outer_sum(x_t, B_t)
     Crot = OM.rot_pairs(C_t, th_t[:, :, None, :])      # reads C in the wrong frame
@@ -468,7 +492,12 @@ def _bad_step_transposed_readout(h, Bp, xp, x_t, B_t, C_t, dt_t, lam_t, th_t, A,
     return h, y
 
 
+def _bad_disc_ignored(dt, lam, A, disc=0):
+    return OM.__dict__["_orig_disc"](dt, lam, A)
+
+
 MUTANTS = {
+    "discretisation_rule_ignored": ("discretize", _bad_disc_ignored),
     "rotation_sign": ("rot_pairs", _bad_rot_sign),
     "rotation_pairing": ("rot_pairs", _bad_rot_halves),
     "decayed_previous_input": ("discretize", _bad_disc_decayed),
