@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 1
+#define M3_ABI_VERSION 2
 
 typedef enum {
   M3_OK = 0,
@@ -66,6 +66,20 @@ typedef enum {
 
 typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
 
+/* Discretisation rule: the per-token weights (alpha, beta, gamma) in
+ *     h = Rot(theta)(alpha h + beta sum_r x_prev[r] (x) B_prev[r]) + gamma sum_r x[r] (x) B[r]
+ * lilting.ch Mamba-3 article, "1. 指数台形離散化" (its table of methods) and
+ * the table "Mamba-2とMamba-3の比較".  alpha = exp(dt A) for every rule.
+ *   M3_DISC_EXP_TRAPEZOID      Mamba-3 (default): beta = (1-lam) dt, gamma = lam dt
+ *   M3_DISC_DECAYED_TRAPEZOID  textbook trapezoid, the previous input decays
+ *                              with the state: beta = alpha (1-lam) dt, gamma = lam dt
+ *   M3_DISC_EXP_EULER          Mamba-2, first order: beta = 0, gamma = dt (lam unused) */
+typedef enum {
+  M3_DISC_EXP_TRAPEZOID = 0,
+  M3_DISC_DECAYED_TRAPEZOID = 1,
+  M3_DISC_EXP_EULER = 2
+} m3_disc;
+
 /* Problem sizes.  Supported set:
  *   batch >= 1, heads >= 1 (batch*heads < 2^31 / 1024),
  *   headdim P in {16, 32, 64, 128},
@@ -75,11 +89,13 @@ typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
  *                                    result does not depend on it, and the
  *                                    library may tile with Q/2 or Q/4 when
  *                                    Q*R rows do not fit its tiles),
- *   io_dtype in m3_dtype.
+ *   io_dtype in m3_dtype,
+ *   disc in m3_disc (0, the default, when the struct is zero-initialised).
  * Anything else returns M3_ERR_UNSUPPORTED (or M3_ERR_SHAPE for values <= 0). */
 typedef struct {
   int32_t batch, heads, headdim, dstate, rank, chunk;
   int32_t io_dtype;
+  int32_t disc;
 } m3_dims;
 
 /* Recurrent state of every (batch, head), in the LAB frame (the frame of the

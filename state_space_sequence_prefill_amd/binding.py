@@ -47,7 +47,7 @@ class M3Error(RuntimeError):
 class m3_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("headdim", ctypes.c_int32),
                 ("dstate", ctypes.c_int32), ("rank", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("io_dtype", ctypes.c_int32)]
+                ("io_dtype", ctypes.c_int32), ("disc", ctypes.c_int32)]
 
 
 class m3_state(ctypes.Structure):
@@ -94,9 +94,12 @@ def _check(status):
         raise M3Error(status, lib().m3_last_error().decode(errors="replace"))
 
 
-def make_dims(batch, heads, headdim, dstate, rank=1, chunk=64, io_dtype="bf16"):
+DISC = {"exp_trapezoid": 0, "decayed_trapezoid": 1, "exp_euler": 2}
+
+
+def make_dims(batch, heads, headdim, dstate, rank=1, chunk=64, io_dtype="bf16", disc="exp_trapezoid"):
     code = {"bf16": M3_BF16, "f32": M3_F32}.get(io_dtype, io_dtype)
-    return m3_dims(batch, heads, headdim, dstate, rank, chunk, code)
+    return m3_dims(batch, heads, headdim, dstate, rank, chunk, code, DISC.get(disc, disc))
 
 
 # ----------------------------------------------------------------------------

@@ -46,6 +46,8 @@ int check_dims(const m3_dims* d, bool need_chunk, m3::Dims* out) {
     return fail(M3_ERR_UNSUPPORTED, "batch*heads = %lld exceeds 2^21",
                 (long long)((int64_t)d->batch * d->heads));
   if (d->dstate % 2) return fail(M3_ERR_UNSUPPORTED, "dstate %d is odd (N/2 complex pairs)", d->dstate);
+  if (d->disc < M3_DISC_EXP_TRAPEZOID || d->disc > M3_DISC_EXP_EULER)
+    return fail(M3_ERR_UNSUPPORTED, "disc %d is not one of m3_disc", d->disc);
   m3::Dims m;
   m.batch = d->batch;
   m.heads = d->heads;
@@ -54,6 +56,7 @@ int check_dims(const m3_dims* d, bool need_chunk, m3::Dims* out) {
   m.R = d->rank;
   m.Q = need_chunk ? d->chunk : 64;
   m.bf16 = d->io_dtype == M3_BF16;
+  m.disc = d->disc;
   const bool supported = need_chunk ? m3::prefill_supported(m) : m3::decode_supported(m);
   if (!supported)
     return fail(M3_ERR_UNSUPPORTED,
@@ -254,6 +257,7 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
   a.B_prev = state->B_prev;
   a.x_prev = state->x_prev;
   a.y = y;
+  a.disc = m.disc;
   a.seqlen = seqlen;
   a.nseg = nseg;
   a.seg_chunks = sc;
@@ -296,6 +300,7 @@ int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const 
   a.B_prev = state->B_prev;
   a.x_prev = state->x_prev;
   a.y = y;
+  a.disc = m.disc;
   return hip_status(m3::launch_decode(m, a, static_cast<hipStream_t>(stream)), "mamba3_decode_step");
 }
 

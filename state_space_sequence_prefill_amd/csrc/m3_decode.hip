@@ -247,8 +247,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
 
   // ---- 2. per-lane operands at columns 4*n4 .. 4*n4+3 for every rank
   const float alpha = expf(dt * Ah);
-  const float beta = (1.0f - lam) * dt;
-  const float gamma = lam * dt;
+  const float2 wt = input_weights(dt, lam, alpha, a.disc);
+  const float beta = wt.x, gamma = wt.y;
   const float2 th = *reinterpret_cast<const float2*>(sTh + 2 * n4);
   float s0, c0, s1, c1;
   sincosf(th.x, &s0, &c0);

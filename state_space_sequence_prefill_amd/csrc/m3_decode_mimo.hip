@@ -117,8 +117,8 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   // ---- 2. derived fp32 operands (whole workgroup)
   {
     const float alpha = expf(dt * Ah);
-    const float beta = (1.0f - lam) * dt;
-    const float gamma = lam * dt;
+    const float2 wt = input_weights(dt, lam, alpha, a.disc);
+    const float beta = wt.x, gamma = wt.y;
     for (int j = tid; j < N / 2; j += nthr) {
       float s, co;
       sincosf(sTh[j], &s, &co);

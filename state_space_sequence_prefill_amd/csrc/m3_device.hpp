@@ -55,6 +55,18 @@ __device__ __forceinline__ void rot2(float& a, float& b, float c, float s) {
   b = nb;
 }
 
+// Previous- and current-input weights (beta, gamma) of one token under the
+// discretisation rule `disc` (m3_disc); alpha = exp(dt A) of the same token.
+// lilting.ch Mamba-3 article, "1. 指数台形離散化": Mamba-3's rule weights the
+// previous input by (1-lam) dt and the current one by lam dt; the textbook
+// trapezoid also decays the previous input by alpha; Mamba-2's exponential
+// Euler step keeps only the current input, weighted by dt.
+__device__ __forceinline__ float2 input_weights(float dt, float lam, float alpha, int disc) {
+  if (disc == 2) return make_float2(0.0f, dt);
+  const float b = (1.0f - lam) * dt;
+  return make_float2(disc == 1 ? alpha * b : b, lam * dt);
+}
+
 // Lane-crossing helpers (wave64).
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, kWave);

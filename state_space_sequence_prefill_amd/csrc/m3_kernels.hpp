@@ -11,6 +11,7 @@ namespace m3 {
 struct Dims {
   int batch, heads, P, N, R, Q;
   bool bf16;
+  int disc;  // m3_disc
 };
 
 // Arguments of one decode step (see mamba3_decode_step in include/mamba3.h).
@@ -27,6 +28,7 @@ struct DecodeArgs {
   void* B_prev;
   void* x_prev;
   void* y;
+  int disc;  // m3_disc
 };
 
 // Arguments of one prefill pass over tokens [0, seqlen) of every chain.
@@ -43,6 +45,7 @@ struct PrefillArgs {
   void* B_prev;   // pending B (batch, heads, R, N), in/out
   void* x_prev;   // pending x (batch, heads, R, P), in/out
   void* y;
+  int disc;  // m3_disc
   int seqlen;
   // Segment path (long prompts, few chains).  nseg == 1: plain fused pass.
   int nseg;        // number of segments the sequence is split into

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
       const float dt0 = DTg[(size_t)ck0 * Q * H];
       const float lm0 = LMg[(size_t)ck0 * Q * H];
       alpha0 = expf(dt0 * Ah);
-      beta0 = (1.0f - lm0) * dt0;
+      beta0 = input_weights(dt0, lm0, alpha0, a.disc).x;
     }
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
@@ -324,13 +324,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
       const float dtv = valid ? pf_dt : 0.f, lmv = valid ? pf_lm : 0.f;
       const float av = (valid && t > 0) ? dtv * Ah : 0.f;
       const float ell = wave_inclusive_scan(av);   // l_t (first token's decay is in E)
-      const float gam = lmv * dtv;
-      const float bet = (1.0f - lmv) * dtv;
+      const float2 wt = input_weights(dtv, lmv, expf(dtv * Ah), a.disc);
+      const float bet = wt.x, gam = wt.y;
       const float dtn = fold_next ? pf_dtn : 0.f;
       const float lmn = fold_next ? pf_lmn : 0.f;
       const float ell_last = __shfl(ell, Lc - 1, kWave);
       const float ellE = ell_last + dtn * Ah;
-      const float bet_next_tok = (1.0f - lmn) * dtn;
+      const float bet_next_tok = input_weights(dtn, lmn, expf(dtn * Ah), a.disc).x;
       const float bet_up = __shfl_down(bet, 1, kWave);
       const float ell_up = __shfl_down(ell, 1, kWave);
       float betn, elln;
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a, int ba
     const float dt0 = a.dt[(size_t)b * a.seqlen * H + hh];
     const float lm0 = a.lam[(size_t)b * a.seqlen * H + hh];
     const float alpha0 = expf(dt0 * a.A[hh]);
-    const float beta0 = (1.0f - lm0) * dt0;
+    const float beta0 = input_weights(dt0, lm0, alpha0, a.disc).x;
     const float* hp = a.h + ((size_t)chain * P + p) * N + 2 * j;
     e0r = alpha0 * hp[0];
     e0i = alpha0 * hp[1];

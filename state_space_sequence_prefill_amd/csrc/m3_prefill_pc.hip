@@ -327,15 +327,15 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const float dtv = valid ? rdt : 0.f, lmv = valid ? rlm : 0.f;
       const float av = (valid && t > 0) ? dtv * Ah : 0.f;
       const float ell = wave_inclusive_scan(av);
-      const float gam = lmv * dtv;
-      const float bet = (1.0f - lmv) * dtv;
+      const float2 wt = input_weights(dtv, lmv, expf(dtv * Ah), a.disc);
+      const float bet = wt.x, gam = wt.y;
       const float dtn = fold_next ? rdtn : 0.f, lmn = fold_next ? rlmn : 0.f;
       const float ell_last = __shfl(ell, Lc - 1, kWave);
       const float ellE = ell_last + dtn * Ah;
       const float bet_up = __shfl_down(bet, 1, kWave);
       const float ell_up = __shfl_down(ell, 1, kWave);
       const bool inner = t < Lc - 1, lastv = t == Lc - 1;
-      const float betn = inner ? bet_up : (lastv ? (1.0f - lmn) * dtn : 0.f);
+      const float betn = inner ? bet_up : (lastv ? input_weights(dtn, lmn, expf(dtn * Ah), a.disc).x : 0.f);
       const float elln = inner ? ell_up : ellE;
       const float ellv = valid ? ell : ell_last;
       const float w = valid ? (gam * expf(ellE - ellv) + betn * expf(ellE - elln)) : 0.f;
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         const float dt0 = DTg[0];
         const float lm0 = LMg[0];
         alpha0 = expf(dt0 * Ah);
-        beta0 = (1.0f - lm0) * dt0;
+        beta0 = input_weights(dt0, lm0, alpha0, a.disc).x;
       }
 #pragma unroll
       for (int u = 0; u < PBW; ++u) {

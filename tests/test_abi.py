@@ -37,7 +37,18 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert B.m3_abi_version() == 1
+    # version 2 added m3_dims.disc (the discretisation rule)
+    assert B.m3_abi_version() == 2
+
+
+def test_dims_struct_matches_header():
+    """The binding's m3_dims mirrors the header field by field (eight int32)."""
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "mamba3.h")).read()
+    body = re.search(r"typedef struct \{([^}]*)\} m3_dims;", hdr).group(1)
+    names = re.findall(r"(\w+)\s*[,;]", body.replace("int32_t", ""))
+    assert names == [f for f, _ in B.m3_dims._fields_]
+    assert ctypes.sizeof(B.m3_dims) == 32
 
 
 def dims(**kw):
@@ -72,6 +83,7 @@ def call_decode(d, ptrs=None, state=None):
     ("dstate", 256, B.M3_ERR_UNSUPPORTED), ("headdim", 48, B.M3_ERR_UNSUPPORTED),
     ("rank", 3, B.M3_ERR_UNSUPPORTED), ("rank", 8, B.M3_ERR_UNSUPPORTED),
     ("chunk", 128, B.M3_ERR_UNSUPPORTED), ("chunk", 24, B.M3_ERR_UNSUPPORTED),
+    ("disc", 3, B.M3_ERR_UNSUPPORTED), ("disc", -1, B.M3_ERR_UNSUPPORTED),
 ])
 def test_prefill_rejects_bad_dims(field, value, status):
     d = dims(**{field: value})

@@ -29,12 +29,12 @@ def W(name, **kw):
     return syn.WORKLOADS[name].with_(**kw)
 
 
-def dims_of(w):
-    return m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype)
+def dims_of(w, disc=0):
+    return m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype, disc)
 
 
-def run_prefill(w, tt, state, seqlen=None):
-    d = dims_of(w)
+def run_prefill(w, tt, state, seqlen=None, disc=0):
+    d = dims_of(w, disc)
     T = w.seqlen if seqlen is None else seqlen
     y = torch.empty((w.batch, T, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
     nws = m3.mamba3_prefill_workspace_bytes(d, T)
@@ -57,23 +57,24 @@ def make_state(w, st=None):
 
 
 def check_prefill(w, seed, pairs=None, st=None, long_memory=False, zero_D=False, tol=None, dt_scale=1.0,
-                  a_scale=1.0):
+                  a_scale=1.0, disc=0):
     ex, tt = inputs_on_gpu(w, seed, long_memory=long_memory, zero_D=zero_D, dt_scale=dt_scale, a_scale=a_scale)
     s = make_state(w, st)
-    y = run_prefill(w, tt, s)
+    y = run_prefill(w, tt, s, disc=disc)
     if pairs is None:
         pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
     st_ex = exact_state(st, w.io_dtype) if st is not None else oracle.zero_state(
         w.batch, w.heads, w.headdim, w.dstate, w.rank)
     args = oracle_args(ex, pairs)
-    y_ref, (h_ref, bp_ref, xp_ref) = oracle.prefill(**args, state=state_slice(st_ex, pairs))
+    y_ref, (h_ref, bp_ref, xp_ref) = oracle.prefill(**args, state=state_slice(st_ex, pairs), disc=disc)
     bs = np.array([p[0] for p in pairs])
     hs = np.array([p[1] for p in pairs])
     y_gpu = np.moveaxis(to_np(y)[bs, :, hs], 0, 1)[None]
     tol = tol_for(w.io_dtype) if tol is None else tol
     ey = relerr(y_gpu, y_ref)
     eh = relerr(to_np(s.h)[bs, hs][None], h_ref)
-    print(f"[{w.name} seed={seed} T={w.seqlen} Q={w.chunk}] rel-L2 y={ey:.3e} h={eh:.3e}", flush=True)
+    print(f"[{w.name} seed={seed} T={w.seqlen} Q={w.chunk} disc={disc}] rel-L2 y={ey:.3e} h={eh:.3e}",
+          flush=True)
     assert ey <= tol, ey
     assert eh <= tol, eh
     assert np.array_equal(to_np(s.B_prev)[bs, hs][None], bp_ref)
@@ -85,8 +86,8 @@ def check_prefill(w, seed, pairs=None, st=None, long_memory=False, zero_D=False,
 # decode
 # ---------------------------------------------------------------------------
 
-def check_decode(w, seed, steps=3, pairs=None, tol=None):
-    d = dims_of(w)
+def check_decode(w, seed, steps=3, pairs=None, tol=None, disc=0):
+    d = dims_of(w, disc)
     rng_state = syn.draw_state(w, seed + 500)
     s = make_state(w, rng_state)
     cur = exact_state(rng_state, w.io_dtype)
@@ -105,7 +106,8 @@ def check_decode(w, seed, steps=3, pairs=None, tol=None):
         torch.cuda.synchronize()
         args = oracle_args(ex, pairs)
         y_ref, cur = oracle.decode_step(args["x"][:, k], args["Bm"][:, k], args["Cm"][:, k], args["dt"][:, k],
-                                        args["lam"][:, k], args["theta"][:, k], args["A"], args["D"], cur)
+                                        args["lam"][:, k], args["theta"][:, k], args["A"], args["D"], cur,
+                                        disc=disc)
         ey = relerr(to_np(y)[bs, hs][None], y_ref)
         eh = relerr(to_np(s.h)[bs, hs][None], cur[0])
         print(f"[decode {w.name} step {k}] rel-L2 y={ey:.3e} h={eh:.3e}", flush=True)
@@ -120,6 +122,14 @@ def check_decode(w, seed, steps=3, pairs=None, tol=None):
 def test_decode_small(io, P, N, R):
     w = W("tiny_siso_f32", batch=3, heads=5, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=1)
     check_decode(w, seed=10 + P + N + R)
+
+
+@pytest.mark.parametrize("disc", [1, 2])
+@pytest.mark.parametrize("io,P,N,R", [("bf16", 64, 128, 1), ("f32", 32, 32, 2), ("bf16", 64, 64, 4)])
+def test_decode_discretisation_rules(io, P, N, R, disc):
+    """Decayed (textbook) trapezoid and exponential Euler through both decode kernels."""
+    w = W("tiny_siso_f32", batch=2, heads=3, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=1)
+    check_decode(w, seed=80 + disc + P + R, disc=disc)
 
 
 @pytest.mark.parametrize("name", ["decode_mimo_r4_n64", "decode_siso_n128"])
@@ -181,6 +191,20 @@ def test_prefill_strong_decay(io, R):
     w = W("tiny_siso_f32", batch=1, heads=3, headdim=32, dstate=32, rank=R, seqlen=200, chunk=64 // R,
           io_dtype=io)
     check_prefill(w, seed=71, st=syn.draw_state(w, 72), dt_scale=8.0, a_scale=8.0)
+
+
+@pytest.mark.parametrize("disc", [1, 2])
+@pytest.mark.parametrize("io,P,N,R,T,Q", [
+    ("bf16", 64, 128, 1, 300, 64),     # producer/consumer kernel, ragged tail
+    ("bf16", 64, 64, 4, 200, 64),      # MIMO, 16-token tiles
+    ("f32", 16, 16, 2, 16 * 50 + 3, 16),  # segment path (three launches)
+    ("f32", 128, 128, 1, 100, 32),     # single-role kernel
+])
+def test_prefill_discretisation_rules(io, P, N, R, T, Q, disc):
+    """Decayed (textbook) trapezoid and exponential Euler on every prefill path,
+    from a nonzero state."""
+    w = W("tiny_siso_f32", batch=1, heads=3, headdim=P, dstate=N, rank=R, seqlen=T, chunk=Q, io_dtype=io)
+    check_prefill(w, seed=90 + disc + R, st=syn.draw_state(w, 91), disc=disc)
 
 
 def test_prefill_segment_path_small():
