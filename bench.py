@@ -6,7 +6,9 @@ One step = one pass of the hot path over one batch: m3_state_zero + one
 mamba3_prefill of the 1.5B-scale SISO layer (batch 8, 32 heads, headdim 64,
 state 128, 4096 tokens, chunk 64, bf16 I/O, fp32 state), inputs resident in
 HBM before the timed region.  `value` is prefill throughput in Mtokens/s
-(tokens = batch x seqlen, all heads).  The same JSON line carries:
+(tokens = batch x seqlen, all heads).  The default 200 warm-up steps (~60 ms)
+let the GPU reach its steady clocks, which takes ~100 steps from idle; with
+only a few warm-up steps the timed region measures the clock ramp.  The same JSON line carries:
   roofline      -- the prefill kernel's algorithmic HBM bytes per launch over
                    its average duration (HIP events on the launch stream),
                    against the MI355X HBM peak of 8 TB/s; `traffic` comes from
@@ -96,12 +98,12 @@ def committed_traffic(workload_name):
 
 
 class Prefill:
-    def __init__(self, w, seed, long_memory=False):
+    def __init__(self, w, seed, long_memory=False, disc="exp_trapezoid"):
         import torch
         import state_space_sequence_prefill_amd as m3
         from state_space_sequence_prefill_amd import synthetic as syn
         self.m3, self.torch, self.w = m3, torch, w
-        self.d = m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype)
+        self.d = m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype, disc)
         self.inp = syn.draw_torch(w, seed, long_memory=long_memory)
         self.state = m3.State.empty(self.d)
         self.y = torch.empty((w.batch, w.seqlen, w.heads, w.rank, w.headdim), dtype=self.inp["x"].dtype,
@@ -316,7 +318,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--profile-prefill", type=int, default=0, metavar="K",
@@ -396,6 +398,17 @@ def main():
             extra[name] = {"ms_per_step": round(ms, 4), "Mtokens_per_s": round(wx.batch * wx.seqlen / ms / 1e3, 3),
                            "launches": p.nlaunch, "algorithmic_bytes": nb,
                            "hbm_frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del p
+            torch.cuda.empty_cache()
+        # the other discretisation rules on the headline shape (same kernel;
+        # the pages compare Mamba-2's exponential Euler with Mamba-3's rule)
+        for disc in ("exp_euler", "decayed_trapezoid"):
+            log(f"bench: prefill {w.name} disc={disc}")
+            p = Prefill(w, seed=1003, disc=disc)
+            ms, kms = p.time(max(3, args.steps // 2), 2)
+            extra[f"{w.name}_{disc}"] = {"ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                                         "Mtokens_per_s": round(w.batch * w.seqlen / ms / 1e3, 3),
+                                         "hbm_frac": round(nbytes / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
             del p
             torch.cuda.empty_cache()
         line["extra"] = extra
