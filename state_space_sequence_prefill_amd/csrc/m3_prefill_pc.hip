@@ -406,9 +406,8 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           // rows past the chunk hold finite duplicates (clamped loads); every
           // use of them is weighted by an exact zero (mask, w) or never stored
           const bool valid = t < Lc;
-          float bv[8], cv[8];
+          float bv[8];
           rs.b[m][k].unpack(bv);
-          rs.c[m][k].unpack(cv);
           float cs4[4], sn4[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -417,14 +416,21 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             cs4[j] = cs;
             sn4[j] = sn;
             rot2(bv[2 * j], bv[2 * j + 1], cs4[j], -sn4[j]);
-            rot2(cv[2 * j], cv[2 * j + 1], cs4[j], -sn4[j]);
           }
           const float wt = valid ? sW[t < Q ? t : 0] : 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) bt[k][e] = bv[e] * wt;
-          if (ist[m]) {
+          // the row-major B~ and C~ tiles feed only the outputs; a segment
+          // summary needs just the state update's tiles
+          if (ist[m] && has_y) {
+            float cv[8];
+            rs.c[m][k].unpack(cv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rot2(cv[2 * j], cv[2 * j + 1], cs4[j], -sn4[j]);
             store8(bf.sB + rho * LDN + 8 * pg, bv);
-            if (has_y) store8(bf.sC + rho * LDN + 8 * pg, cv);
+            store8(bf.sC + rho * LDN + 8 * pg, cv);
+          }
+          if (ist[m]) {
             if (valid && t == te && (rho & (R - 1)) == 0) {
 #pragma unroll
               for (int j = 0; j < 4; ++j)
