@@ -262,6 +262,17 @@ def test_split_prefill_handoff_and_decode_continuation():
     assert ey <= 2e-2 and eh <= 2e-2
 
 
+def test_prefill_very_long_single_chain():
+    """One chain of 2^18 tokens: the segment plan's largest split (64 segments
+    of 64 chunks), checked token by token against the oracle."""
+    w = W("tiny_siso_f32", batch=1, heads=1, headdim=16, dstate=16, rank=1, seqlen=1 << 18, chunk=64,
+          io_dtype="f32")
+    d = dims_of(w)
+    # 64 segments: states 64*16*16*4 B, decays 64*4 B, angles 64*8*4 B, each 256-B aligned
+    assert m3.mamba3_prefill_workspace_bytes(d, w.seqlen) == 65536 + 256 + 2048
+    check_prefill(w, seed=97, st=syn.draw_state(w, 98))
+
+
 def test_zero_length_prefill_is_noop():
     w = W("tiny_siso_f32", batch=1, heads=2, headdim=16, dstate=16, seqlen=0, io_dtype="f32")
     d = dims_of(w)
