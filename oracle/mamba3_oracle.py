@@ -336,3 +336,23 @@ def prefill_chunked(x, Bm, Cm, dt, lam, theta, A, D, state=None, chunk=64, disc=
                 xp = np.array(x[b, e - 1, hd], dtype=np.float64)
             h_out[b, hd], Bp_out[b, hd], xp_out[b, hd] = h, Bp, xp
     return y, (h_out, Bp_out, xp_out)
+
+
+def gated_rmsnorm(y, z, weight, eps):
+    """Output epilogue: pre-gate grouped RMSNorm of the scan output.
+
+    ai-flow-lab.com Mamba-3 summary, section "実装とカーネル最適化" (a grouped
+    RMSNorm placed before the output gate), and lilting.ch Mamba-3 article,
+    table "Mamba-2とMamba-3の比較" (normalisation row).  Each (token, head,
+    rank) row of P output channels is one group; it is normalised by its root
+    mean square, scaled per channel by the head's weight, then multiplied by
+    the gate's SiLU:
+        out[..., h, r, p] = weight[h, p] * y[..., h, r, p] / sqrt(mean_p y[..., h, r, :]^2 + eps)
+                            * z[..., h, r, p] * sigmoid(z[..., h, r, p])
+    y, z: (..., H, R, P); weight: (H, P); eps: scalar >= 0.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    ms = np.mean(y * y, axis=-1, keepdims=True)
+    silu = z / (1.0 + np.exp(-z))
+    return np.asarray(weight, dtype=np.float64)[:, None, :] * y / np.sqrt(ms + eps) * silu

@@ -517,3 +517,69 @@ def test_pins_catch_planted_mistake(mutant, monkeypatch):
     monkeypatch.setattr(OM, attr, bad)
     caught = [name for name, (fn, tol) in ALL_PINS.items() if not fn() < tol]
     assert caught, f"planted mistake {mutant!r} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# Output epilogue: pre-gate grouped RMSNorm
+# ---------------------------------------------------------------------------
+
+def test_gated_rmsnorm_worked_example():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "gated_rmsnorm_worked.json")))
+    y = np.array(g["y"])[None, None, :]           # (H=1, R=1, P=2)
+    z = np.array(g["z"])[None, None, :]
+    w = np.array(g["weight"])[None, :]
+    out = oracle.gated_rmsnorm(y, z, w, g["eps"])
+    assert np.max(np.abs(out[0, 0] - np.array(g["out"]))) < g["tolerance"]
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5, 0.3])
+def test_gated_rmsnorm_matches_torch(eps):
+    """torch's rms_norm and silu (an independent implementation) on random rows."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    b, T, H, R, P = 2, 3, 4, 2, 16
+    y = rng.standard_normal((b, T, H, R, P))
+    z = rng.standard_normal((b, T, H, R, P)) * 3
+    w = rng.standard_normal((H, P))
+    out = oracle.gated_rmsnorm(y, z, w, eps)
+    ty, tz, tw = (torch.from_numpy(a) for a in (y, z, w))
+    ref = torch.stack([torch.nn.functional.rms_norm(ty[:, :, h], (P,), weight=tw[h], eps=eps)
+                       for h in range(H)], dim=2) * torch.nn.functional.silu(tz)
+    assert relerr(out, ref.numpy()) < 1e-13
+
+
+def test_gated_rmsnorm_scale_invariant():
+    """With eps = 0 the output does not change when a row of y is scaled."""
+    rng = np.random.default_rng(6)
+    y = rng.standard_normal((5, 3, 2, 8))
+    z = rng.standard_normal((5, 3, 2, 8))
+    w = rng.standard_normal((3, 8))
+    c = rng.uniform(0.1, 10.0, (5, 3, 2, 1))
+    assert relerr(oracle.gated_rmsnorm(c * y, z, w, 0.0), oracle.gated_rmsnorm(y, z, w, 0.0)) < 1e-13
+
+
+def _bad_gate_post(y, z, weight, eps):
+    """Gate applied before the norm (post-gate RMSNorm)."""
+    z = np.asarray(z, dtype=np.float64)
+    g = np.asarray(y, dtype=np.float64) * z / (1 + np.exp(-z))
+    return np.asarray(weight)[:, None, :] * g / np.sqrt(np.mean(g * g, axis=-1, keepdims=True) + eps)
+
+
+def _bad_gate_axis(y, z, weight, eps):
+    """Normalised over the ranks instead of the channels of a row."""
+    y = np.asarray(y, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    ms = np.mean(y * y, axis=-2, keepdims=True)
+    return np.asarray(weight)[:, None, :] * y / np.sqrt(ms + eps) * z / (1 + np.exp(-z))
+
+
+@pytest.mark.parametrize("bad", [_bad_gate_post, _bad_gate_axis])
+def test_gated_rmsnorm_pins_catch_planted_mistake(bad, monkeypatch):
+    monkeypatch.setattr(oracle, "gated_rmsnorm", bad)
+    caught = 0
+    for fn in (test_gated_rmsnorm_worked_example, lambda: test_gated_rmsnorm_matches_torch(1e-5)):
+        try:
+            fn()
+        except AssertionError:
+            caught += 1
+    assert caught > 0
