@@ -17,8 +17,11 @@ only a few warm-up steps the timed region measures the clock ramp.  The same JSO
   cpu_baseline  -- the fp64 oracle timed on the host on a bounded sample;
   extra         -- decode step (256 x 32 heads, MIMO R=4 N=64 and SISO N=128;
                    1000 steps captured in a HIP graph, plus a run with a
-                   512 MiB cache flush between steps), and MIMO / 16K-token
-                   prefill throughput.
+                   512 MiB cache flush between steps), MIMO / 16K-token
+                   prefill throughput, the headline shape under the other two
+                   discretisation rules, and the gated entry points (pre-gate
+                   grouped RMSNorm fused into the store of y) on the headline
+                   prefill and both decode shapes.
 Prints exactly one JSON line (rank 0).
 """
 
@@ -63,6 +66,13 @@ def prefill_flops(w):
     return th * (4 * w.rank * w.dstate * w.headdim + 2 * w.chunk * w.rank ** 2 * (w.dstate + w.headdim))
 
 
+def gate_bytes(w, tokens):
+    """Extra bytes of the output epilogue: the gate input z (one I/O element
+    per output) and the fp32 channel weights."""
+    e = 2 if w.io_dtype == "bf16" else 4
+    return w.batch * tokens * w.heads * w.rank * w.headdim * e + w.heads * w.headdim * 4
+
+
 def decode_bytes(w):
     """Algorithmic bytes of one decode step: h read + written, pending pair
     read + written, one token of x, B, C, dt, lam, theta read, y written."""
@@ -98,7 +108,7 @@ def committed_traffic(workload_name):
 
 
 class Prefill:
-    def __init__(self, w, seed, long_memory=False, disc="exp_trapezoid"):
+    def __init__(self, w, seed, long_memory=False, disc="exp_trapezoid", gated=False):
         import torch
         import state_space_sequence_prefill_amd as m3
         from state_space_sequence_prefill_amd import synthetic as syn
@@ -111,14 +121,20 @@ class Prefill:
         nws = m3.mamba3_prefill_workspace_bytes(self.d, w.seqlen)
         self.ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
         self.nlaunch = 1 if not nws else 3
+        self.gate = syn.draw_gate_torch(w, seed + 1) if gated else None
 
     def step(self, ev=None):
         i = self.inp
         self.m3.m3_state_zero(self.d, self.state)
         if ev is not None:
             ev[0].record()
-        self.m3.mamba3_prefill(self.d, self.w.seqlen, i["x"], i["B"], i["C"], i["dt"], i["lam"], i["theta"],
-                               i["A"], i["D"], self.state, self.y, self.ws)
+        if self.gate is None:
+            self.m3.mamba3_prefill(self.d, self.w.seqlen, i["x"], i["B"], i["C"], i["dt"], i["lam"], i["theta"],
+                                   i["A"], i["D"], self.state, self.y, self.ws)
+        else:
+            z, gw = self.gate
+            self.m3.mamba3_prefill_gated(self.d, self.w.seqlen, i["x"], i["B"], i["C"], i["dt"], i["lam"],
+                                         i["theta"], i["A"], i["D"], z, gw, 1e-5, self.state, self.y, self.ws)
         if ev is not None:
             ev[1].record()
 
@@ -138,7 +154,7 @@ class Prefill:
         return wall / steps * 1e3, kern_ms
 
 
-def time_decode(w, seed, steps=1000, flush_steps=20):
+def time_decode(w, seed, steps=1000, flush_steps=20, gated=False):
     import torch
     import state_space_sequence_prefill_amd as m3
     from state_space_sequence_prefill_amd import synthetic as syn
@@ -153,10 +169,18 @@ def time_decode(w, seed, steps=1000, flush_steps=20):
     st.B_prev.copy_(torch.randn(st.B_prev.shape, generator=g, device="cuda").to(st.B_prev.dtype))
     st.x_prev.copy_(torch.randn(st.x_prev.shape, generator=g, device="cuda").to(st.x_prev.dtype))
     y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=toks["x"].dtype, device="cuda")
+    if gated:
+        z, gw = syn.draw_gate_torch(w, seed + 2)
+        z = z[:, 0].contiguous()
 
     def one(j):
         s = sets[j % nset]
-        m3.mamba3_decode_step(d, s["x"], s["B"], s["C"], s["dt"], s["lam"], s["theta"], s["A"], s["D"], st, y)
+        if gated:
+            m3.mamba3_decode_step_gated(d, s["x"], s["B"], s["C"], s["dt"], s["lam"], s["theta"], s["A"], s["D"],
+                                        z, gw, 1e-5, st, y)
+        else:
+            m3.mamba3_decode_step(d, s["x"], s["B"], s["C"], s["dt"], s["lam"], s["theta"], s["A"], s["D"], st,
+                                  y)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -193,9 +217,9 @@ def time_decode(w, seed, steps=1000, flush_steps=20):
         torch.cuda.synchronize()
         tot += a.elapsed_time(b)
     us_flush = tot * 1e3 / flush_steps
-    nb = decode_bytes(w)
+    nb = decode_bytes(w) + (gate_bytes(w, 1) if gated else 0)
     return {
-        "workload": w.name, "batch": w.batch, "heads": w.heads, "headdim": w.headdim, "dstate": w.dstate,
+        "workload": w.name + ("_gated" if gated else ""), "batch": w.batch, "heads": w.heads, "headdim": w.headdim, "dstate": w.dstate,
         "rank": w.rank, "us_per_step_graph": round(us_graph, 2), "steps_graph": reps * per_graph,
         "us_per_step_flushed": round(us_flush, 2), "bytes_per_step": nb,
         "hbm_GBs_graph": round(nb / us_graph / 1e3, 1), "hbm_frac_graph": round(nb / us_graph / 1e3 / HBM_PEAK_GBS, 4),
@@ -410,6 +434,22 @@ def main():
                                          "Mtokens_per_s": round(w.batch * w.seqlen / ms / 1e3, 3),
                                          "hbm_frac": round(nbytes / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
             del p
+            torch.cuda.empty_cache()
+        # the output epilogue (pre-gate grouped RMSNorm) fused into the store
+        # of y: the headline shape and both decode shapes
+        log(f"bench: gated prefill {w.name}")
+        p = Prefill(w, seed=1004, gated=True)
+        ms, kms = p.time(max(3, args.steps // 2), 2)
+        nbg = nbytes + gate_bytes(w, w.seqlen)
+        extra[f"{w.name}_gated"] = {"ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                                    "Mtokens_per_s": round(w.batch * w.seqlen / ms / 1e3, 3),
+                                    "algorithmic_bytes": nbg,
+                                    "hbm_frac": round(nbg / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del p
+        torch.cuda.empty_cache()
+        for name in ("decode_mimo_r4_n64", "decode_siso_n128"):
+            log(f"bench: gated decode {name}")
+            extra[f"{name}_gated"] = time_decode(syn.WORKLOADS[name], seed=7, flush_steps=5, gated=True)
             torch.cuda.empty_cache()
         line["extra"] = extra
 

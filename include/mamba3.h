@@ -174,6 +174,38 @@ int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const 
                        const float* A, const float* D, m3_state* state, void* y,
                        void* stream);
 
+/* Output epilogue: pre-gate grouped RMSNorm, fused into the store of y
+ * (ai-flow-lab.com Mamba-3 summary, section "実装とカーネル最適化": a grouped
+ * RMSNorm before the output gate).  Each (token, head, rank) row of P output
+ * channels s[0..P) of the scan is one group:
+ *   y[p] = weight[head][p] * s[p] / sqrt(mean_p s[p]^2 + eps) * silu(z[p]),
+ *   silu(v) = v / (1 + exp(-v)).
+ *   z       io    same layout as y (the gate input)
+ *   weight  fp32  (heads, P)
+ *   eps     >= 0 */
+typedef struct {
+  const void* z;
+  const float* weight;
+  float eps;
+} m3_gate;
+
+/* mamba3_prefill with the epilogue: y receives the gated, normalised output
+ * (the raw scan output is not written).  Same arguments and errors as
+ * mamba3_prefill, plus M3_ERR_NULL / M3_ERR_ALIGN for gate, gate->z,
+ * gate->weight, M3_ERR_SHAPE for a negative or NaN eps, and
+ * M3_ERR_UNSUPPORTED for shapes that only the single-role prefill kernel
+ * handles (fp32 I/O with tiles too large for the producer/consumer kernel). */
+int mamba3_prefill_gated(const m3_dims* dims, int32_t seqlen, const void* x, const void* B,
+                         const void* C, const float* dt, const float* lam, const float* theta,
+                         const float* A, const float* D, const m3_gate* gate, m3_state* state,
+                         void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mamba3_decode_step with the epilogue (z of shape (batch, heads, R, P)). */
+int mamba3_decode_step_gated(const m3_dims* dims, const void* x, const void* B, const void* C,
+                             const float* dt, const float* lam, const float* theta,
+                             const float* A, const float* D, const m3_gate* gate, m3_state* state,
+                             void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

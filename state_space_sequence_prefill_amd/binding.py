@@ -35,6 +35,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "m3_abi_version", "m3_last_error", "m3_state_bytes", "m3_state_zero", "m3_state_load",
     "m3_state_readout", "mamba3_prefill_workspace_bytes", "mamba3_prefill", "mamba3_decode_step",
+    "mamba3_prefill_gated", "mamba3_decode_step_gated",
 )
 
 
@@ -54,6 +55,10 @@ class m3_state(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("B_prev", ctypes.c_void_p), ("x_prev", ctypes.c_void_p)]
 
 
+class m3_gate(ctypes.Structure):
+    _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -66,7 +71,7 @@ def lib():
                               "`python -m state_space_sequence_prefill_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-        D, S = ctypes.POINTER(m3_dims), ctypes.POINTER(m3_state)
+        D, S, G = ctypes.POINTER(m3_dims), ctypes.POINTER(m3_state), ctypes.POINTER(m3_gate)
         L.m3_abi_version.restype = ctypes.c_int
         L.m3_abi_version.argtypes = []
         L.m3_last_error.restype = ctypes.c_char_p
@@ -85,6 +90,10 @@ def lib():
         L.mamba3_prefill.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp, sz, vp]
         L.mamba3_decode_step.restype = ctypes.c_int
         L.mamba3_decode_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp]
+        L.mamba3_prefill_gated.restype = ctypes.c_int
+        L.mamba3_prefill_gated.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, G, S, vp, vp, sz, vp]
+        L.mamba3_decode_step_gated.restype = ctypes.c_int
+        L.mamba3_decode_step_gated.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, G, S, vp, vp]
         _lib = L
     return _lib
 
@@ -212,10 +221,46 @@ def mamba3_prefill_workspace_bytes(dims, seqlen):
     return n.value
 
 
+def _gate(dims, z, weight, eps, lead):
+    """m3_gate for gate input z of shape lead + (heads, R, P) and weight (heads, P)."""
+    d = dims
+    pz = _ptr(z, "z", tuple(lead) + (d.heads, d.rank, d.headdim), _io_torch_dtype(d))
+    pw = _ptr(weight, "weight", (d.heads, d.headdim), _torch().float32)
+    return m3_gate(pz, pw, float(eps))
+
+
+def _workspace(workspace):
+    if workspace is None:
+        return None, 0
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def mamba3_prefill(dims, seqlen, x, B, C, dt, lam, theta, A, D, state, y, workspace=None, stream=None):
     """Chunked prefill of `seqlen` tokens; `state` (State) is updated in place,
     `y` receives the outputs.  `workspace` is a uint8 GPU tensor of at least
     mamba3_prefill_workspace_bytes(dims, seqlen) bytes (or None when that is 0)."""
+    args, py = _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y)
+    ws, wsb = _workspace(workspace)
+    cs = state.c_struct()
+    _check(lib().mamba3_prefill(ctypes.byref(dims), int(seqlen), *args, ctypes.byref(cs), py, ws, wsb,
+                                _stream(stream)))
+
+
+def mamba3_prefill_gated(dims, seqlen, x, B, C, dt, lam, theta, A, D, z, weight, eps, state, y,
+                         workspace=None, stream=None):
+    """mamba3_prefill whose y is the gated, normalised output: z is the gate
+    input (batch, seqlen, heads, R, P), weight fp32 (heads, P), eps >= 0."""
+    args, py = _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y)
+    g = _gate(dims, z, weight, eps, (dims.batch, int(seqlen)))
+    ws, wsb = _workspace(workspace)
+    cs = state.c_struct()
+    _check(lib().mamba3_prefill_gated(ctypes.byref(dims), int(seqlen), *args, ctypes.byref(g),
+                                      ctypes.byref(cs), py, ws, wsb, _stream(stream)))
+
+
+def _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y):
     torch = _torch()
     d = dims
     io = _io_torch_dtype(d)
@@ -232,17 +277,27 @@ def mamba3_prefill(dims, seqlen, x, B, C, dt, lam, theta, A, D, state, y, worksp
         _ptr(D, "D", (Hh,), f32),
     ]
     py = _ptr(y, "y", (d.batch, T, Hh, R, P), io)
-    ws, wsb = None, 0
-    if workspace is not None:
-        if workspace.device.type != "cuda" or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    cs = state.c_struct()
-    _check(lib().mamba3_prefill(ctypes.byref(d), T, *args, ctypes.byref(cs), py, ws, wsb, _stream(stream)))
+    return args, py
 
 
 def mamba3_decode_step(dims, x, B, C, dt, lam, theta, A, D, state, y, stream=None):
     """One decode step for every (batch, head); `state` is updated in place."""
+    args, py = _decode_args(dims, x, B, C, dt, lam, theta, A, D, y)
+    cs = state.c_struct()
+    _check(lib().mamba3_decode_step(ctypes.byref(dims), *args, ctypes.byref(cs), py, _stream(stream)))
+
+
+def mamba3_decode_step_gated(dims, x, B, C, dt, lam, theta, A, D, z, weight, eps, state, y, stream=None):
+    """mamba3_decode_step whose y is the gated, normalised output (z of shape
+    (batch, heads, R, P), weight fp32 (heads, P), eps >= 0)."""
+    args, py = _decode_args(dims, x, B, C, dt, lam, theta, A, D, y)
+    g = _gate(dims, z, weight, eps, (dims.batch,))
+    cs = state.c_struct()
+    _check(lib().mamba3_decode_step_gated(ctypes.byref(dims), *args, ctypes.byref(g), ctypes.byref(cs), py,
+                                          _stream(stream)))
+
+
+def _decode_args(dims, x, B, C, dt, lam, theta, A, D, y):
     torch = _torch()
     d = dims
     io = _io_torch_dtype(d)
@@ -259,5 +314,4 @@ def mamba3_decode_step(dims, x, B, C, dt, lam, theta, A, D, state, y, stream=Non
         _ptr(D, "D", (Hh,), f32),
     ]
     py = _ptr(y, "y", (d.batch, Hh, R, P), io)
-    cs = state.c_struct()
-    _check(lib().mamba3_decode_step(ctypes.byref(d), *args, ctypes.byref(cs), py, _stream(stream)))
+    return args, py

@@ -217,15 +217,44 @@ int mamba3_prefill_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* 
   return ok();
 }
 
-int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
-                   const float* dt, const float* lam, const float* theta, const float* A,
-                   const float* D, m3_state* state, void* y, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Gate argument checks; *gz stays nullptr without a gate.
+int check_gate(const m3_gate* gate, const void** gz, const float** gw, float* geps) {
+  *gz = nullptr;
+  *gw = nullptr;
+  *geps = 0.f;
+  if (!gate) return fail(M3_ERR_NULL, "gate is NULL");
+  int st;
+  if ((st = check_ptr(gate->z, "gate.z")) != M3_OK) return st;
+  if ((st = check_ptr(gate->weight, "gate.weight")) != M3_OK) return st;
+  if (!(gate->eps >= 0.f)) return fail(M3_ERR_SHAPE, "gate.eps must be >= 0 (got %g)", (double)gate->eps);
+  *gz = gate->z;
+  *gw = gate->weight;
+  *geps = gate->eps;
+  return M3_OK;
+}
+
+int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                 const float* dt, const float* lam, const float* theta, const float* A, const float* D,
+                 const m3_gate* gate, bool gated, m3_state* state, void* y, void* workspace,
+                 size_t workspace_bytes, void* stream, const char* what) {
   m3::Dims m;
   int st = check_dims(dims, true, &m);
   if (st != M3_OK) return st;
   if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
   if ((st = check_state(state, "state")) != M3_OK) return st;
+  const void* gz = nullptr;
+  const float* gw = nullptr;
+  float geps = 0.f;
+  if (gated) {
+    if ((st = check_gate(gate, &gz, &gw, &geps)) != M3_OK) return st;
+    if (!m3::prefill_gated_supported(m))
+      return fail(M3_ERR_UNSUPPORTED, "the gated epilogue needs the producer/consumer prefill kernel, whose "
+                                      "tiles do not fit for these sizes");
+  }
   if (seqlen == 0) return ok();
   m.Q = m3::prefill_tile_chunk(m);
   if ((int64_t)seqlen * m.batch * m.heads * m.R * (m.N > m.P ? m.N : m.P) > ((int64_t)1 << 40))
@@ -258,6 +287,9 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
   a.x_prev = state->x_prev;
   a.y = y;
   a.disc = m.disc;
+  a.gz = gz;
+  a.gw = gw;
+  a.geps = geps;
   a.seqlen = seqlen;
   a.nseg = nseg;
   a.seg_chunks = sc;
@@ -273,16 +305,20 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
     w += align256(cs * sizeof(float));
     a.seg_angle = reinterpret_cast<float*>(w);
   }
-  return hip_status(m3::launch_prefill(m, a, static_cast<hipStream_t>(stream)), "mamba3_prefill");
+  return hip_status(m3::launch_prefill(m, a, static_cast<hipStream_t>(stream)), what);
 }
 
-int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const void* C,
-                       const float* dt, const float* lam, const float* theta, const float* A,
-                       const float* D, m3_state* state, void* y, void* stream) {
+int decode_impl(const m3_dims* dims, const void* x, const void* B, const void* C, const float* dt,
+                const float* lam, const float* theta, const float* A, const float* D, const m3_gate* gate,
+                bool gated, m3_state* state, void* y, void* stream, const char* what) {
   m3::Dims m;
   int st = check_dims(dims, false, &m);
   if (st != M3_OK) return st;
   if ((st = check_state(state, "state")) != M3_OK) return st;
+  const void* gz = nullptr;
+  const float* gw = nullptr;
+  float geps = 0.f;
+  if (gated && (st = check_gate(gate, &gz, &gw, &geps)) != M3_OK) return st;
   const void* ptrs[] = {x, B, C, dt, lam, theta, A, D, y};
   const char* names[] = {"x", "B", "C", "dt", "lam", "theta", "A", "D", "y"};
   for (int i = 0; i < 9; ++i)
@@ -301,7 +337,45 @@ int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const 
   a.x_prev = state->x_prev;
   a.y = y;
   a.disc = m.disc;
-  return hip_status(m3::launch_decode(m, a, static_cast<hipStream_t>(stream)), "mamba3_decode_step");
+  a.gz = gz;
+  a.gw = gw;
+  a.geps = geps;
+  return hip_status(m3::launch_decode(m, a, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                   const float* dt, const float* lam, const float* theta, const float* A,
+                   const float* D, m3_state* state, void* y, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, nullptr, false, state, y, workspace,
+                      workspace_bytes, stream, "mamba3_prefill");
+}
+
+int mamba3_prefill_gated(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                         const float* dt, const float* lam, const float* theta, const float* A,
+                         const float* D, const m3_gate* gate, m3_state* state, void* y, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, gate, true, state, y, workspace,
+                      workspace_bytes, stream, "mamba3_prefill_gated");
+}
+
+int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const void* C,
+                       const float* dt, const float* lam, const float* theta, const float* A,
+                       const float* D, m3_state* state, void* y, void* stream) {
+  return decode_impl(dims, x, B, C, dt, lam, theta, A, D, nullptr, false, state, y, stream,
+                     "mamba3_decode_step");
+}
+
+int mamba3_decode_step_gated(const m3_dims* dims, const void* x, const void* B, const void* C,
+                             const float* dt, const float* lam, const float* theta, const float* A,
+                             const float* D, const m3_gate* gate, m3_state* state, void* y, void* stream) {
+  return decode_impl(dims, x, B, C, dt, lam, theta, A, D, gate, true, state, y, stream,
+                     "mamba3_decode_step_gated");
 }
 
 }  // extern "C"
+

@@ -210,6 +210,12 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
                                 reinterpret_cast<const uint4*>(x),
                                 reinterpret_cast<const uint4*>(a.theta + (size_t)head * (N / 2))};
   const int gstart[6] = {0, gB, 2 * gB, 3 * gB, 3 * gB + gX, 3 * gB + 2 * gX};
+  // output epilogue operands first: the wait below then covers them as well
+  const bool gated = a.gz != nullptr;
+  DecodeGate<IO, R> gate;
+  if (gated)
+    gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * R * P, a.gw + (size_t)hh * P, P, wave,
+                  nthr / kWave, lane);
   // KG granules per thread (the launch picks KG with KG * threads >= total);
   // every load is unconditional (clamped duplicates are not stored)
   uint4 gv[KG];
@@ -303,6 +309,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
   // ---- 4. readout: reduce the partial sums over the lanes of each row
   int base, dup;
   reduce_scatter<K, LPR>(part, n4, base, dup);
+  // (gated: the fp32 outputs go to LDS behind the operand block first)
+  float* const sYg = reinterpret_cast<float*>(dsm + Ops::bytes(P));
   if ((n4 & dup) == 0) {
     constexpr int kOut = ReduceScatter<K, LPR>::kOut;
     IO* y = static_cast<IO*>(a.y) + (size_t)head * R * P;
@@ -311,7 +319,10 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
       const int idx = base + j;
       const int i = idx / R;
       const int r = idx % R;
-      y[r * P + row0 + i] = from_f32<IO>(part[j]);
+      if (gated)
+        sYg[r * P + row0 + i] = part[j];
+      else
+        y[r * P + row0 + i] = from_f32<IO>(part[j]);
     }
   }
   // ---- 5. new pending pair (B_prev, x_prev) <- (B, x) from the LDS copies,
@@ -322,6 +333,11 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
       reinterpret_cast<uint4*>(Bp_)[e] = reinterpret_cast<const uint4*>(sBc)[e];
     else
       reinterpret_cast<uint4*>(xp_)[e - gB] = reinterpret_cast<const uint4*>(sXc)[e - gB];
+  }
+  // ---- 6. output epilogue (pre-gate grouped RMSNorm) over the LDS outputs
+  if (gated) {
+    __syncthreads();
+    gate.apply(sYg, static_cast<IO*>(a.y) + (size_t)head * R * P, a.geps, P, wave, nthr / kWave, lane);
   }
 }
 
@@ -338,7 +354,7 @@ template <typename IO, int N, int R, int IT>
 hipError_t launch_t(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   const int waves = d.P * N / (4 * kWave * IT);
   const dim3 grid(d.batch * d.heads), block(waves * kWave);
-  const size_t lds = DecOps<IO, N, R>::bytes(d.P);
+  const size_t lds = DecOps<IO, N, R>::bytes(d.P) + (a.gz ? (size_t)R * d.P * sizeof(float) : 0);
   if (DecOps<IO, N, R>::granules(d.P) <= waves * kWave)
     hipLaunchKernelGGL((decode_kernel<IO, N, R, IT, 1>), grid, block, lds, s, a, d.heads, d.P);
   else

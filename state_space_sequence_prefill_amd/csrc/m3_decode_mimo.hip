@@ -78,6 +78,12 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
                                 reinterpret_cast<const uint4*>(x),
                                 reinterpret_cast<const uint4*>(a.theta + (size_t)head * (N / 2))};
   const int gstart[6] = {0, gB, 2 * gB, 3 * gB, 3 * gB + gX, 3 * gB + 2 * gX};
+  // output epilogue operands first: the wait below then covers them as well
+  const bool gated = a.gz != nullptr;
+  DecodeGate<IO, R> gate;
+  if (gated)
+    gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * R * P, a.gw + (size_t)hh * P, P, wave,
+                  nthr / kWave, lane);
   uint4 gv[KG];
 #pragma unroll
   for (int k = 0; k < KG; ++k) {
@@ -173,12 +179,17 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
     yacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cr.w, acc[3], yacc, 0, 0, 0);
   }
   // ---- 4. y: lanes g = 0 hold Y^T[r = i][p = 16pb + c] for r < R
+  //         (gated: the fp32 outputs go to LDS behind the derived operands)
+  float* const sYg = reinterpret_cast<float*>(dsm + L::bytes(P));
   if (g == 0) {
     IO* y = static_cast<IO*>(a.y) + (size_t)head * R * P + 16 * pb + c;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float xr = sXk[(R + r) * P + 16 * pb + c];
-      y[r * P] = from_f32<IO>(yacc[r] + Dh * xr);
+      if (gated)
+        sYg[r * P + 16 * pb + c] = yacc[r] + Dh * xr;
+      else
+        y[r * P] = from_f32<IO>(yacc[r] + Dh * xr);
     }
   }
   // ---- 5. new pending pair from the raw LDS copies, issued last
@@ -188,13 +199,18 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
     else
       reinterpret_cast<uint4*>(xp_)[e - gB] = reinterpret_cast<const uint4*>(sXc)[e - gB];
   }
+  // ---- 6. output epilogue (pre-gate grouped RMSNorm) over the LDS outputs
+  if (gated) {
+    __syncthreads();
+    gate.apply(sYg, static_cast<IO*>(a.y) + (size_t)head * R * P, a.geps, P, wave, nthr / kWave, lane);
+  }
 }
 
 template <typename IO, int N, int R>
 hipError_t launch_mimo_t(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   const int waves = d.P / 16;
   const dim3 grid(d.batch * d.heads), block(waves * kWave);
-  const size_t lds = MimoLds<IO, N, R>::bytes(d.P);
+  const size_t lds = MimoLds<IO, N, R>::bytes(d.P) + (a.gz ? (size_t)R * d.P * sizeof(float) : 0);
   if (MimoLds<IO, N, R>::granules(d.P) <= waves * kWave)
     hipLaunchKernelGGL((decode_mimo_kernel<IO, N, R, 1>), grid, block, lds, s, a, d.heads, d.P);
   else

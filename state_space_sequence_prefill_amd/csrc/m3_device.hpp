@@ -47,6 +47,36 @@ __device__ __forceinline__ void store4(bf16* p, const float (&v)[4]) {
   *reinterpret_cast<bf16x4*>(p) = o;
 }
 
+// One 16-byte granule of I/O elements (4 fp32 or 8 bf16) as fp32 values.
+template <typename IO> struct Gran;
+template <> struct Gran<float> {
+  static constexpr int kN = 4;
+  __device__ static __forceinline__ void unpack(const uint4& g, float (&o)[4]) {
+    o[0] = __uint_as_float(g.x); o[1] = __uint_as_float(g.y);
+    o[2] = __uint_as_float(g.z); o[3] = __uint_as_float(g.w);
+  }
+  __device__ static __forceinline__ uint4 pack(const float (&v)[4]) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  }
+};
+template <> struct Gran<bf16> {
+  static constexpr int kN = 8;
+  __device__ static __forceinline__ void unpack(const uint4& g, float (&o)[8]) {
+    const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ uint4 pack(const float (&v)[8]) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+    return __builtin_bit_cast(uint4, o);
+  }
+};
+
 // Pair rotation by (c, s): (a, b) -> (a c - b s, a s + b c).
 __device__ __forceinline__ void rot2(float& a, float& b, float c, float s) {
   const float na = a * c - b * s;
@@ -117,6 +147,67 @@ __device__ __forceinline__ float segment_inclusive_scan(float v, int width) {
   }
   return v;
 }
+
+// Sum over aligned groups of `width` consecutive lanes (a power of two <= 64);
+// every lane of a group receives the group's sum.  Within a 16-lane row the
+// partners come from DPP (quad permutes, half-row and row mirrors: each pairs
+// the lower and the upper half of its group, which is all a sum needs).
+__device__ __forceinline__ float lane_group_sum(float v, int width) {
+  if (width >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, true));
+  if (width >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, true));
+  if (width >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, true));
+  if (width >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, true));
+  if (width >= 32) v += __shfl_xor(v, 16, kWave);
+  if (width >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// The output epilogue's per-element map: weight * s * inv_rms * silu(z), with
+// silu(z) = z / (1 + exp(-z)) from the hardware exp2 and reciprocal (a correctly
+// rounded division would cost ten instructions per element).  Both limits are
+// exact: exp2 overflows to inf (silu -> 0) or underflows to 0 (silu -> z).
+__device__ __forceinline__ float gate_out(float s, float inv_rms, float w, float z) {
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+  return w * s * inv_rms * (z * sig);
+}
+
+// Output epilogue of a decode step for one head: R rows of P fp32 scan
+// outputs sy[r * P + p] (in LDS) -> y, each row normalised by its RMS, scaled
+// by the head's weights and gated.  Wave w of nw handles rows w, w + nw, ...;
+// lane l channels l and l + 64 (P <= 128).  The gate and weight values are
+// fetched ahead, before the step's own loads.
+template <typename IO, int R>
+struct DecodeGate {
+  float z[R][2];
+  float w[2];
+  __device__ __forceinline__ void prefetch(const IO* zg, const float* wg, int P, int wave, int nw, int lane) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) w[k] = lane + 64 * k < P ? wg[lane + 64 * k] : 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = wave + i * nw, p = lane + 64 * k;
+        z[i][k] = (r < R && p < P) ? to_f32(zg[r * P + p]) : 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void apply(const float* sy, IO* y, float eps, int P, int wave, int nw,
+                                        int lane) const {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int r = wave + i * nw;
+      if (r < R) {  // uniform over the wave
+        const float v0 = lane < P ? sy[r * P + lane] : 0.f;
+        const float v1 = lane + 64 < P ? sy[r * P + lane + 64] : 0.f;
+        const float ss = lane_group_sum(v0 * v0 + v1 * v1, kWave);
+        const float inv = rsqrtf(ss / (float)P + eps);
+        if (lane < P) y[r * P + lane] = from_f32<IO>(gate_out(v0, inv, w[0], z[i][0]));
+        if (lane + 64 < P) y[r * P + lane + 64] = from_f32<IO>(gate_out(v1, inv, w[1], z[i][1]));
+      }
+    }
+  }
+};
 
 // Inclusive prefix sums over strided lanes, K independent values at once (so
 // each step's K lane reads are in flight together): within each aligned group

@@ -29,6 +29,9 @@ struct DecodeArgs {
   void* x_prev;
   void* y;
   int disc;  // m3_disc
+  const void* gz;  // output epilogue, as in PrefillArgs
+  const float* gw;
+  float geps;
 };
 
 // Arguments of one prefill pass over tokens [0, seqlen) of every chain.
@@ -46,6 +49,10 @@ struct PrefillArgs {
   void* x_prev;   // pending x (batch, heads, R, P), in/out
   void* y;
   int disc;  // m3_disc
+  // output epilogue (pre-gate grouped RMSNorm); gz == nullptr: plain y
+  const void* gz;
+  const float* gw;
+  float geps;
   int seqlen;
   // Segment path (long prompts, few chains).  nseg == 1: plain fused pass.
   int nseg;        // number of segments the sequence is split into
@@ -69,6 +76,8 @@ bool prefill_supported(const Dims& d);
 // Producer/consumer prefill (m3_prefill_pc.hip): used for every pass whose
 // double-buffered tiles fit; `mode` 0 fused, 1 segment summaries, 2 segments.
 bool prefill_pc_supported(const Dims& d);
+// Whether the gated epilogue is available for these dims (producer/consumer path).
+bool prefill_gated_supported(const Dims& d);
 // Chunk length the prefill kernels tile with (<= d.Q; see m3_prefill.hip).
 int prefill_tile_chunk(const Dims& d);
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);

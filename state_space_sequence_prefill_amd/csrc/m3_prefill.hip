@@ -735,6 +735,7 @@ hipError_t launch_fused_t(const Dims& d, const PrefillArgs& a, hipStream_t st) {
   kp.Q = d.Q;
   const int chains = d.batch * d.heads;
   const bool pc = prefill_pc_supported(d);
+  if (a.gz && !pc) return hipErrorInvalidValue;  // the epilogue lives in the producer/consumer kernel
   auto pass = [&](int mode, int nblocks) -> hipError_t {
     if (pc) return launch_prefill_pc(d, a, st, mode, nblocks);
     kp.mode = mode;
@@ -819,6 +820,12 @@ int prefill_tile_chunk(const Dims& d) {
     if (prefill_pc_supported(e)) return q;
   }
   return d.Q;
+}
+
+bool prefill_gated_supported(const Dims& d) {
+  Dims e = d;
+  e.Q = prefill_tile_chunk(d);
+  return prefill_pc_supported(e);
 }
 
 hipError_t launch_prefill(const Dims& d, const PrefillArgs& a, hipStream_t s) {

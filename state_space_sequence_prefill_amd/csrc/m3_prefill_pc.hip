@@ -571,21 +571,89 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         }
       }
     }
+    // the entry-state loads retire here, once: otherwise the loop below would
+    // wait for every outstanding memory operation at each first use of Hreg
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     // y of chunk jy leaves the LDS output tile as whole 16-byte runs of its
     // rows (each (token, rank) row is P contiguous elements in HBM)
+    constexpr int EG = Gran<IO>::kN;                 // elements per 16-byte granule
+    constexpr int G16 = P / EG;                      // granules per row (2 .. 32)
+    constexpr int kCT = kConsWaves * kWave;          // consumer threads
+    constexpr int KZ = (RMAX * G16 + kCT - 1) / kCT;  // granules per consumer thread
+    const int ct = tid - kProdThreads;
+    auto gran_off = [&](int c0, int e) -> size_t {
+      const int row = e / G16, gq = e % G16;
+      return (size_t)(c0 + (row >> lgR)) * tokX + (row & (R - 1)) * P + gq * EG;
+    };
+    // Output epilogue (pre-gate grouped RMSNorm): a consumer thread always
+    // handles granule column ct % G16 of its rows (kCT is a multiple of G16),
+    // so its EG weights are loaded once; the G16 granules of one row sit in
+    // G16 aligned consecutive lanes, which sum the squares among themselves.
+    // The gate of chunk j is loaded one iteration ahead of its use.
+    const bool gated = has_y && a.gz != nullptr;
+    const IO* Zg = gated ? static_cast<const IO*>(a.gz) + ((size_t)b * T * H + hh) * R * P : nullptr;
+    float gwr[EG];
+    uint4 zr[KZ];
+    if (gated) {
+#pragma unroll
+      for (int q = 0; q < EG; ++q) gwr[q] = a.gw[(size_t)hh * P + (ct % G16) * EG + q];
+    }
+    auto load_z = [&](int jz) {
+      const int ng = chunk_len(jz) * R * G16;
+#pragma unroll
+      for (int k = 0; k < KZ; ++k) {
+        const int e = ct + k * kCT;  // clamped duplicate past the tail, never used
+        zr[k] = *reinterpret_cast<const uint4*>(Zg + gran_off(jz * Q, e < ng ? e : ng - 1));
+      }
+    };
     auto store_y = [&](int jy) {
-      const int c0 = jy * Q, nrow = chunk_len(jy) * R;
-      constexpr int G16 = P * (int)sizeof(IO) / 16;  // 16-byte granules per row
-      for (int e = tid - kProdThreads; e < nrow * G16; e += kConsWaves * kWave) {
+      const int c0 = jy * Q, ng = chunk_len(jy) * R * G16;
+      for (int e = ct; e < ng; e += kCT) {
         const int row = e / G16, gq = e % G16;
-        const uint4 v = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * (16 / sizeof(IO)));
-        *reinterpret_cast<uint4*>(Yg + (size_t)(c0 + (row >> lgR)) * tokX + (row & (R - 1)) * P +
-                                  gq * (16 / sizeof(IO))) = v;
+        *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG);
+      }
+    };
+    uint4 gres[KZ];
+    auto gate_y = [&](int jy) {
+      const int ng = chunk_len(jy) * R * G16;
+#pragma unroll
+      for (int k = 0; k < KZ; ++k) {
+        const int e = ct + k * kCT;
+        if (e < ng) {  // whole rows: all G16 lanes of a row agree
+          const int row = e / G16, gq = e % G16;
+          float v[EG], z[EG];
+          Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG), v);
+          float ss = 0.f;
+#pragma unroll
+          for (int q = 0; q < EG; ++q) ss += v[q] * v[q];
+          ss = lane_group_sum(ss, G16);
+          const float inv = rsqrtf(ss * (1.0f / P) + a.geps);
+          Gran<IO>::unpack(zr[k], z);
+#pragma unroll
+          for (int q = 0; q < EG; ++q) v[q] = gate_out(v[q], inv, gwr[q], z[q]);
+          gres[k] = Gran<IO>::pack(v);
+        }
+      }
+    };
+    auto store_gated = [&](int jy) {
+      const int c0 = jy * Q, ng = chunk_len(jy) * R * G16;
+#pragma unroll
+      for (int k = 0; k < KZ; ++k) {
+        const int e = ct + k * kCT;
+        if (e < ng) *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = gres[k];
       }
     };
     for (int i = ck0; i <= ck1; ++i) {
-      if (has_y && i >= ck0 + 2) store_y(i - 2);
+      if (gated) {
+        // results of chunk i-2, then the gate loads of chunk i-1, then the
+        // stores: loads issued ahead of the stores never wait for them
+        if (i >= ck0 + 2) gate_y(i - 2);
+        if (i > ck0) load_z(i - 1);
+        if (i >= ck0 + 2) store_gated(i - 2);
+      } else if (has_y && i >= ck0 + 2) {
+        store_y(i - 2);
+      }
       // ---- phase 1: this wave's 16x16 blocks of S.M for chunk i-1 ----
       // Blocks (rb, kb), kb <= rb, are dealt round-robin to the 4 consumer
       // waves.  S^T = Bt Ct^T leaves the accumulator with 4 consecutive keys
@@ -766,7 +834,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
       __syncthreads();
     }
-    if (has_y && ck1 > ck0) store_y(ck1 - 1);
+    if (gated && ck1 > ck0) {
+      gate_y(ck1 - 1);
+      store_gated(ck1 - 1);
+    } else if (has_y && ck1 > ck0) {
+      store_y(ck1 - 1);
+    }
   }
 
   if (writes_final) {

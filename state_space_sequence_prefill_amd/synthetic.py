@@ -12,7 +12,8 @@ Workload shapes and distributions (per token-head unless noted):
     A        = -exp(U(-1, 1))           per head   ("long memory": -exp(U(-5, -3)))
     D        ~ N(0, 1)                  per head
 Draw order with numpy's PCG64 generator: x, B, C, dt_raw, lam_raw, theta_raw,
-A_raw, D.  Values are drawn in float64 and then cast to the I/O dtype by
+A_raw, D.  The output gate (``draw_gate``, its own seed) draws z ~ N(0, 1)
+(same layout as x) and then the per-head channel weights ~ U(0.5, 1.5).  Values are drawn in float64 and then cast to the I/O dtype by
 round-to-nearest-even; the exact cast values are what every consumer sees.
 
 The named workloads mirror the pages' 1.5B-scale Mamba-3 layers (32 heads of
@@ -81,6 +82,32 @@ def draw(w: Workload, seed: int, long_memory: bool = False, seqlen=None):
         A = -np.exp(rng.uniform(-1.0, 1.0, H))
     D = rng.standard_normal(H)
     return {"x": x, "B": Bm, "C": Cm, "dt": dt, "lam": lam, "theta": theta, "A": A, "D": D}
+
+
+def draw_gate(w: Workload, seed: int, seqlen=None, decode: bool = False):
+    """Gate input z (b,T,H,R,P), or (b,H,R,P) for a decode step, and the
+    per-head channel weights (H,P) of the output epilogue, fp64."""
+    T = w.seqlen if seqlen is None else seqlen
+    b, H, R, P = w.batch, w.heads, w.rank, w.headdim
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((b, H, R, P) if decode else (b, T, H, R, P))
+    weight = rng.uniform(0.5, 1.5, (H, P))
+    return z, weight
+
+
+def draw_gate_torch(w: Workload, seed: int, device="cuda", seqlen=None):
+    """``draw_gate``'s distributions on the device (z in the I/O dtype,
+    weights fp32), for timing runs."""
+    import torch
+
+    T = w.seqlen if seqlen is None else seqlen
+    b, H, R, P = w.batch, w.heads, w.rank, w.headdim
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    z = torch.randn((b, T, H, R, P), generator=g, device=device, dtype=torch.float32).to(io)
+    weight = torch.rand((H, P), generator=g, device=device, dtype=torch.float32) + 0.5
+    return z, weight
 
 
 def draw_state(w: Workload, seed: int, scale: float = 1.0):

@@ -192,3 +192,61 @@ def test_last_error_is_cleared_by_success():
     assert "odd" in B.m3_last_error()
     B.m3_state_bytes(dims())
     assert B.m3_last_error() == ""
+
+
+# ---------------------------------------------------------------------------
+# gated entry points (output epilogue)
+# ---------------------------------------------------------------------------
+
+def test_gate_struct_matches_header():
+    hdr = open(HEADER).read()
+    body = re.search(r"typedef struct \{([^}]*)\} m3_gate;", hdr).group(1)
+    names = re.findall(r"(\w+)\s*;", body)
+    assert names == [f for f, _ in B.m3_gate._fields_]
+    assert ctypes.sizeof(B.m3_gate) == 24
+
+
+def call_prefill_gated(d, gate, seqlen=16, ptrs=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    g = None if gate is None else ctypes.byref(gate)
+    return B.lib().mamba3_prefill_gated(ctypes.byref(d), seqlen, *p[:8], g, ctypes.byref(fake_state()), p[8],
+                                        None, 0, None)
+
+
+def call_decode_gated(d, gate, ptrs=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    g = None if gate is None else ctypes.byref(gate)
+    return B.lib().mamba3_decode_step_gated(ctypes.byref(d), *p[:8], g, ctypes.byref(fake_state()), p[8], None)
+
+
+@pytest.mark.parametrize("call", [call_prefill_gated, call_decode_gated])
+def test_gate_argument_checks(call):
+    d = dims()
+    assert call(d, None) == B.M3_ERR_NULL
+    assert call(d, B.m3_gate(None, FAKE, 1e-5)) == B.M3_ERR_NULL
+    assert call(d, B.m3_gate(FAKE, None, 1e-5)) == B.M3_ERR_NULL
+    assert call(d, B.m3_gate(FAKE + 2, FAKE, 1e-5)) == B.M3_ERR_ALIGN
+    assert call(d, B.m3_gate(FAKE, FAKE + 4, 1e-5)) == B.M3_ERR_ALIGN
+    assert call(d, B.m3_gate(FAKE, FAKE, -1e-5)) == B.M3_ERR_SHAPE
+    assert call(d, B.m3_gate(FAKE, FAKE, float("nan"))) == B.M3_ERR_SHAPE
+    assert "eps" in B.m3_last_error()
+    # the other arguments are still checked
+    p = [FAKE] * 9
+    p[8] = None
+    assert call(d, B.m3_gate(FAKE, FAKE, 0.0), ptrs=p) == B.M3_ERR_NULL
+
+
+def test_gated_prefill_needs_the_producer_consumer_kernel():
+    """fp32 with N = P = 128 and rank 2 has no producer/consumer tiling at any
+    chunk height; the plain prefill serves it, the gated one refuses it."""
+    d = dims(io_dtype="f32", dstate=128, headdim=128, rank=2, chunk=16)
+    ok = B.m3_gate(FAKE, FAKE, 1e-5)
+    assert call_prefill(d, seqlen=0) == B.M3_OK
+    assert call_prefill_gated(d, ok, seqlen=0) == B.M3_ERR_UNSUPPORTED
+    # every bf16 shape the headline families use is served
+    for r, n, c in ((1, 128, 64), (2, 128, 64), (4, 64, 64), (4, 128, 32)):
+        assert call_prefill_gated(dims(rank=r, dstate=n, chunk=c), ok, seqlen=0) == B.M3_OK
+
+
+def test_gated_zero_seqlen_is_a_noop():
+    assert call_prefill_gated(dims(), B.m3_gate(FAKE, FAKE, 0.0), seqlen=0, ptrs=[None] * 9) == B.M3_OK

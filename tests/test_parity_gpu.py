@@ -14,7 +14,7 @@ import oracle
 from state_space_sequence_prefill_amd import synthetic as syn
 
 from m3_testlib import (exact_state, inputs_on_gpu, oracle_args, relerr, state_slice, state_to_gpu,
-                        to_np, tol_for)
+                        to_gpu, to_np, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -307,3 +307,133 @@ def test_prefill_full_size_sampled(name):
     rng = np.random.default_rng(99)
     chains = sorted({(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(6)})
     check_prefill(w, seed=1000 + list(syn.WORKLOADS).index(name), pairs=chains)
+
+
+# ---------------------------------------------------------------------------
+# gated entry points: the output epilogue (pre-gate grouped RMSNorm) fused
+# into the store of y, against oracle.gated_rmsnorm of the oracle's y
+# ---------------------------------------------------------------------------
+
+def gate_on_gpu(w, seed, decode=False, seqlen=None):
+    z, gw = syn.draw_gate(w, seed, seqlen=seqlen, decode=decode)
+    z_ex, gw_ex = syn.round_io(z, w.io_dtype), syn.round_io(gw, "f32")
+    return z_ex, gw_ex, to_gpu(z_ex, w.io_dtype, "x"), to_gpu(gw_ex, "f32", "weight")
+
+
+def check_prefill_gated(w, seed, eps=1e-5, pairs=None, disc=0, st=None):
+    ex, tt = inputs_on_gpu(w, seed)
+    z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 7000)
+    s = make_state(w, st)
+    d = dims_of(w, disc)
+    T = w.seqlen
+    y = torch.empty((w.batch, T, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
+    nws = m3.mamba3_prefill_workspace_bytes(d, T)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    m3.mamba3_prefill_gated(d, T, tt["x"], tt["B"], tt["C"], tt["dt"], tt["lam"], tt["theta"], tt["A"], tt["D"],
+                            zt, gwt, eps, s, y, ws)
+    torch.cuda.synchronize()
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    st_ex = exact_state(st, w.io_dtype) if st is not None else oracle.zero_state(
+        w.batch, w.heads, w.headdim, w.dstate, w.rank)
+    y_ref, (h_ref, bp_ref, xp_ref) = oracle.prefill(**oracle_args(ex, pairs), state=state_slice(st_ex, pairs),
+                                                   disc=disc)
+    g_ref = oracle.gated_rmsnorm(y_ref, np.moveaxis(z_ex[bs, :, hs], 0, 1)[None], gw_ex[hs], eps)
+    g_gpu = np.moveaxis(to_np(y)[bs, :, hs], 0, 1)[None]
+    tol = tol_for(w.io_dtype)
+    eg = relerr(g_gpu, g_ref)
+    eh = relerr(to_np(s.h)[bs, hs][None], h_ref)
+    print(f"[gated {w.name} seed={seed} T={T} Q={w.chunk} eps={eps}] rel-L2 out={eg:.3e} h={eh:.3e}", flush=True)
+    assert eg <= tol, eg
+    assert eh <= tol, eh
+    assert np.array_equal(to_np(s.B_prev)[bs, hs][None], bp_ref)
+    assert np.array_equal(to_np(s.x_prev)[bs, hs][None], xp_ref)
+
+
+@pytest.mark.parametrize("io,P,N,R,T,Q", [
+    ("f32", 16, 16, 1, 64, 16),     # 4 fp32 granules per row
+    ("bf16", 16, 32, 2, 50, 16),    # 2 bf16 granules per row, ragged tail
+    ("bf16", 64, 128, 1, 200, 64),  # the headline family, ragged tail
+    ("bf16", 64, 64, 4, 130, 64),   # MIMO rank 4: 16-token tiles
+    ("f32", 32, 32, 2, 100, 32),
+    ("bf16", 128, 64, 1, 96, 32),   # 16 granules per row
+    ("f32", 128, 32, 1, 70, 16),    # 32 granules per row: the sum crosses rows of 16 lanes
+])
+def test_prefill_gated_shapes(io, P, N, R, T, Q):
+    w = W("tiny_siso_f32", batch=2, heads=3, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=T, chunk=Q)
+    check_prefill_gated(w, seed=900 + P + N + R + T)
+
+
+def test_prefill_gated_eps_and_state():
+    """A large eps (visible in every row) and a non-zero initial state."""
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=64, dstate=64, rank=1, io_dtype="bf16", seqlen=150, chunk=64)
+    check_prefill_gated(w, seed=931, eps=0.75, st=syn.draw_state(w, 932))
+
+
+def test_prefill_gated_segment_path():
+    """Few long chains: the gate is applied by the segment pass."""
+    w = W("tiny_siso_f32", batch=1, heads=2, headdim=64, dstate=128, rank=1, io_dtype="bf16", seqlen=64 * 40,
+          chunk=64)
+    assert m3.mamba3_prefill_workspace_bytes(dims_of(w), w.seqlen) > 0
+    check_prefill_gated(w, seed=940)
+
+
+@pytest.mark.parametrize("disc", [1, 2])
+def test_prefill_gated_discretisation_rules(disc):
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=32, dstate=64, rank=2, io_dtype="f32", seqlen=90, chunk=32)
+    check_prefill_gated(w, seed=950 + disc, disc=disc)
+
+
+def test_prefill_gated_full_size_sampled():
+    w = syn.WORKLOADS["siso_1p5b_t4096"]
+    rng = np.random.default_rng(5)
+    chains = sorted({(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(4)})
+    check_prefill_gated(w, seed=960, pairs=chains)
+
+
+def check_decode_gated(w, seed, eps=1e-5, steps=2, pairs=None):
+    d = dims_of(w)
+    st0 = syn.draw_state(w, seed + 500)
+    s = make_state(w, st0)
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    cur = state_slice(exact_state(st0, w.io_dtype), pairs)
+    ex, tt = inputs_on_gpu(w, seed, seqlen=steps)
+    tol = tol_for(w.io_dtype)
+    for k in range(steps):
+        z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 100 * k + 7, decode=True)
+        tok = {key: (v[:, k].contiguous() if v.dim() >= 3 else v) for key, v in tt.items()}
+        y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
+        m3.mamba3_decode_step_gated(d, tok["x"], tok["B"], tok["C"], tok["dt"], tok["lam"], tok["theta"],
+                                    tok["A"], tok["D"], zt, gwt, eps, s, y)
+        torch.cuda.synchronize()
+        args = oracle_args(ex, pairs)
+        y_ref, cur = oracle.decode_step(args["x"][:, k], args["Bm"][:, k], args["Cm"][:, k], args["dt"][:, k],
+                                        args["lam"][:, k], args["theta"][:, k], args["A"], args["D"], cur)
+        g_ref = oracle.gated_rmsnorm(y_ref, z_ex[bs, hs][None], gw_ex[hs], eps)
+        eg = relerr(to_np(y)[bs, hs][None], g_ref)
+        eh = relerr(to_np(s.h)[bs, hs][None], cur[0])
+        print(f"[gated decode {w.name} step {k}] rel-L2 out={eg:.3e} h={eh:.3e}", flush=True)
+        assert eg <= tol and eh <= tol, (eg, eh)
+        assert np.array_equal(to_np(s.B_prev)[bs, hs][None], cur[1])
+        assert np.array_equal(to_np(s.x_prev)[bs, hs][None], cur[2])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("P,N,R", [(16, 16, 1), (64, 128, 1), (128, 128, 1), (32, 32, 2), (64, 64, 4),
+                                   (128, 64, 4)])
+def test_decode_gated(io, P, N, R):
+    w = W("tiny_siso_f32", batch=3, heads=4, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=1)
+    check_decode_gated(w, seed=970 + P + N + R)
+
+
+@pytest.mark.parametrize("name", ["decode_mimo_r4_n64", "decode_siso_n128"])
+def test_decode_gated_full_size_sampled(name):
+    w = syn.WORKLOADS[name]
+    rng = np.random.default_rng(11)
+    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(16)]
+    check_decode_gated(w, seed=990, eps=1e-3, pairs=pairs)
