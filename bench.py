@@ -40,7 +40,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "state_space_sequence_prefill_amd", "csrc")
 # sources whose code the fused prefill launch runs (kernel, device helpers)
-PREFILL_SRCS = ("m3_prefill_pc.hip", "m3_mfma.hpp", "m3_device.hpp")
+PREFILL_SRCS = ("m3_prefill_pc.hpp", "m3_prefill_pc.hip", "m3_mfma.hpp", "m3_device.hpp")
 HEADLINE = "siso_1p5b_t4096"
 METRIC = "Mamba-3 scan prefill Mtokens/s + decode \u00b5s/step; % of MFMA / HBM peak"
 

@@ -81,5 +81,7 @@ bool prefill_gated_supported(const Dims& d);
 // Chunk length the prefill kernels tile with (<= d.Q; see m3_prefill.hip).
 int prefill_tile_chunk(const Dims& d);
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
+// The same with y stored through the output epilogue (m3_prefill_pc_gated.hip).
+hipError_t launch_prefill_pc_gated(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
 
 }  // namespace m3

@@ -1,915 +1,9 @@
-// Mamba-3 chunked prefill for gfx950: producer/consumer form.
-//
-// Same algebra as the single-role kernel in m3_prefill.hip (chunked "dual"
-// form of the exponential-trapezoid recurrence with rotating state; lilting.ch
-// Mamba-3 article, "アーキテクチャ改善" 1-3, and its SSM-history section on the
-// matmul-shaped restructuring): per chunk, with local angles phi and local
-// log-decay l,
-//     y^T[p][t]  = e^{l_t} (E^T Ct^T)[p][t] + (X^T (S.M)^T)[p][t]    (+ D x on the diagonal of S.M)
-//     E'         = Rot(phi_e) [ e^{l_E} E + Bt^T diag(w) X ]
-// where E is the chunk's entry value (the carried lab-frame state with the
-// first token's decay and previous-input term applied), S^T = Bt Ct^T, and M
-// the trapezoid decay mask.
-//
-// One workgroup of 8 waves per chain (or chain segment):
-//   waves 0-3 produce: stream dt, lam, theta, B, C, x for chunk i+1 / i+2 from
-//     HBM into registers (16-byte loads, addresses clamped so every load is
-//     unconditional), run the in-chunk decay scan and angle prefix, rotate B
-//     and C, and write chunk i's bf16/fp32 tiles into LDS buffer i%2;
-//   waves 4-7 consume chunk i-1 from buffer (i-1)%2 on the matrix cores.  Each
-//     consumer wave owns 16-column slices (p-blocks) of the P x N state, kept
-//     in fp32 registers as E^T tiles (rows n, columns p).  Because the K order
-//     inside an MFMA is free as long as both operands agree, the state tiles
-//     feed the carried-state product E^T Ct^T directly (two adjacent n-tiles
-//     give one 32-wide K slab), and the masked score tile S^T leaves its
-//     accumulator as the B operand of X^T (S.M)^T; the output comes out as
-//     y^T, so each lane stores 4 consecutive p of one token (8-byte stores).
-// A single workgroup barrier per chunk separates the roles' buffers: tiles
-// are double buffered, per-token coefficients triple buffered (written one
-// chunk ahead by the producers, read by producers in the next chunk and by
-// consumers in the one after).
-#include "m3_kernels.hpp"
-#include "m3_mfma.hpp"
+// Producer/consumer prefill (m3_prefill_pc.hpp): the instances that store the
+// plain scan output, the support test, and the dispatch between the plain
+// and the gated instances.
+#include "m3_prefill_pc.hpp"
 
 namespace m3 {
-namespace {
-
-constexpr int kPcThreads = 512;
-constexpr int kProdThreads = 256;
-constexpr int kConsWaves = 4;
-constexpr float kLog2ePc = 1.4426950408889634f;
-
-enum PcMode : int { kPcFused = 0, kPcSummary = 1, kPcSegment = 2 };
-
-struct PcParams {
-  PrefillArgs a;
-  int batch, heads, R, lgR, Q;
-  int mode;
-  int nblocks;
-};
-
-__device__ __forceinline__ int pc_remap_block(int bid, int nblocks) {
-  if (nblocks % 8 != 0) return bid;
-  return (bid % 8) * (nblocks / 8) + bid / 8;
-}
-
-// LDS layout for <IO, N, P> with tiles of `rows` (token, rank) rows.
-template <typename IO, int N, int P>
-struct PcLds {
-  static constexpr int E = sizeof(IO);
-  static constexpr int PAD = 16 / E;
-  static constexpr int NK = N < 32 ? 32 : N;
-  static constexpr int LDN = NK + PAD;
-  // one tile buffer
-  __host__ __device__ static constexpr size_t buf_bytes(int rows) {
-    return (size_t)rows * LDN * E * 2            // sB, sC
-           + (size_t)N * (rows + PAD) * E        // sBt
-           + (size_t)P * (rows + PAD) * E        // sXt
-           + (size_t)(N / 2) * 16;               // sEnd {cos, sin, phi, 0}
-  }
-  // masked score tile (S.M) shared by the consumer waves: rows = queries,
-  // columns = keys
-  __host__ __device__ static constexpr size_t sm_bytes(int rows) { return (size_t)rows * (rows + PAD) * E; }
-  // output tile: the consumer waves' y slices meet here and leave as whole rows
-  __host__ __device__ static constexpr size_t y_bytes(int rows) { return (size_t)rows * (P + PAD) * E; }
-  static constexpr size_t kCoefBytes = 64 * 20 + 16;  // one coefficient slot (Q <= 64)
-  __host__ __device__ static constexpr size_t bytes(int rows) {
-    return 2 * buf_bytes(rows) + sm_bytes(rows) + y_bytes(rows) + 3 * kCoefBytes + (N / 2) * 4;
-  }
-};
-
-template <typename IO, int N, int P>
-struct PcBuf {
-  IO *sB, *sC, *sBt, *sXt;
-  float4* sEnd;
-};
-struct PcCoef {
-  float4* sTok;  // [Q] {gamma, l*log2e, beta of the next token, l_next*log2e}
-  float* sW;     // [Q] state-update weights
-  float* sMisc;  // [0] l_E, [1] l_E*log2e
-};
-
-// Largest padded row count and register-array bounds of an instance.
-template <typename IO, int N, int P>
-struct PcLimits {
-  static constexpr int NK = PcLds<IO, N, P>::NK;
-  static constexpr bool fits(int r) {
-    return PcLds<IO, N, P>::bytes(r) <= 160 * 1024 && r * NK * (int)sizeof(IO) <= 16384 &&
-           (r / 4) * (N / 8) <= 2 * kProdThreads && (r / 4) * (P / 8) <= 2 * kProdThreads;
-  }
-  static constexpr int kMaxRows = fits(128) ? 128 : fits(64) ? 64 : fits(32) ? 32 : 0;
-  static constexpr int kMaxRB = kMaxRows / 16;                                    // row blocks
-  static constexpr int kMI = (kMaxRows / 4) * (N / 8) > kProdThreads ? 2 : 1;     // B/C items per thread
-  static constexpr int kMX = (kMaxRows / 4) * (P / 8) > kProdThreads ? 2 : 1;     // x items per thread
-  static constexpr int kPBW = (P / 16 + kConsWaves - 1) / kConsWaves;            // p-blocks per consumer
-};
-
-// One chunk's raw inputs as a producer thread holds them in registers.
-template <typename IO, int MI, int MX>
-struct PcRaw {
-  Raw8<IO> b[MI][4], c[MI][4], x[MX][4];
-  float4 th[MI][4];
-};
-
-template <typename IO, int N, int P>
-__global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) {
-  using L = PcLds<IO, N, P>;
-  using Lim = PcLimits<IO, N, P>;
-  constexpr int NB = N / 16, PB = P / 16;
-  constexpr int NK = L::NK, LDN = L::LDN, PAD = L::PAD;
-  constexpr int NS = NK / 32;
-  constexpr int MI = Lim::kMI, MX = Lim::kMX, PBW = Lim::kPBW;
-  // Tiles always hold RMAX rows; rows past Q*R stay zero, so every consumer
-  // loop has compile-time bounds.
-  // (instances whose tiles do not fit at all are never launched; they compile
-  // with the smallest tile height)
-  constexpr int RMAX = Lim::kMaxRows > 0 ? Lim::kMaxRows : 32, KSM = RMAX / 32, RBM = RMAX / 16;
-  constexpr int ldr = RMAX + PAD;
-  extern __shared__ __align__(16) char smem[];
-
-  const PrefillArgs& a = kp.a;
-  const int Q = kp.Q, R = kp.R, lgR = kp.lgR, H = kp.heads;
-  const int T = a.seqlen;
-  const int mode = kp.mode;
-  const int nseg_grid = (mode == kPcFused) ? 1 : (mode == kPcSummary ? a.nseg - 1 : a.nseg);
-  const int bid = pc_remap_block(blockIdx.x, kp.nblocks);
-  const int chain = bid / nseg_grid;
-  const int seg = bid % nseg_grid;
-  const int b = chain / H, hh = chain % H;
-  const int nchunks = (T + Q - 1) / Q;
-  const int ck0 = (mode == kPcFused) ? 0 : seg * a.seg_chunks;
-  int ck1 = (mode == kPcFused) ? nchunks : ck0 + a.seg_chunks;
-  if (ck1 > nchunks) ck1 = nchunks;
-  const bool writes_final = (mode == kPcFused) || (mode == kPcSegment && seg == a.nseg - 1);
-  const bool has_y = mode != kPcSummary;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const bool producer = wave < 4;
-  const int rows = Q * R;
-  const int rows_pad = (rows + 31) & ~31;
-
-  // ---- LDS: [tile buffer 0 | tile buffer 1 | sSM | sY | coefs x3 | sSeg] ----
-  constexpr size_t bufB = (size_t)RMAX * LDN * sizeof(IO);  // sB, sC
-  constexpr size_t bufBt = (size_t)N * ldr * sizeof(IO);
-  constexpr size_t bufXt = (size_t)P * ldr * sizeof(IO);
-  constexpr size_t bufStride = L::buf_bytes(RMAX);
-  constexpr size_t coefStride = L::kCoefBytes;
-  constexpr size_t smStride = L::sm_bytes(RMAX);
-  constexpr size_t yStride = L::y_bytes(RMAX);
-  constexpr int ldy = P + PAD;
-  IO* const sSM = reinterpret_cast<IO*>(smem + 2 * bufStride);
-  IO* const sY = reinterpret_cast<IO*>(smem + 2 * bufStride + smStride);
-  char* const coefBase = smem + 2 * bufStride + smStride + yStride;
-  float* const sSeg = reinterpret_cast<float*>(coefBase + 3 * coefStride);
-  auto getbuf = [&](int ck) {
-    char* p = smem + (size_t)(ck & 1) * bufStride;
-    PcBuf<IO, N, P> r;
-    r.sB = reinterpret_cast<IO*>(p);
-    r.sC = reinterpret_cast<IO*>(p + bufB);
-    r.sBt = reinterpret_cast<IO*>(p + 2 * bufB);
-    r.sXt = reinterpret_cast<IO*>(p + 2 * bufB + bufBt);
-    r.sEnd = reinterpret_cast<float4*>(p + 2 * bufB + bufBt + bufXt);
-    return r;
-  };
-  auto getcoef = [&](int ck) {
-    char* p = coefBase + (size_t)(ck % 3) * coefStride;
-    PcCoef r;
-    r.sTok = reinterpret_cast<float4*>(p);
-    r.sW = reinterpret_cast<float*>(p + (size_t)Q * 16);
-    r.sMisc = reinterpret_cast<float*>(p + (size_t)Q * 20);
-    return r;
-  };
-  // Zero both tile buffers and the score tile once: padding rows and
-  // columns, and score blocks above the diagonal, are never written.
-  for (size_t e = tid; e < (2 * bufStride + smStride) / 16; e += kPcThreads)
-    reinterpret_cast<uint4*>(smem)[e] = make_uint4(0u, 0u, 0u, 0u);
-  if (mode == kPcSummary)
-    for (int j = tid; j < N / 2; j += kPcThreads) sSeg[j] = 0.f;
-
-  const float Ah = a.A[hh];
-  const float Dh = a.D[hh];
-  const size_t tokBC = (size_t)H * R * N;
-  const size_t tokX = (size_t)H * R * P;
-  const size_t tokTh = (size_t)H * (N / 2);
-  const IO* Bg = static_cast<const IO*>(a.B) + ((size_t)b * T * H + hh) * R * N;
-  const IO* Cg = static_cast<const IO*>(a.C) + ((size_t)b * T * H + hh) * R * N;
-  const IO* Xg = static_cast<const IO*>(a.x) + ((size_t)b * T * H + hh) * R * P;
-  IO* Yg = static_cast<IO*>(a.y) + ((size_t)b * T * H + hh) * R * P;
-  const float* THg = a.theta + ((size_t)b * T * H + hh) * (N / 2);
-  const float* DTg = a.dt + (size_t)b * T * H + hh;
-  const float* LMg = a.lam + (size_t)b * T * H + hh;
-
-  auto chunk_len = [&](int ck) { return (T - ck * Q < Q) ? (T - ck * Q) : Q; };
-
-  if (producer) {
-    // ======================= producers (waves 0-3) =======================
-    // Item = (row group rg: 4 consecutive (token, rank) rows, pair group pg:
-    // 4 state pairs = 8 columns).  Lanes run over GW adjacent pair groups
-    // first, then over the RG = rows_pad/4 row groups, so 16 lanes read GW*16
-    // contiguous bytes of 16/GW rows (few cache lines per load instruction),
-    // and the RG row groups of one pair group stay inside one wave (GW*RG <=
-    // 64): the angle prefix over the chunk is an in-wave strided scan.
-    // Inside the chunk loop every load and every use of a loaded register is
-    // unconditional (threads past the item count work on a clamped duplicate
-    // item and skip only their LDS stores): a load or use behind a branch
-    // would make the compiler wait for all outstanding loads.
-    const int pt = tid;
-    const int pw = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform producer index
-    const int RG = rows_pad / 4;
-    const int npg = N / 8;
-    const int GW = npg < 64 / RG ? npg : 64 / RG;  // pair groups per lane group
-    const int npx = P / 8;
-    const int GX = npx < 64 / RG ? npx : 64 / RG;  // x column groups per lane group
-    const int nbitems = RG * npg;
-    const int nxitems = RG * npx;
-    const int ntok = 4 >> lgR;  // tokens per row group (R <= 4)
-    const IO* const Csrc = has_y ? Cg : Bg;  // segment summaries never read C
-    // Two register sets: chunk i is built from one while chunk i+1's loads
-    // land in the other, and chunk i+2's loads are issued into the first
-    // right after it is consumed (two chunks of HBM latency hidden).
-    PcRaw<IO, MI, MX> rsA, rsB;
-    float rdt, rlm, rdtn, rlmn;  // raw dt/lam of the chunk after next
-
-    // Per item: row group, column group, and 32-bit element offsets of its
-    // rows relative to the chunk's first token (the host keeps
-    // chunk * heads * rank * max(N, P) below 2^31).
-    int irg[MI], ipg[MI], rtok[MI][4];
-    bool ist[MI];
-    uint32_t ob[MI][4], oth[MI][4], obs[MI], oths[MI];
-    int xrg[MX], xxg[MX], xtok[MX][4];
-    bool xst[MX];
-    uint32_t ox[MX][4], oxs[MX];
-#pragma unroll
-    for (int m = 0; m < MI; ++m) {
-      const int it0 = pt + m * kProdThreads;
-      ist[m] = it0 < nbitems;
-      const int it = ist[m] ? it0 : it0 % nbitems;
-      const int rg = (it / GW) % RG, pg = (it / (GW * RG)) * GW + it % GW;
-      irg[m] = rg;
-      ipg[m] = pg;
-      const int t0 = (4 * rg) >> lgR;
-      obs[m] = 8u * pg;
-      oths[m] = 4u * pg;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int rho = 4 * rg + k;
-        rtok[m][k] = rho < rows ? (rho >> lgR) : Q;
-        ob[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokBC + (uint32_t)(rho & (R - 1)) * N + 8 * pg;
-        oth[m][k] = (uint32_t)(t0 + (k < ntok ? k : ntok - 1)) * (uint32_t)tokTh + 4 * pg;
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < MX; ++m) {
-      const int it0 = pt + m * kProdThreads;
-      xst[m] = it0 < nxitems;
-      const int it = xst[m] ? it0 : it0 % nxitems;
-      const int rg = (it / GX) % RG, xg = (it / (GX * RG)) * GX + it % GX;
-      xrg[m] = rg;
-      xxg[m] = xg;
-      oxs[m] = 8u * xg;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int rho = 4 * rg + k;
-        xtok[m][k] = rho < rows ? (rho >> lgR) : Q;
-        ox[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokX + (uint32_t)(rho & (R - 1)) * P + 8 * xg;
-      }
-    }
-
-    auto load_chunk = [&](int ck, PcRaw<IO, MI, MX>& rs) {  // B, C, x, theta of chunk ck (rows past the chunk read token 0)
-      const int c0 = ck * Q, Lc = chunk_len(ck);
-      const IO* Bc = Bg + (size_t)c0 * tokBC;
-      const IO* Cc = Csrc + (size_t)c0 * tokBC;
-      const IO* Xc = Xg + (size_t)c0 * tokX;
-      const float* Tc = THg + (size_t)c0 * tokTh;
-#pragma unroll
-      for (int m = 0; m < MI; ++m) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t o = rtok[m][k] < Lc ? ob[m][k] : obs[m];
-          rs.b[m][k].load(Bc + o);
-          rs.c[m][k].load(Cc + o);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t o = rtok[m][0] + (q < ntok ? q : ntok - 1) < Lc ? oth[m][q] : oths[m];
-          rs.th[m][q] = *reinterpret_cast<const float4*>(Tc + o);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MX; ++m) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t o = xtok[m][k] < Lc ? ox[m][k] : oxs[m];
-          rs.x[m][k].load(Xc + o);
-        }
-      }
-    };
-    auto load_dt = [&](int ck) {  // dt, lam of chunk ck (lane = token) and of the token after it
-      const int c0 = ck * Q, Lc = chunk_len(ck);
-      const int t = lane < Lc ? lane : Lc - 1;
-      rdt = DTg[(size_t)(c0 + t) * H];
-      rlm = LMg[(size_t)(c0 + t) * H];
-      const int tn = (c0 + Lc < T) ? c0 + Lc : c0 + Lc - 1;
-      rdtn = DTg[(size_t)tn * H];
-      rlmn = LMg[(size_t)tn * H];
-    };
-    // In-chunk decay scan and per-token coefficients of chunk ck -> coef slot
-    // ck % 3 (producer wave 0 only, which alone loads dt and lam).
-    // sTok[t] = {A_t, B_t, L_t, 0} with L_t = l_t log2(e) and the mask weights
-    // gamma_t 2^{L_q - L_t} = 2^{L_q - A_t},  beta_{t+1} 2^{L_q - L_{t+1}} = 2^{L_q - B_t}
-    // (a zero weight gives an infinite exponent and an exact zero).
-    auto decay_coefs = [&](int ck, bool store) {
-      const int c0 = ck * Q, Lc = chunk_len(ck);
-      const bool fold_next = c0 + Lc < T;
-      const PcCoef co = getcoef(ck);
-      const int t = lane;
-      const bool valid = t < Lc;
-      const float dtv = valid ? rdt : 0.f, lmv = valid ? rlm : 0.f;
-      const float av = (valid && t > 0) ? dtv * Ah : 0.f;
-      const float ell = wave_inclusive_scan(av);
-      const float2 wt = input_weights(dtv, lmv, expf(dtv * Ah), a.disc);
-      const float bet = wt.x, gam = wt.y;
-      const float dtn = fold_next ? rdtn : 0.f, lmn = fold_next ? rlmn : 0.f;
-      const float ell_last = __shfl(ell, Lc - 1, kWave);
-      const float ellE = ell_last + dtn * Ah;
-      const float bet_up = __shfl_down(bet, 1, kWave);
-      const float ell_up = __shfl_down(ell, 1, kWave);
-      const bool inner = t < Lc - 1, lastv = t == Lc - 1;
-      const float betn = inner ? bet_up : (lastv ? input_weights(dtn, lmn, expf(dtn * Ah), a.disc).x : 0.f);
-      const float elln = inner ? ell_up : ellE;
-      const float ellv = valid ? ell : ell_last;
-      const float w = valid ? (gam * expf(ellE - ellv) + betn * expf(ellE - elln)) : 0.f;
-      const float inf = __builtin_huge_valf();
-      const float L2 = ellv * kLog2ePc;
-      const float Ak = (valid && gam > 0.f) ? L2 - __log2f(gam) : inf;
-      const float Bk = (valid && betn > 0.f) ? elln * kLog2ePc - __log2f(betn) : inf;
-      // key factor for score blocks below the diagonal: with e the last token
-      // of the key's 16-row block, M[q][k] = 2^{L_q - L_e} * Kf_k for every
-      // query q after that block (both factors <= 1 except Kf's beta term at
-      // k = e, which is 1/alpha of the next token)
-      const int te = t | ((16 >> lgR) - 1);
-      const float Le = __shfl(L2, te < Lc ? te : Lc - 1, kWave);
-      const float Kf = valid ? gam * exp2f(Le - L2) + betn * exp2f(Le - elln * kLog2ePc) : 0.f;
-      if (store && t < Q) {
-        co.sTok[t] = make_float4(Ak, Bk, L2, Kf);
-        co.sW[t] = w;
-        if (t == 0) {
-          co.sMisc[0] = ellE;
-          co.sMisc[1] = ellE * kLog2ePc;
-        }
-      }
-    };
-    // Angles (in-wave scan), rotation, and the tiles of chunk ck -> tile buffer ck % 2.
-    auto build_tiles = [&](int ck, const PcRaw<IO, MI, MX>& rs) {
-      const int Lc = chunk_len(ck);
-      const int te = Lc - 1;
-      const PcBuf<IO, N, P> bf = getbuf(ck);
-      const float* sW = getcoef(ck).sW;
-#pragma unroll
-      for (int m = 0; m < MI; ++m) {
-        const int rg = irg[m], pg = ipg[m];
-        const int t0 = rtok[m][0];
-        float th[4][4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float tv = (q < ntok && t0 + q < Lc) ? 1.f : 0.f;
-          th[q][0] = tv * rs.th[m][q].x;
-          th[q][1] = tv * rs.th[m][q].y;
-          th[q][2] = tv * rs.th[m][q].z;
-          th[q][3] = tv * rs.th[m][q].w;
-        }
-        // exclusive prefix of the row groups' totals within the pair group
-        float base[4], tot[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          tot[j] = th[0][j] + th[1][j] + th[2][j] + th[3][j];
-          base[j] = tot[j];
-        }
-        strided_inclusive_scan(base, GW, RG);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) base[j] -= tot[j];
-        // per-row angles: rows of one token share its prefix
-        float ph[4][4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int kq = R == 1 ? k : (k >> lgR);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            ph[k][j] = base[j] + th[0][j] + (kq >= 1 ? th[1][j] : 0.f) + (kq >= 2 ? th[2][j] : 0.f) +
-                       (kq >= 3 ? th[3][j] : 0.f);
-        }
-        float bt[4][8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int rho = 4 * rg + k;
-          const int t = rtok[m][k];
-          // rows past the chunk hold finite duplicates (clamped loads); every
-          // use of them is weighted by an exact zero (mask, w) or never stored
-          const bool valid = t < Lc;
-          float bv[8];
-          rs.b[m][k].unpack(bv);
-          float cs4[4], sn4[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float sn, cs;
-            trig<IO>(ph[k][j], sn, cs);
-            cs4[j] = cs;
-            sn4[j] = sn;
-            rot2(bv[2 * j], bv[2 * j + 1], cs4[j], -sn4[j]);
-          }
-          const float wt = valid ? sW[t < Q ? t : 0] : 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bt[k][e] = bv[e] * wt;
-          // the row-major B~ and C~ tiles feed only the outputs; a segment
-          // summary needs just the state update's tiles
-          if (ist[m] && has_y) {
-            float cv[8];
-            rs.c[m][k].unpack(cv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) rot2(cv[2 * j], cv[2 * j + 1], cs4[j], -sn4[j]);
-            store8(bf.sB + rho * LDN + 8 * pg, bv);
-            store8(bf.sC + rho * LDN + 8 * pg, cv);
-          }
-          if (ist[m]) {
-            if (valid && t == te && (rho & (R - 1)) == 0) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                bf.sEnd[4 * pg + j] = make_float4(cs4[j], sn4[j], ph[k][j], 0.f);
-            }
-          }
-        }
-        if (ist[m]) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float col[4] = {bt[0][e], bt[1][e], bt[2][e], bt[3][e]};
-            store4(bf.sBt + (8 * pg + e) * ldr + 4 * rg, col);
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MX; ++m) {
-        const int rg = xrg[m], xg = xxg[m];
-        if constexpr (sizeof(IO) == 2) {
-          // transpose 4 rows x 8 bf16 columns with byte permutes (no unpack)
-          uint32_t w[4][4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w[k][q] = rs.x[m][k].w[q];
-          uint2 v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            v[e].x = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
-            v[e].y = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
-          }
-          if (xst[m]) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2*>(bf.sXt + (8 * xg + e) * ldr + 4 * rg) = v[e];
-          }
-        } else {
-          float xv[4][8];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) rs.x[m][k].unpack(xv[k]);
-          if (xst[m]) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float col[4] = {xv[0][e], xv[1][e], xv[2][e], xv[3][e]};
-              store4(bf.sXt + (8 * xg + e) * ldr + 4 * rg, col);
-            }
-          }
-        }
-      }
-    };
-
-    // One pipeline step = one chunk and two barriers (the consumers count the
-    // same: two per chunk plus a last pair).  Building chunk i overlaps the
-    // consumers' shared score tile of chunk i-1 (other buffers); the first
-    // barrier ends both, and the coefficient work and the next loads then
-    // overlap the consumers' outputs and state update.
-    auto step = [&](int i, PcRaw<IO, MI, MX>& rs) {
-      build_tiles(i, rs);
-      __syncthreads();
-      const int n1 = i + 1 < ck1 ? i + 1 : i;  // clamped: past the end the data is reloaded, not used
-      const int n2 = i + 2 < ck1 ? i + 2 : n1;
-      if (pw == 0) {
-        decay_coefs(n1, n1 != i);
-        // dt first: the vmcnt counter is in order, so consuming dt next step
-        // then leaves this step's chunk batch in flight
-        load_dt(n2);
-      }
-      load_chunk(n2, rs);
-      __syncthreads();
-    };
-    if (ck0 < ck1) {
-      // prologue: coefficients of the first chunk, then the first prefetches
-      const int n1 = ck0 + 1 < ck1 ? ck0 + 1 : ck0;
-      if (pw == 0) {
-        load_dt(ck0);
-        decay_coefs(ck0, true);
-      }
-      load_chunk(ck0, rsA);
-      if (pw == 0) load_dt(n1);
-      load_chunk(n1, rsB);
-    }
-    __syncthreads();
-    // the pair loop has no conditional loads, so the wait counts the compiler
-    // derives around its back edge stay exact (only the batch consumed waits)
-    int i = ck0;
-    for (; i + 1 < ck1; i += 2) {
-      step(i, rsA);
-      step(i + 1, rsB);
-    }
-    if (i < ck1) step(i, rsA);
-    __syncthreads();
-    __syncthreads();
-  } else {
-    // ======================= consumers (waves 4-7) =======================
-    const int cw = __builtin_amdgcn_readfirstlane(wave - 4);  // wave-uniform
-    f32x4 Hreg[PBW][NB];  // E^T tiles: rows n = 16nb + 4g + i, column p = 16pb + c
-    float lsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < PBW; ++u)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) Hreg[u][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      float alpha0 = 0.f, beta0 = 0.f;
-      if (mode == kPcFused) {
-        const float dt0 = DTg[0];
-        const float lm0 = LMg[0];
-        alpha0 = expf(dt0 * Ah);
-        beta0 = input_weights(dt0, lm0, alpha0, a.disc).x;
-      }
-#pragma unroll
-      for (int u = 0; u < PBW; ++u) {
-        const int pb = cw + kConsWaves * u;
-        if (pb < PB) {
-          const int p = 16 * pb + c;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int n0 = 16 * nb + 4 * g;
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if (mode == kPcFused) {
-              float h0[4];
-              load4(a.h + ((size_t)chain * P + p) * N + n0, h0);
-              const IO* Bp = static_cast<const IO*>(a.B_prev) + (size_t)chain * R * N;
-              const IO* Xp = static_cast<const IO*>(a.x_prev) + (size_t)chain * R * P;
-#pragma unroll
-              for (int i4 = 0; i4 < 4; ++i4) v[i4] = alpha0 * h0[i4];
-              for (int r = 0; r < R; ++r) {
-                float bp[4];
-                load4(Bp + r * N + n0, bp);
-                const float xp = beta0 * to_f32(Xp[r * P + p]);
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) v[i4] += xp * bp[i4];
-              }
-            } else if (mode == kPcSegment) {
-              load4(a.seg_state + (((size_t)seg * kp.batch * H + chain) * P + p) * N + n0, v);
-            }
-            Hreg[u][nb] = f32x4{v[0], v[1], v[2], v[3]};
-          }
-        }
-      }
-    }
-    // the entry-state loads retire here, once: otherwise the loop below would
-    // wait for every outstanding memory operation at each first use of Hreg
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    // y of chunk jy leaves the LDS output tile as whole 16-byte runs of its
-    // rows (each (token, rank) row is P contiguous elements in HBM)
-    constexpr int EG = Gran<IO>::kN;                 // elements per 16-byte granule
-    constexpr int G16 = P / EG;                      // granules per row (2 .. 32)
-    constexpr int kCT = kConsWaves * kWave;          // consumer threads
-    constexpr int KZ = (RMAX * G16 + kCT - 1) / kCT;  // granules per consumer thread
-    const int ct = tid - kProdThreads;
-    auto gran_off = [&](int c0, int e) -> size_t {
-      const int row = e / G16, gq = e % G16;
-      return (size_t)(c0 + (row >> lgR)) * tokX + (row & (R - 1)) * P + gq * EG;
-    };
-    // Output epilogue (pre-gate grouped RMSNorm): a consumer thread always
-    // handles granule column ct % G16 of its rows (kCT is a multiple of G16),
-    // so its EG weights are loaded once; the G16 granules of one row sit in
-    // G16 aligned consecutive lanes, which sum the squares among themselves.
-    // The gate of chunk j is loaded one iteration ahead of its use.
-    const bool gated = has_y && a.gz != nullptr;
-    const IO* Zg = gated ? static_cast<const IO*>(a.gz) + ((size_t)b * T * H + hh) * R * P : nullptr;
-    float gwr[EG];
-    uint4 zr[KZ];
-    if (gated) {
-#pragma unroll
-      for (int q = 0; q < EG; ++q) gwr[q] = a.gw[(size_t)hh * P + (ct % G16) * EG + q];
-    }
-    auto load_z = [&](int jz) {
-      const int ng = chunk_len(jz) * R * G16;
-#pragma unroll
-      for (int k = 0; k < KZ; ++k) {
-        const int e = ct + k * kCT;  // clamped duplicate past the tail, never used
-        zr[k] = *reinterpret_cast<const uint4*>(Zg + gran_off(jz * Q, e < ng ? e : ng - 1));
-      }
-    };
-    auto store_y = [&](int jy) {
-      const int c0 = jy * Q, ng = chunk_len(jy) * R * G16;
-      for (int e = ct; e < ng; e += kCT) {
-        const int row = e / G16, gq = e % G16;
-        *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG);
-      }
-    };
-    uint4 gres[KZ];
-    auto gate_y = [&](int jy) {
-      const int ng = chunk_len(jy) * R * G16;
-#pragma unroll
-      for (int k = 0; k < KZ; ++k) {
-        const int e = ct + k * kCT;
-        if (e < ng) {  // whole rows: all G16 lanes of a row agree
-          const int row = e / G16, gq = e % G16;
-          float v[EG], z[EG];
-          Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG), v);
-          float ss = 0.f;
-#pragma unroll
-          for (int q = 0; q < EG; ++q) ss += v[q] * v[q];
-          ss = lane_group_sum(ss, G16);
-          const float inv = rsqrtf(ss * (1.0f / P) + a.geps);
-          Gran<IO>::unpack(zr[k], z);
-#pragma unroll
-          for (int q = 0; q < EG; ++q) v[q] = gate_out(v[q], inv, gwr[q], z[q]);
-          gres[k] = Gran<IO>::pack(v);
-        }
-      }
-    };
-    auto store_gated = [&](int jy) {
-      const int c0 = jy * Q, ng = chunk_len(jy) * R * G16;
-#pragma unroll
-      for (int k = 0; k < KZ; ++k) {
-        const int e = ct + k * kCT;
-        if (e < ng) *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = gres[k];
-      }
-    };
-    for (int i = ck0; i <= ck1; ++i) {
-      if (gated) {
-        // results of chunk i-2, then the gate loads of chunk i-1, then the
-        // stores: loads issued ahead of the stores never wait for them
-        if (i >= ck0 + 2) gate_y(i - 2);
-        if (i > ck0) load_z(i - 1);
-        if (i >= ck0 + 2) store_gated(i - 2);
-      } else if (has_y && i >= ck0 + 2) {
-        store_y(i - 2);
-      }
-      // ---- phase 1: this wave's 16x16 blocks of S.M for chunk i-1 ----
-      // Blocks (rb, kb), kb <= rb, are dealt round-robin to the 4 consumer
-      // waves.  S^T = Bt Ct^T leaves the accumulator with 4 consecutive keys
-      // per lane for one query, masked by the trapezoid decay and stored as
-      // one 4-element run of row `query` of sSM (D x on the diagonal).
-      if (i > ck0 && has_y) {
-        const int j = i - 1;
-        const PcBuf<IO, N, P> bf = getbuf(j);
-        const PcCoef co = getcoef(j);
-        const int rbn = (rows + 15) >> 4;
-        const int nblk = rbn * (rbn + 1) / 2;
-        // groups of up to kGrp blocks in straight-line code, so the LDS reads
-        // of a group are all in flight before its first product
-        constexpr int NBLK = RBM * (RBM + 1) / 2, NQ = (NBLK + kConsWaves - 1) / kConsWaves;
-        constexpr int kGrp = NQ < 3 ? NQ : 3;
-        for (int q0 = 0; q0 < NQ; q0 += kGrp) {
-          int rbq[kGrp], kbq[kGrp];
-          bool okq[kGrp];
-#pragma unroll
-          for (int q = 0; q < kGrp; ++q) {
-            const int bi = cw + kConsWaves * (q0 + q);
-            okq[q] = bi < nblk;
-            int rem = okq[q] ? bi : 0, rb = 0;
-            while (rem > rb) {  // block index -> (row block, key block), kb <= rb
-              rem -= rb + 1;
-              ++rb;
-            }
-            rbq[q] = rb;
-            kbq[q] = rem;
-          }
-          Frag<IO> Bf[kGrp][NS], Cf[kGrp][NS];
-          float4 kt[kGrp][4];
-          float lq[kGrp], le[kGrp];
-#pragma unroll
-          for (int q = 0; q < kGrp; ++q) {
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {  // K = n in natural order (one 16-byte read each)
-              Bf[q][ns].load8(bf.sB + (16 * kbq[q] + c) * LDN + 32 * ns + 8 * g);
-              Cf[q][ns].load8(bf.sC + (16 * rbq[q] + c) * LDN + 32 * ns + 8 * g);
-            }
-            const int tq = (16 * rbq[q] + c) >> lgR;
-            lq[q] = co.sTok[tq < Q ? tq : Q - 1].z;
-            const int tkl = (16 * kbq[q] + 15) >> lgR;  // last token of the key block
-            le[q] = co.sTok[tkl < Q ? tkl : Q - 1].z;
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-              const int tk = (16 * kbq[q] + 4 * g + i4) >> lgR;
-              kt[q][i4] = co.sTok[tk < Q ? tk : Q - 1];
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < kGrp; ++q) {
-            f32x4 St = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) mma(St, Bf[q][ns], Cf[q][ns]);
-            const int rq = 16 * rbq[q] + c, tq = rq >> lgR;
-            float v[4];
-            if (kbq[q] < rbq[q]) {
-              // below the diagonal every key precedes every query: one row
-              // factor 2^{L_q - L_e} times the key factors
-              const float rf = __builtin_amdgcn_exp2f(lq[q] - le[q]);
-#pragma unroll
-              for (int i4 = 0; i4 < 4; ++i4) v[i4] = St[i4] * (rf * kt[q][i4].w);
-            } else {
-#pragma unroll
-              for (int i4 = 0; i4 < 4; ++i4) {
-                const int rk = 16 * kbq[q] + 4 * g + i4, tk = rk >> lgR;
-                float m = (tk <= tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].x) : 0.f;
-                m += (tk < tq) ? __builtin_amdgcn_exp2f(lq[q] - kt[q][i4].y) : 0.f;
-                v[i4] = St[i4] * m + ((rk == rq) ? Dh : 0.f);
-              }
-            }
-            if (okq[q]) store4(sSM + rq * ldr + 16 * kbq[q] + 4 * g, v);
-          }
-        }
-      }
-      __syncthreads();
-      // ---- phase 2: outputs and state update for this wave's p-blocks ----
-      if (i > ck0) {
-        const int j = i - 1;
-        const int c0 = j * Q, Lc = chunk_len(j);
-        const PcBuf<IO, N, P> bf = getbuf(j);
-        const PcCoef co = getcoef(j);
-        const bool last_chunk = j == ck1 - 1;
-#pragma unroll
-        for (int u = 0; u < PBW; ++u) {
-          const int pb = cw + kConsWaves * u;
-          if (pb >= PB) continue;
-          if (has_y) {
-            // carried-state operand: E^T rows p, K = n in the accumulator order
-            Frag<IO> Hf[NS];
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-              for (int i4 = 0; i4 < 4; ++i4) {
-                Hf[ns].set(i4, Hreg[u][2 * ns][i4]);
-                Hf[ns].set(4 + i4, (2 * ns + 1 < NB) ? Hreg[u][(2 * ns + 1 < NB) ? 2 * ns + 1 : 0][i4] : 0.f);
-              }
-            Frag<IO> Xf[KSM];  // K = keys in natural order, as the score rows below
-#pragma unroll
-            for (int ks = 0; ks < KSM; ++ks) Xf[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
-#pragma unroll
-            for (int rb = 0; rb < RBM; ++rb) {
-              const int rho = 16 * rb + c;
-              f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-              {
-                Frag<IO> Cf[NS];
-#pragma unroll
-                for (int ns = 0; ns < NS; ++ns) {
-                  const IO* cr = bf.sC + rho * LDN + 32 * ns + 4 * g;
-                  Cf[ns].load44(cr, cr + 16);
-                }
-#pragma unroll
-                for (int ns = 0; ns < NS; ++ns) mma(acc, Hf[ns], Cf[ns]);
-                const int tq = rho >> lgR;
-                acc = acc * __builtin_amdgcn_exp2f(co.sTok[tq < Q ? tq : Q - 1].z);
-              }
-#pragma unroll
-              for (int ks = 0; ks < KSM; ++ks) {
-                if (2 * ks <= rb) {
-                  Frag<IO> SMf;
-                  SMf.load8(sSM + rho * ldr + 32 * ks + 8 * g);
-                  mma(acc, Xf[ks], SMf);
-                }
-              }
-              // y (row rho, columns 16pb + 4g .. +3) into the output tile
-              const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-              store4(sY + rho * ldy + 16 * pb + 4 * g, v);
-            }
-          }
-          // state update and rotation into the next chunk's frame
-          const float decE = expf(co.sMisc[0]);
-          // all operands first (independent LDS reads), then the MFMA chains
-          Frag<IO> Xs[KSM];
-          Frag<IO> Bs[NB][KSM];
-          float2 r0[NB], r1[NB];
-#pragma unroll
-          for (int ks = 0; ks < KSM; ++ks) Xs[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-            for (int ks = 0; ks < KSM; ++ks) Bs[nb][ks].load8(bf.sBt + (16 * nb + c) * ldr + 32 * ks + 8 * g);
-            const float4 e0 = bf.sEnd[8 * nb + 2 * g];
-            const float4 e1 = bf.sEnd[8 * nb + 2 * g + 1];
-            r0[nb] = make_float2(e0.x, e0.y);
-            r1[nb] = make_float2(e1.x, e1.y);
-          }
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            f32x4 hacc = Hreg[u][nb] * decE;
-#pragma unroll
-            for (int ks = 0; ks < KSM; ++ks) mma(hacc, Bs[nb][ks], Xs[ks]);
-            float v[4] = {hacc[0], hacc[1], hacc[2], hacc[3]};
-            rot2(v[0], v[1], r0[nb].x, r0[nb].y);
-            rot2(v[2], v[3], r1[nb].x, r1[nb].y);
-            Hreg[u][nb] = f32x4{v[0], v[1], v[2], v[3]};
-            if (last_chunk) {
-              const int p = 16 * pb + c, n0 = 16 * nb + 4 * g;
-              if (writes_final)
-                store4(a.h + ((size_t)chain * P + p) * N + n0, v);
-              else if (mode == kPcSummary)
-                store4(a.seg_state + (((size_t)seg * kp.batch * H + chain) * P + p) * N + n0, v);
-            }
-          }
-        }
-        if (mode == kPcSummary) {
-          const int ct = tid - kProdThreads;
-          if (ct < N / 2) {
-            const float tot = sSeg[ct] + bf.sEnd[ct].z;
-            sSeg[ct] = tot;
-            if (last_chunk) a.seg_angle[((size_t)seg * kp.batch * H + chain) * (N / 2) + ct] = tot;
-          }
-          if (ct == 0) {
-            lsum += co.sMisc[0];
-            if (last_chunk) a.seg_decay[(size_t)seg * kp.batch * H + chain] = lsum;
-          }
-        }
-      }
-      __syncthreads();
-    }
-    if (gated && ck1 > ck0) {
-      gate_y(ck1 - 1);
-      store_gated(ck1 - 1);
-    } else if (has_y && ck1 > ck0) {
-      store_y(ck1 - 1);
-    }
-  }
-
-  if (writes_final) {
-    const IO* Bl = Bg + (size_t)(T - 1) * tokBC;
-    const IO* Xl = Xg + (size_t)(T - 1) * tokX;
-    IO* Bp = static_cast<IO*>(a.B_prev) + (size_t)chain * R * N;
-    IO* Xp = static_cast<IO*>(a.x_prev) + (size_t)chain * R * P;
-    for (int e = tid; e < R * N; e += kPcThreads) Bp[e] = Bl[e];
-    for (int e = tid; e < R * P; e += kPcThreads) Xp[e] = Xl[e];
-  }
-}
-
-template <typename IO, int N, int P>
-hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int mode, int nblocks) {
-  const size_t lds = PcLds<IO, N, P>::bytes(PcLimits<IO, N, P>::kMaxRows);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  PcParams kp;
-  kp.a = a;
-  kp.batch = d.batch;
-  kp.heads = d.heads;
-  kp.R = d.R;
-  kp.lgR = d.R == 1 ? 0 : (d.R == 2 ? 1 : 2);
-  kp.Q = d.Q;
-  kp.mode = mode;
-  kp.nblocks = nblocks;
-  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
-  return hipGetLastError();
-}
-
-template <typename IO, int N>
-hipError_t pc_p(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nb) {
-  switch (d.P) {
-    case 16: return launch_pc_t<IO, N, 16>(d, a, s, mode, nb);
-    case 32: return launch_pc_t<IO, N, 32>(d, a, s, mode, nb);
-    case 64: return launch_pc_t<IO, N, 64>(d, a, s, mode, nb);
-    default: return launch_pc_t<IO, N, 128>(d, a, s, mode, nb);
-  }
-}
-
-template <typename IO>
-hipError_t pc_n(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nb) {
-  switch (d.N) {
-    case 16: return pc_p<IO, 16>(d, a, s, mode, nb);
-    case 32: return pc_p<IO, 32>(d, a, s, mode, nb);
-    case 64: return pc_p<IO, 64>(d, a, s, mode, nb);
-    default: return pc_p<IO, 128>(d, a, s, mode, nb);
-  }
-}
-
-template <typename IO>
-int pc_max_rows(const Dims& d) {
-  switch (d.N * 1000 + d.P) {
-#define M3_CASE(NN, PP) \
-  case NN * 1000 + PP: return PcLimits<IO, NN, PP>::kMaxRows;
-    M3_CASE(16, 16) M3_CASE(16, 32) M3_CASE(16, 64) M3_CASE(16, 128)
-    M3_CASE(32, 16) M3_CASE(32, 32) M3_CASE(32, 64) M3_CASE(32, 128)
-    M3_CASE(64, 16) M3_CASE(64, 32) M3_CASE(64, 64) M3_CASE(64, 128)
-    M3_CASE(128, 16) M3_CASE(128, 32) M3_CASE(128, 64) M3_CASE(128, 128)
-#undef M3_CASE
-    default: return 0;
-  }
-}
-
-}  // namespace
 
 bool prefill_pc_supported(const Dims& d) {
   const int rows_pad = ((d.Q * d.R) + 31) & ~31;
@@ -917,7 +11,9 @@ bool prefill_pc_supported(const Dims& d) {
 }
 
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks) {
-  return d.bf16 ? pc_n<bf16>(d, a, s, mode, nblocks) : pc_n<float>(d, a, s, mode, nblocks);
+  // segment summaries write no y, so they never need the epilogue
+  if (a.gz && mode != kPcSummary) return launch_prefill_pc_gated(d, a, s, mode, nblocks);
+  return launch_pc<false>(d, a, s, mode, nblocks);
 }
 
 }  // namespace m3
