@@ -338,6 +338,25 @@ def prefill_chunked(x, Bm, Cm, dt, lam, theta, A, D, state=None, chunk=64, disc=
     return y, (h_out, Bp_out, xp_out)
 
 
+def rank_down_projection(y, down):
+    """MIMO read-out: the R rank outputs of a (token, head) folded into one row
+    of P channels.
+
+    lilting.ch Mamba-3 article, "3. MIMO SSM" (channels enter one rank-r SSM
+    and leave it as channels again, coupled through an r-dimensional
+    subspace): the rank-r output is brought back to the P channels by a
+    learned per-(head, rank, channel) weight, channel by channel:
+        s[..., h, p] = sum_r down[h, r, p] * y[..., h, r, p]
+    y: (..., H, R, P); down: (H, R, P).  Returns (..., H, P).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    down = np.asarray(down, dtype=np.float64)
+    s = np.zeros(y.shape[:-2] + y.shape[-1:])
+    for r in range(y.shape[-2]):
+        s = s + down[:, r, :] * y[..., r, :]
+    return s
+
+
 def gated_rmsnorm(y, z, weight, eps):
     """Output epilogue: pre-gate grouped RMSNorm of the scan output.
 

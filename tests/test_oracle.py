@@ -583,3 +583,61 @@ def test_gated_rmsnorm_pins_catch_planted_mistake(bad, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught > 0
+
+
+# ---------------------------------------------------------------------------
+# MIMO rank down-projection (read-out of the R rank outputs to P channels)
+# ---------------------------------------------------------------------------
+
+def _down_example():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rank_down_worked.json")))
+    return g, np.array(g["y"])[None, :, :], np.array(g["down"])[None, :, :]   # (H=1, R=2, P=2)
+
+
+def test_rank_down_worked_example():
+    g, y, down = _down_example()
+    s = oracle.rank_down_projection(y, down)
+    assert np.max(np.abs(s[0] - np.array(g["s"]))) < g["tolerance"]
+    out = oracle.gated_rmsnorm(s[:, None, :], np.array(g["z"])[None, None, :], np.array(g["weight"])[None, :],
+                               g["eps"])
+    assert np.max(np.abs(out[0, 0] - np.array(g["out"]))) < g["tolerance"]
+
+
+def test_rank_down_special_cases():
+    """One-hot weights pick one rank; unit weights sum the ranks (numpy's sum)."""
+    rng = np.random.default_rng(21)
+    b, T, H, R, P = 2, 3, 3, 4, 8
+    y = rng.standard_normal((b, T, H, R, P))
+    for r0 in range(R):
+        onehot = np.zeros((H, R, P))
+        onehot[:, r0, :] = 1.0
+        assert np.array_equal(oracle.rank_down_projection(y, onehot), y[..., r0, :])
+    assert relerr(oracle.rank_down_projection(y, np.ones((H, R, P))), np.sum(y, axis=-2)) < 1e-15
+
+
+def test_rank_down_matches_torch_einsum():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(22)
+    y = rng.standard_normal((2, 5, 3, 4, 16))
+    down = rng.standard_normal((3, 4, 16))
+    ref = torch.einsum("bthrp,hrp->bthp", torch.from_numpy(y), torch.from_numpy(down)).numpy()
+    assert relerr(oracle.rank_down_projection(y, down), ref) < 1e-14
+
+
+def _bad_down_transposed(y, down):
+    """Weights indexed [h, p, r] (only defined when R == P)."""
+    down = np.asarray(down, dtype=np.float64)
+    return np.sum(np.swapaxes(down, -1, -2)[None] * np.asarray(y, dtype=np.float64), axis=-2)
+
+
+def _bad_down_rank_shift(y, down):
+    """Rank r weighted by rank r+1's weights."""
+    down = np.roll(np.asarray(down, dtype=np.float64), 1, axis=1)
+    return np.sum(down * np.asarray(y, dtype=np.float64), axis=-2)
+
+
+@pytest.mark.parametrize("bad", [_bad_down_transposed, _bad_down_rank_shift])
+def test_rank_down_pins_catch_planted_mistake(bad, monkeypatch):
+    monkeypatch.setattr(oracle, "rank_down_projection", bad)
+    with pytest.raises(AssertionError):
+        test_rank_down_worked_example()
