@@ -73,6 +73,15 @@ def gate_bytes(w, tokens):
     return w.batch * tokens * w.heads * w.rank * w.headdim * e + w.heads * w.headdim * 4
 
 
+def down_bytes_delta(w, tokens):
+    """Change in bytes when the R rank outputs are folded into P channels
+    before the epilogue: y and z lose the rank axis, the fp32 projection
+    weights (heads, R, P) are read once."""
+    e = 2 if w.io_dtype == "bf16" else 4
+    rows = w.batch * tokens * w.heads * w.headdim
+    return -2 * (w.rank - 1) * rows * e + w.heads * w.rank * w.headdim * 4
+
+
 def decode_bytes(w):
     """Algorithmic bytes of one decode step: h read + written, pending pair
     read + written, one token of x, B, C, dt, lam, theta read, y written."""
@@ -108,7 +117,7 @@ def committed_traffic(workload_name):
 
 
 class Prefill:
-    def __init__(self, w, seed, long_memory=False, disc="exp_trapezoid", gated=False):
+    def __init__(self, w, seed, long_memory=False, disc="exp_trapezoid", gated=False, down=False):
         import torch
         import state_space_sequence_prefill_amd as m3
         from state_space_sequence_prefill_amd import synthetic as syn
@@ -116,12 +125,12 @@ class Prefill:
         self.d = m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype, disc)
         self.inp = syn.draw_torch(w, seed, long_memory=long_memory)
         self.state = m3.State.empty(self.d)
-        self.y = torch.empty((w.batch, w.seqlen, w.heads, w.rank, w.headdim), dtype=self.inp["x"].dtype,
-                             device="cuda")
+        yshape = (w.batch, w.seqlen, w.heads, w.headdim) if down else (w.batch, w.seqlen, w.heads, w.rank, w.headdim)
+        self.y = torch.empty(yshape, dtype=self.inp["x"].dtype, device="cuda")
         nws = m3.mamba3_prefill_workspace_bytes(self.d, w.seqlen)
         self.ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
         self.nlaunch = 1 if not nws else 3
-        self.gate = syn.draw_gate_torch(w, seed + 1) if gated else None
+        self.gate = syn.draw_gate_torch(w, seed + 1, folded=down) if gated or down else None
 
     def step(self, ev=None):
         i = self.inp
@@ -132,9 +141,11 @@ class Prefill:
             self.m3.mamba3_prefill(self.d, self.w.seqlen, i["x"], i["B"], i["C"], i["dt"], i["lam"], i["theta"],
                                    i["A"], i["D"], self.state, self.y, self.ws)
         else:
-            z, gw = self.gate
+            z, gw = self.gate[:2]
+            dw = self.gate[2] if len(self.gate) > 2 else None
             self.m3.mamba3_prefill_gated(self.d, self.w.seqlen, i["x"], i["B"], i["C"], i["dt"], i["lam"],
-                                         i["theta"], i["A"], i["D"], z, gw, 1e-5, self.state, self.y, self.ws)
+                                         i["theta"], i["A"], i["D"], z, gw, 1e-5, self.state, self.y, self.ws,
+                                         down=dw)
         if ev is not None:
             ev[1].record()
 
@@ -154,7 +165,7 @@ class Prefill:
         return wall / steps * 1e3, kern_ms
 
 
-def time_decode(w, seed, steps=1000, flush_steps=20, gated=False):
+def time_decode(w, seed, steps=1000, flush_steps=20, gated=False, down=False):
     import torch
     import state_space_sequence_prefill_amd as m3
     from state_space_sequence_prefill_amd import synthetic as syn
@@ -168,8 +179,14 @@ def time_decode(w, seed, steps=1000, flush_steps=20, gated=False):
     st.h.copy_(torch.randn(st.h.shape, generator=g, device="cuda"))
     st.B_prev.copy_(torch.randn(st.B_prev.shape, generator=g, device="cuda").to(st.B_prev.dtype))
     st.x_prev.copy_(torch.randn(st.x_prev.shape, generator=g, device="cuda").to(st.x_prev.dtype))
-    y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=toks["x"].dtype, device="cuda")
-    if gated:
+    y = torch.empty((w.batch, w.heads, w.headdim) if down else (w.batch, w.heads, w.rank, w.headdim),
+                    dtype=toks["x"].dtype, device="cuda")
+    dw = None
+    if down:
+        z, gw, dw = syn.draw_gate_torch(w, seed + 2, folded=True)
+        z = z[:, 0].contiguous()
+        gated = True
+    elif gated:
         z, gw = syn.draw_gate_torch(w, seed + 2)
         z = z[:, 0].contiguous()
 
@@ -177,7 +194,7 @@ def time_decode(w, seed, steps=1000, flush_steps=20, gated=False):
         s = sets[j % nset]
         if gated:
             m3.mamba3_decode_step_gated(d, s["x"], s["B"], s["C"], s["dt"], s["lam"], s["theta"], s["A"], s["D"],
-                                        z, gw, 1e-5, st, y)
+                                        z, gw, 1e-5, st, y, down=dw)
         else:
             m3.mamba3_decode_step(d, s["x"], s["B"], s["C"], s["dt"], s["lam"], s["theta"], s["A"], s["D"], st,
                                   y)
@@ -217,9 +234,9 @@ def time_decode(w, seed, steps=1000, flush_steps=20, gated=False):
         torch.cuda.synchronize()
         tot += a.elapsed_time(b)
     us_flush = tot * 1e3 / flush_steps
-    nb = decode_bytes(w) + (gate_bytes(w, 1) if gated else 0)
+    nb = decode_bytes(w) + (gate_bytes(w, 1) if gated else 0) + (down_bytes_delta(w, 1) if down else 0)
     return {
-        "workload": w.name + ("_gated" if gated else ""), "batch": w.batch, "heads": w.heads, "headdim": w.headdim, "dstate": w.dstate,
+        "workload": w.name + ("_down_gated" if down else "_gated" if gated else ""), "batch": w.batch, "heads": w.heads, "headdim": w.headdim, "dstate": w.dstate,
         "rank": w.rank, "us_per_step_graph": round(us_graph, 2), "steps_graph": reps * per_graph,
         "us_per_step_flushed": round(us_flush, 2), "bytes_per_step": nb,
         "hbm_GBs_graph": round(nb / us_graph / 1e3, 1), "hbm_frac_graph": round(nb / us_graph / 1e3 / HBM_PEAK_GBS, 4),
@@ -451,6 +468,23 @@ def main():
             log(f"bench: gated decode {name}")
             extra[f"{name}_gated"] = time_decode(syn.WORKLOADS[name], seed=7, flush_steps=5, gated=True)
             torch.cuda.empty_cache()
+        # MIMO with the rank down-projection folded into the store (y and z
+        # lose the rank axis), then the epilogue: prefill and decode
+        wm = syn.WORKLOADS["mimo_r4_t4096"]
+        log(f"bench: down-projected gated prefill {wm.name}")
+        p = Prefill(wm, seed=1005, down=True)
+        ms, kms = p.time(max(3, args.steps // 2), 2)
+        nbd = prefill_bytes(wm) + gate_bytes(wm, wm.seqlen) + down_bytes_delta(wm, wm.seqlen)
+        extra[f"{wm.name}_down_gated"] = {"ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                                          "Mtokens_per_s": round(wm.batch * wm.seqlen / ms / 1e3, 3),
+                                          "algorithmic_bytes": nbd,
+                                          "hbm_frac": round(nbd / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del p
+        torch.cuda.empty_cache()
+        log("bench: down-projected gated decode decode_mimo_r4_n64")
+        extra["decode_mimo_r4_n64_down_gated"] = time_decode(syn.WORKLOADS["decode_mimo_r4_n64"], seed=7,
+                                                             flush_steps=5, down=True)
+        torch.cuda.empty_cache()
         line["extra"] = extra
 
     if not args.no_cpu_baseline:

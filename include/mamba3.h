@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 2
+#define M3_ABI_VERSION 3
 
 typedef enum {
   M3_OK = 0,
@@ -180,17 +180,25 @@ int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const 
  * channels s[0..P) of the scan is one group:
  *   y[p] = weight[head][p] * s[p] / sqrt(mean_p s[p]^2 + eps) * silu(z[p]),
  *   silu(v) = v / (1 + exp(-v)).
+ * With down != NULL the R rank rows of a (token, head) are first folded into
+ * one row of P channels (lilting.ch Mamba-3 article, "3. MIMO SSM": the
+ * rank-r output returns to the channels), s[p] = sum_r down[head][r][p] *
+ * scan[r][p], and that row is the group; y and z then have no rank axis.
  *   z       io    same layout as y (the gate input)
  *   weight  fp32  (heads, P)
- *   eps     >= 0 */
+ *   eps     >= 0
+ *   down    fp32  (heads, R, P), or NULL: no down-projection
+ * All pointers are device pointers, 16-byte aligned, owned by the caller. */
 typedef struct {
   const void* z;
   const float* weight;
   float eps;
+  const float* down;
 } m3_gate;
 
 /* mamba3_prefill with the epilogue: y receives the gated, normalised output
- * (the raw scan output is not written).  Same arguments and errors as
+ * (the raw scan output is not written); with gate->down, y and gate->z are
+ * (batch, seqlen, heads, P).  Same arguments and errors as
  * mamba3_prefill, plus M3_ERR_NULL / M3_ERR_ALIGN for gate, gate->z,
  * gate->weight, M3_ERR_SHAPE for a negative or NaN eps, and
  * M3_ERR_UNSUPPORTED for shapes that only the single-role prefill kernel
@@ -200,7 +208,8 @@ int mamba3_prefill_gated(const m3_dims* dims, int32_t seqlen, const void* x, con
                          const float* A, const float* D, const m3_gate* gate, m3_state* state,
                          void* y, void* workspace, size_t workspace_bytes, void* stream);
 
-/* mamba3_decode_step with the epilogue (z of shape (batch, heads, R, P)). */
+/* mamba3_decode_step with the epilogue (z and y of shape (batch, heads, R, P),
+ * or (batch, heads, P) with gate->down). */
 int mamba3_decode_step_gated(const m3_dims* dims, const void* x, const void* B, const void* C,
                              const float* dt, const float* lam, const float* theta,
                              const float* A, const float* D, const m3_gate* gate, m3_state* state,

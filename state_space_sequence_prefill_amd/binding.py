@@ -56,7 +56,8 @@ class m3_state(ctypes.Structure):
 
 
 class m3_gate(ctypes.Structure):
-    _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+    _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("down", ctypes.c_void_p)]
 
 
 _lib = None
@@ -221,12 +222,16 @@ def mamba3_prefill_workspace_bytes(dims, seqlen):
     return n.value
 
 
-def _gate(dims, z, weight, eps, lead):
-    """m3_gate for gate input z of shape lead + (heads, R, P) and weight (heads, P)."""
+def _gate(dims, z, weight, eps, lead, down=None):
+    """m3_gate for gate input z of shape lead + (heads, R, P) (lead + (heads, P)
+    with the rank down-projection `down`, fp32 (heads, R, P)) and weight (heads, P)."""
     d = dims
-    pz = _ptr(z, "z", tuple(lead) + (d.heads, d.rank, d.headdim), _io_torch_dtype(d))
-    pw = _ptr(weight, "weight", (d.heads, d.headdim), _torch().float32)
-    return m3_gate(pz, pw, float(eps))
+    f32 = _torch().float32
+    tail = (d.heads, d.headdim) if down is not None else (d.heads, d.rank, d.headdim)
+    pz = _ptr(z, "z", tuple(lead) + tail, _io_torch_dtype(d))
+    pw = _ptr(weight, "weight", (d.heads, d.headdim), f32)
+    pd = _ptr(down, "down", (d.heads, d.rank, d.headdim), f32)
+    return m3_gate(pz, pw, float(eps), pd)
 
 
 def _workspace(workspace):
@@ -249,18 +254,20 @@ def mamba3_prefill(dims, seqlen, x, B, C, dt, lam, theta, A, D, state, y, worksp
 
 
 def mamba3_prefill_gated(dims, seqlen, x, B, C, dt, lam, theta, A, D, z, weight, eps, state, y,
-                         workspace=None, stream=None):
+                         workspace=None, stream=None, down=None):
     """mamba3_prefill whose y is the gated, normalised output: z is the gate
-    input (batch, seqlen, heads, R, P), weight fp32 (heads, P), eps >= 0."""
-    args, py = _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y)
-    g = _gate(dims, z, weight, eps, (dims.batch, int(seqlen)))
+    input (batch, seqlen, heads, R, P), weight fp32 (heads, P), eps >= 0.
+    With `down` (fp32 (heads, R, P)) the ranks are first folded into P
+    channels and y, z are (batch, seqlen, heads, P)."""
+    args, py = _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y, down is not None)
+    g = _gate(dims, z, weight, eps, (dims.batch, int(seqlen)), down)
     ws, wsb = _workspace(workspace)
     cs = state.c_struct()
     _check(lib().mamba3_prefill_gated(ctypes.byref(dims), int(seqlen), *args, ctypes.byref(g),
                                       ctypes.byref(cs), py, ws, wsb, _stream(stream)))
 
 
-def _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y):
+def _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y, no_rank=False):
     torch = _torch()
     d = dims
     io = _io_torch_dtype(d)
@@ -276,7 +283,7 @@ def _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y):
         _ptr(A, "A", (Hh,), f32),
         _ptr(D, "D", (Hh,), f32),
     ]
-    py = _ptr(y, "y", (d.batch, T, Hh, R, P), io)
+    py = _ptr(y, "y", (d.batch, T, Hh, P) if no_rank else (d.batch, T, Hh, R, P), io)
     return args, py
 
 
@@ -287,17 +294,19 @@ def mamba3_decode_step(dims, x, B, C, dt, lam, theta, A, D, state, y, stream=Non
     _check(lib().mamba3_decode_step(ctypes.byref(dims), *args, ctypes.byref(cs), py, _stream(stream)))
 
 
-def mamba3_decode_step_gated(dims, x, B, C, dt, lam, theta, A, D, z, weight, eps, state, y, stream=None):
+def mamba3_decode_step_gated(dims, x, B, C, dt, lam, theta, A, D, z, weight, eps, state, y, stream=None,
+                             down=None):
     """mamba3_decode_step whose y is the gated, normalised output (z of shape
-    (batch, heads, R, P), weight fp32 (heads, P), eps >= 0)."""
-    args, py = _decode_args(dims, x, B, C, dt, lam, theta, A, D, y)
-    g = _gate(dims, z, weight, eps, (dims.batch,))
+    (batch, heads, R, P), weight fp32 (heads, P), eps >= 0; with `down`, fp32
+    (heads, R, P), z and y are (batch, heads, P))."""
+    args, py = _decode_args(dims, x, B, C, dt, lam, theta, A, D, y, down is not None)
+    g = _gate(dims, z, weight, eps, (dims.batch,), down)
     cs = state.c_struct()
     _check(lib().mamba3_decode_step_gated(ctypes.byref(dims), *args, ctypes.byref(g), ctypes.byref(cs), py,
                                           _stream(stream)))
 
 
-def _decode_args(dims, x, B, C, dt, lam, theta, A, D, y):
+def _decode_args(dims, x, B, C, dt, lam, theta, A, D, y, no_rank=False):
     torch = _torch()
     d = dims
     io = _io_torch_dtype(d)
@@ -313,5 +322,5 @@ def _decode_args(dims, x, B, C, dt, lam, theta, A, D, y):
         _ptr(A, "A", (Hh,), f32),
         _ptr(D, "D", (Hh,), f32),
     ]
-    py = _ptr(y, "y", (d.batch, Hh, R, P), io)
+    py = _ptr(y, "y", (d.batch, Hh, P) if no_rank else (d.batch, Hh, R, P), io)
     return args, py

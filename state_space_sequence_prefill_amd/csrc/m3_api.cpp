@@ -222,18 +222,21 @@ int mamba3_prefill_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* 
 namespace {
 
 // Gate argument checks; *gz stays nullptr without a gate.
-int check_gate(const m3_gate* gate, const void** gz, const float** gw, float* geps) {
+int check_gate(const m3_gate* gate, const void** gz, const float** gw, float* geps, const float** gdown) {
   *gz = nullptr;
   *gw = nullptr;
   *geps = 0.f;
+  *gdown = nullptr;
   if (!gate) return fail(M3_ERR_NULL, "gate is NULL");
   int st;
   if ((st = check_ptr(gate->z, "gate.z")) != M3_OK) return st;
   if ((st = check_ptr(gate->weight, "gate.weight")) != M3_OK) return st;
   if (!(gate->eps >= 0.f)) return fail(M3_ERR_SHAPE, "gate.eps must be >= 0 (got %g)", (double)gate->eps);
+  if (gate->down && !aligned16(gate->down)) return fail(M3_ERR_ALIGN, "gate.down is not 16-byte aligned");
   *gz = gate->z;
   *gw = gate->weight;
   *geps = gate->eps;
+  *gdown = gate->down;
   return M3_OK;
 }
 
@@ -248,9 +251,10 @@ int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void*
   if ((st = check_state(state, "state")) != M3_OK) return st;
   const void* gz = nullptr;
   const float* gw = nullptr;
+  const float* gdown = nullptr;
   float geps = 0.f;
   if (gated) {
-    if ((st = check_gate(gate, &gz, &gw, &geps)) != M3_OK) return st;
+    if ((st = check_gate(gate, &gz, &gw, &geps, &gdown)) != M3_OK) return st;
     if (!m3::prefill_gated_supported(m))
       return fail(M3_ERR_UNSUPPORTED, "the gated epilogue needs the producer/consumer prefill kernel, whose "
                                       "tiles do not fit for these sizes");
@@ -290,6 +294,7 @@ int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void*
   a.gz = gz;
   a.gw = gw;
   a.geps = geps;
+  a.gdown = gdown;
   a.seqlen = seqlen;
   a.nseg = nseg;
   a.seg_chunks = sc;
@@ -317,8 +322,9 @@ int decode_impl(const m3_dims* dims, const void* x, const void* B, const void* C
   if ((st = check_state(state, "state")) != M3_OK) return st;
   const void* gz = nullptr;
   const float* gw = nullptr;
+  const float* gdown = nullptr;
   float geps = 0.f;
-  if (gated && (st = check_gate(gate, &gz, &gw, &geps)) != M3_OK) return st;
+  if (gated && (st = check_gate(gate, &gz, &gw, &geps, &gdown)) != M3_OK) return st;
   const void* ptrs[] = {x, B, C, dt, lam, theta, A, D, y};
   const char* names[] = {"x", "B", "C", "dt", "lam", "theta", "A", "D", "y"};
   for (int i = 0; i < 9; ++i)
@@ -340,6 +346,7 @@ int decode_impl(const m3_dims* dims, const void* x, const void* B, const void* C
   a.gz = gz;
   a.gw = gw;
   a.geps = geps;
+  a.gdown = gdown;
   return hip_status(m3::launch_decode(m, a, static_cast<hipStream_t>(stream)), what);
 }
 

@@ -214,8 +214,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
   const bool gated = a.gz != nullptr;
   DecodeGate<IO, R> gate;
   if (gated)
-    gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * R * P, a.gw + (size_t)hh * P, P, wave,
-                  nthr / kWave, lane);
+    gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * (a.gdown ? 1 : R) * P, a.gw + (size_t)hh * P,
+                  a.gdown != nullptr, P, wave, nthr / kWave, lane);
   // KG granules per thread (the launch picks KG with KG * threads >= total);
   // every load is unconditional (clamped duplicates are not stored)
   uint4 gv[KG];
@@ -337,7 +337,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
   // ---- 6. output epilogue (pre-gate grouped RMSNorm) over the LDS outputs
   if (gated) {
     __syncthreads();
-    gate.apply(sYg, static_cast<IO*>(a.y) + (size_t)head * R * P, a.geps, P, wave, nthr / kWave, lane);
+    gate.apply(sYg, static_cast<IO*>(a.y) + (size_t)head * (a.gdown ? 1 : R) * P,
+               a.gdown ? a.gdown + (size_t)hh * R * P : nullptr, a.geps, P, wave, nthr / kWave, lane);
   }
 }
 

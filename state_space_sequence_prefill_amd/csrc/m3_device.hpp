@@ -174,36 +174,59 @@ __device__ __forceinline__ float gate_out(float s, float inv_rms, float w, float
 // Output epilogue of a decode step for one head: R rows of P fp32 scan
 // outputs sy[r * P + p] (in LDS) -> y, each row normalised by its RMS, scaled
 // by the head's weights and gated.  Wave w of nw handles rows w, w + nw, ...;
-// lane l channels l and l + 64 (P <= 128).  The gate and weight values are
-// fetched ahead, before the step's own loads.
+// lane l channels l and l + 64 (P <= 128).  With the rank down-projection
+// (weights dg (R, P) of this head) the R rows are first folded into one row of
+// P channels, which wave 0 normalises and gates.  The gate and weight values
+// are fetched ahead, before the step's own loads (every array element is
+// assigned unconditionally, with selects around masked loads, so the arrays
+// stay in registers); the few projection weights are read at the end.
 template <typename IO, int R>
 struct DecodeGate {
   float z[R][2];
   float w[2];
-  __device__ __forceinline__ void prefetch(const IO* zg, const float* wg, int P, int wave, int nw, int lane) {
+  __device__ __forceinline__ void prefetch(const IO* zg, const float* wg, bool down, int P, int wave, int nw,
+                                           int lane) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) w[k] = lane + 64 * k < P ? wg[lane + 64 * k] : 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int r = wave + i * nw, p = lane + 64 * k;
-        z[i][k] = (r < R && p < P) ? to_f32(zg[r * P + p]) : 0.f;
+        const int p = lane + 64 * k;
+        const int r = down ? 0 : wave + i * nw;
+        const bool ok = p < P && (down ? (i == 0 && wave == 0) : r < R);
+        z[i][k] = ok ? to_f32(zg[r * P + p]) : 0.f;
       }
     }
   }
-  __device__ __forceinline__ void apply(const float* sy, IO* y, float eps, int P, int wave, int nw,
+  __device__ __forceinline__ void row(float v0, float v1, IO* yr, float eps, int P, int lane, float z0,
+                                      float z1) const {
+    const float ss = lane_group_sum(v0 * v0 + v1 * v1, kWave);
+    const float inv = rsqrtf(ss / (float)P + eps);
+    if (lane < P) yr[lane] = from_f32<IO>(gate_out(v0, inv, w[0], z0));
+    if (lane + 64 < P) yr[lane + 64] = from_f32<IO>(gate_out(v1, inv, w[1], z1));
+  }
+  __device__ __forceinline__ void apply(const float* sy, IO* y, const float* dg, float eps, int P, int wave, int nw,
                                         int lane) const {
+    if (dg) {
+      if (wave == 0) {
+        float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          v0 += lane < P ? dg[r * P + lane] * sy[r * P + lane] : 0.f;
+          v1 += lane + 64 < P ? dg[r * P + lane + 64] * sy[r * P + lane + 64] : 0.f;
+        }
+        row(v0, v1, y, eps, P, lane, z[0][0], z[0][1]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int r = wave + i * nw;
       if (r < R) {  // uniform over the wave
         const float v0 = lane < P ? sy[r * P + lane] : 0.f;
         const float v1 = lane + 64 < P ? sy[r * P + lane + 64] : 0.f;
-        const float ss = lane_group_sum(v0 * v0 + v1 * v1, kWave);
-        const float inv = rsqrtf(ss / (float)P + eps);
-        if (lane < P) y[r * P + lane] = from_f32<IO>(gate_out(v0, inv, w[0], z[i][0]));
-        if (lane + 64 < P) y[r * P + lane + 64] = from_f32<IO>(gate_out(v1, inv, w[1], z[i][1]));
+        row(v0, v1, y + r * P, eps, P, lane, z[i][0], z[i][1]);
       }
     }
   }

@@ -32,6 +32,7 @@ struct DecodeArgs {
   const void* gz;  // output epilogue, as in PrefillArgs
   const float* gw;
   float geps;
+  const float* gdown;
 };
 
 // Arguments of one prefill pass over tokens [0, seqlen) of every chain.
@@ -49,10 +50,13 @@ struct PrefillArgs {
   void* x_prev;   // pending x (batch, heads, R, P), in/out
   void* y;
   int disc;  // m3_disc
-  // output epilogue (pre-gate grouped RMSNorm); gz == nullptr: plain y
+  // output epilogue (pre-gate grouped RMSNorm); gz == nullptr: plain y.
+  // gdown != nullptr (with gz): MIMO rank down-projection (heads, R, P) first;
+  // y and z are then (batch, T, heads, P)
   const void* gz;
   const float* gw;
   float geps;
+  const float* gdown;
   int seqlen;
   // Segment path (long prompts, few chains).  nseg == 1: plain fused pass.
   int nseg;        // number of segments the sequence is split into
@@ -81,7 +85,9 @@ bool prefill_gated_supported(const Dims& d);
 // Chunk length the prefill kernels tile with (<= d.Q; see m3_prefill.hip).
 int prefill_tile_chunk(const Dims& d);
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
-// The same with y stored through the output epilogue (m3_prefill_pc_gated.hip).
+// The same with y stored through the output epilogue (m3_prefill_pc_gated.hip),
+// and through the rank down-projection and the epilogue (m3_prefill_pc_down.hip).
 hipError_t launch_prefill_pc_gated(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
+hipError_t launch_prefill_pc_down(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
 
 }  // namespace m3

@@ -12,8 +12,9 @@ bool prefill_pc_supported(const Dims& d) {
 
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks) {
   // segment summaries write no y, so they never need the epilogue
-  if (a.gz && mode != kPcSummary) return launch_prefill_pc_gated(d, a, s, mode, nblocks);
-  return launch_pc<false>(d, a, s, mode, nblocks);
+  if (a.gz && mode != kPcSummary)
+    return a.gdown ? launch_prefill_pc_down(d, a, s, mode, nblocks) : launch_prefill_pc_gated(d, a, s, mode, nblocks);
+  return launch_pc<kEpiPlain>(d, a, s, mode, nblocks);
 }
 
 }  // namespace m3

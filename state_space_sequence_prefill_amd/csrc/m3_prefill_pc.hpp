@@ -11,8 +11,9 @@
 // first token's decay and previous-input term applied), S^T = Bt Ct^T, and M
 // the trapezoid decay mask.
 //
-// Included by m3_prefill_pc.hip (plain y store) and m3_prefill_pc_gated.hip
-// (y store through the output epilogue), one set of instances each.
+// Included by m3_prefill_pc.hip (plain y store), m3_prefill_pc_gated.hip (y
+// through the output epilogue) and m3_prefill_pc_down.hip (the MIMO rank
+// down-projection, then the epilogue), one set of instances each.
 //
 // One workgroup of 8 waves per chain (or chain segment):
 //   waves 0-3 produce: stream dt, lam, theta, B, C, x for chunk i+1 / i+2 from
@@ -117,8 +118,14 @@ struct PcRaw {
   float4 th[MI][4];
 };
 
-// GATE: y leaves through the output epilogue (a.gz, a.gw, a.geps set).
-template <typename IO, int N, int P, bool GATE>
+// How y leaves the kernel.
+enum PcEpi : int {
+  kEpiPlain = 0,  // the scan output (batch, T, H, R, P)
+  kEpiGate = 1,   // pre-gate grouped RMSNorm per (token, head, rank) row (a.gz, a.gw, a.geps)
+  kEpiDown = 2,   // rank down-projection (a.gdown) to (batch, T, H, P), then the same epilogue per (token, head)
+};
+
+template <typename IO, int N, int P, int EPI>
 __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) {
   using L = PcLds<IO, N, P>;
   using Lim = PcLimits<IO, N, P>;
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // waits for every outstanding memory operation (the gate loads of the
     // next chunk among them) at each first use of Hreg.  Measured: 2% faster
     // with the epilogue, and 1% slower without it, where no load is in flight.
-    if constexpr (GATE) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if constexpr (EPI != kEpiPlain) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     // y of chunk jy leaves the LDS output tile as whole 16-byte runs of its
     // rows (each (token, rank) row is P contiguous elements in HBM)
@@ -600,20 +607,43 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // so its EG weights are loaded once; the G16 granules of one row sit in
     // G16 aligned consecutive lanes, which sum the squares among themselves.
     // The gate of chunk j is loaded one iteration ahead of its use.
-    const bool gated = GATE && has_y;
-    const IO* Zg = gated ? static_cast<const IO*>(a.gz) + ((size_t)b * T * H + hh) * R * P : nullptr;
+    // With the down-projection the output rows are tokens: row t sums the R
+    // output-tile rows t*R + r, which phase 2 already scaled by the weights.
+    constexpr bool kDown = EPI == kEpiDown;
+    const bool gated = EPI != kEpiPlain && has_y;
+    const int RO = kDown ? 1 : R;                    // output rows per token
+    const size_t tokO = (size_t)H * RO * P;          // output row stride per token
+    const IO* Zg = gated ? static_cast<const IO*>(a.gz) + ((size_t)b * T * H + hh) * RO * P : nullptr;
+    IO* const Og = static_cast<IO*>(a.y) + ((size_t)b * T * H + hh) * RO * P;
+    auto out_off = [&](int c0, int e) -> size_t {
+      const int row = e / G16, gq = e % G16;
+      if constexpr (kDown) return (size_t)(c0 + row) * tokO + gq * EG;
+      return (size_t)(c0 + (row >> lgR)) * tokO + (row & (R - 1)) * P + gq * EG;
+    };
     float gwr[EG];
     uint4 zr[KZ];
     if (gated) {
 #pragma unroll
       for (int q = 0; q < EG; ++q) gwr[q] = a.gw[(size_t)hh * P + (ct % G16) * EG + q];
     }
+    // down-projection weights of this lane's output-tile entries in phase 2:
+    // rows rho = 16 rb + c all have rank c % R, columns 16 pb + 4 g .. + 3
+    float dwr[kDown ? PBW : 1][4];
+    if constexpr (kDown) {
+#pragma unroll
+      for (int u = 0; u < PBW; ++u) {
+        const int pb = cw + kConsWaves * u;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          dwr[u][i4] = pb < PB ? a.gdown[((size_t)hh * R + (c & (R - 1))) * P + 16 * pb + 4 * g + i4] : 0.f;
+      }
+    }
     auto load_z = [&](int jz) {
-      const int ng = chunk_len(jz) * R * G16;
+      const int ng = chunk_len(jz) * RO * G16;
 #pragma unroll
       for (int k = 0; k < KZ; ++k) {
         const int e = ct + k * kCT;  // clamped duplicate past the tail, never used
-        zr[k] = *reinterpret_cast<const uint4*>(Zg + gran_off(jz * Q, e < ng ? e : ng - 1));
+        zr[k] = *reinterpret_cast<const uint4*>(Zg + out_off(jz * Q, e < ng ? e : ng - 1));
       }
     };
     auto store_y = [&](int jy) {
@@ -625,14 +655,27 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     };
     uint4 gres[KZ];
     auto gate_y = [&](int jy) {
-      const int ng = chunk_len(jy) * R * G16;
+      const int ng = chunk_len(jy) * RO * G16;
 #pragma unroll
       for (int k = 0; k < KZ; ++k) {
         const int e = ct + k * kCT;
         if (e < ng) {  // whole rows: all G16 lanes of a row agree
           const int row = e / G16, gq = e % G16;
           float v[EG], z[EG];
-          Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG), v);
+          if constexpr (kDown) {
+            Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + row * R * ldy + gq * EG), v);
+#pragma unroll
+            for (int r = 1; r < 4; ++r) {
+              if (r < R) {
+                float w[EG];
+                Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + (row * R + r) * ldy + gq * EG), w);
+#pragma unroll
+                for (int q = 0; q < EG; ++q) v[q] += w[q];
+              }
+            }
+          } else {
+            Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG), v);
+          }
           float ss = 0.f;
 #pragma unroll
           for (int q = 0; q < EG; ++q) ss += v[q] * v[q];
@@ -646,11 +689,11 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
     };
     auto store_gated = [&](int jy) {
-      const int c0 = jy * Q, ng = chunk_len(jy) * R * G16;
+      const int c0 = jy * Q, ng = chunk_len(jy) * RO * G16;
 #pragma unroll
       for (int k = 0; k < KZ; ++k) {
         const int e = ct + k * kCT;
-        if (e < ng) *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = gres[k];
+        if (e < ng) *reinterpret_cast<uint4*>(Og + out_off(c0, e)) = gres[k];
       }
     };
     for (int i = ck0; i <= ck1; ++i) {
@@ -789,7 +832,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
                 }
               }
               // y (row rho, columns 16pb + 4g .. +3) into the output tile
-              const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+              // (down-projection: scaled by the weights of rank rho % R)
+              float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+              if constexpr (kDown) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) v[i4] *= dwr[u][i4];
+              }
               store4(sY + rho * ldy + 16 * pb + 4 * g, v);
             }
           }
@@ -861,12 +909,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   }
 }
 
-template <typename IO, int N, int P, bool GATE>
+template <typename IO, int N, int P, int EPI>
 hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int mode, int nblocks) {
   const size_t lds = PcLds<IO, N, P>::bytes(PcLimits<IO, N, P>::kMaxRows);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, GATE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -880,33 +928,33 @@ hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int 
   kp.Q = d.Q;
   kp.mode = mode;
   kp.nblocks = nblocks;
-  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, GATE>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
+  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
   return hipGetLastError();
 }
 
-template <typename IO, int N, bool GATE>
+template <typename IO, int N, int EPI>
 hipError_t pc_p(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nb) {
   switch (d.P) {
-    case 16: return launch_pc_t<IO, N, 16, GATE>(d, a, s, mode, nb);
-    case 32: return launch_pc_t<IO, N, 32, GATE>(d, a, s, mode, nb);
-    case 64: return launch_pc_t<IO, N, 64, GATE>(d, a, s, mode, nb);
-    default: return launch_pc_t<IO, N, 128, GATE>(d, a, s, mode, nb);
+    case 16: return launch_pc_t<IO, N, 16, EPI>(d, a, s, mode, nb);
+    case 32: return launch_pc_t<IO, N, 32, EPI>(d, a, s, mode, nb);
+    case 64: return launch_pc_t<IO, N, 64, EPI>(d, a, s, mode, nb);
+    default: return launch_pc_t<IO, N, 128, EPI>(d, a, s, mode, nb);
   }
 }
 
-template <typename IO, bool GATE>
+template <typename IO, int EPI>
 hipError_t pc_n(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nb) {
   switch (d.N) {
-    case 16: return pc_p<IO, 16, GATE>(d, a, s, mode, nb);
-    case 32: return pc_p<IO, 32, GATE>(d, a, s, mode, nb);
-    case 64: return pc_p<IO, 64, GATE>(d, a, s, mode, nb);
-    default: return pc_p<IO, 128, GATE>(d, a, s, mode, nb);
+    case 16: return pc_p<IO, 16, EPI>(d, a, s, mode, nb);
+    case 32: return pc_p<IO, 32, EPI>(d, a, s, mode, nb);
+    case 64: return pc_p<IO, 64, EPI>(d, a, s, mode, nb);
+    default: return pc_p<IO, 128, EPI>(d, a, s, mode, nb);
   }
 }
 
-template <bool GATE>
+template <int EPI>
 hipError_t launch_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks) {
-  return d.bf16 ? pc_n<bf16, GATE>(d, a, s, mode, nblocks) : pc_n<float, GATE>(d, a, s, mode, nblocks);
+  return d.bf16 ? pc_n<bf16, EPI>(d, a, s, mode, nblocks) : pc_n<float, EPI>(d, a, s, mode, nblocks);
 }
 
 template <typename IO>

@@ -13,7 +13,10 @@ Workload shapes and distributions (per token-head unless noted):
     D        ~ N(0, 1)                  per head
 Draw order with numpy's PCG64 generator: x, B, C, dt_raw, lam_raw, theta_raw,
 A_raw, D.  The output gate (``draw_gate``, its own seed) draws z ~ N(0, 1)
-(same layout as x) and then the per-head channel weights ~ U(0.5, 1.5).  Values are drawn in float64 and then cast to the I/O dtype by
+(same layout as x, or without the rank axis when the ranks are folded) and
+then the per-head channel weights ~ U(0.5, 1.5); the rank down-projection
+(``draw_down``, its own seed) draws weights ~ U(-1, 1) per (head, rank,
+channel).  Values are drawn in float64 and then cast to the I/O dtype by
 round-to-nearest-even; the exact cast values are what every consumer sees.
 
 The named workloads mirror the pages' 1.5B-scale Mamba-3 layers (32 heads of
@@ -84,20 +87,29 @@ def draw(w: Workload, seed: int, long_memory: bool = False, seqlen=None):
     return {"x": x, "B": Bm, "C": Cm, "dt": dt, "lam": lam, "theta": theta, "A": A, "D": D}
 
 
-def draw_gate(w: Workload, seed: int, seqlen=None, decode: bool = False):
-    """Gate input z (b,T,H,R,P), or (b,H,R,P) for a decode step, and the
+def draw_gate(w: Workload, seed: int, seqlen=None, decode: bool = False, folded: bool = False):
+    """Gate input z (b,T,H,R,P), or (b,H,R,P) for a decode step (no R axis
+    when ``folded``: the ranks are folded by the down-projection), and the
     per-head channel weights (H,P) of the output epilogue, fp64."""
     T = w.seqlen if seqlen is None else seqlen
     b, H, R, P = w.batch, w.heads, w.rank, w.headdim
     rng = np.random.default_rng(seed)
-    z = rng.standard_normal((b, H, R, P) if decode else (b, T, H, R, P))
+    lead = (b,) if decode else (b, T)
+    z = rng.standard_normal(lead + ((H, P) if folded else (H, R, P)))
     weight = rng.uniform(0.5, 1.5, (H, P))
     return z, weight
 
 
-def draw_gate_torch(w: Workload, seed: int, device="cuda", seqlen=None):
+def draw_down(w: Workload, seed: int):
+    """Rank down-projection weights (H,R,P), fp64."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(-1.0, 1.0, (w.heads, w.rank, w.headdim))
+
+
+def draw_gate_torch(w: Workload, seed: int, device="cuda", seqlen=None, folded: bool = False):
     """``draw_gate``'s distributions on the device (z in the I/O dtype,
-    weights fp32), for timing runs."""
+    weights fp32), for timing runs; with ``folded`` also the down-projection
+    weights (returned third)."""
     import torch
 
     T = w.seqlen if seqlen is None else seqlen
@@ -105,9 +117,13 @@ def draw_gate_torch(w: Workload, seed: int, device="cuda", seqlen=None):
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
-    z = torch.randn((b, T, H, R, P), generator=g, device=device, dtype=torch.float32).to(io)
+    shape = (b, T, H, P) if folded else (b, T, H, R, P)
+    z = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(io)
     weight = torch.rand((H, P), generator=g, device=device, dtype=torch.float32) + 0.5
-    return z, weight
+    if not folded:
+        return z, weight
+    down = torch.rand((H, R, P), generator=g, device=device, dtype=torch.float32) * 2.0 - 1.0
+    return z, weight, down
 
 
 def draw_state(w: Workload, seed: int, scale: float = 1.0):

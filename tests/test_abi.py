@@ -37,8 +37,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    # version 2 added m3_dims.disc (the discretisation rule)
-    assert B.m3_abi_version() == 2
+    # version 2 added m3_dims.disc (the discretisation rule); version 3 the
+    # gated entry points and m3_gate
+    assert B.m3_abi_version() == 3
 
 
 def test_dims_struct_matches_header():
@@ -203,7 +204,7 @@ def test_gate_struct_matches_header():
     body = re.search(r"typedef struct \{([^}]*)\} m3_gate;", hdr).group(1)
     names = re.findall(r"(\w+)\s*;", body)
     assert names == [f for f, _ in B.m3_gate._fields_]
-    assert ctypes.sizeof(B.m3_gate) == 24
+    assert ctypes.sizeof(B.m3_gate) == 32
 
 
 def call_prefill_gated(d, gate, seqlen=16, ptrs=None):
@@ -230,6 +231,8 @@ def test_gate_argument_checks(call):
     assert call(d, B.m3_gate(FAKE, FAKE, -1e-5)) == B.M3_ERR_SHAPE
     assert call(d, B.m3_gate(FAKE, FAKE, float("nan"))) == B.M3_ERR_SHAPE
     assert "eps" in B.m3_last_error()
+    assert call(d, B.m3_gate(FAKE, FAKE, 1e-5, FAKE + 4)) == B.M3_ERR_ALIGN
+    assert "down" in B.m3_last_error()
     # the other arguments are still checked
     p = [FAKE] * 9
     p[8] = None

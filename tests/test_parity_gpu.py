@@ -314,23 +314,30 @@ def test_prefill_full_size_sampled(name):
 # into the store of y, against oracle.gated_rmsnorm of the oracle's y
 # ---------------------------------------------------------------------------
 
-def gate_on_gpu(w, seed, decode=False, seqlen=None):
-    z, gw = syn.draw_gate(w, seed, seqlen=seqlen, decode=decode)
+def gate_on_gpu(w, seed, decode=False, seqlen=None, folded=False):
+    z, gw = syn.draw_gate(w, seed, seqlen=seqlen, decode=decode, folded=folded)
     z_ex, gw_ex = syn.round_io(z, w.io_dtype), syn.round_io(gw, "f32")
     return z_ex, gw_ex, to_gpu(z_ex, w.io_dtype, "x"), to_gpu(gw_ex, "f32", "weight")
 
 
-def check_prefill_gated(w, seed, eps=1e-5, pairs=None, disc=0, st=None):
+def down_on_gpu(w, seed):
+    dw_ex = syn.round_io(syn.draw_down(w, seed), "f32")
+    return dw_ex, to_gpu(dw_ex, "f32", "down")
+
+
+def check_prefill_gated(w, seed, eps=1e-5, pairs=None, disc=0, st=None, down=False):
     ex, tt = inputs_on_gpu(w, seed)
-    z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 7000)
+    z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 7000, folded=down)
+    dw_ex, dwt = down_on_gpu(w, seed + 7100) if down else (None, None)
     s = make_state(w, st)
     d = dims_of(w, disc)
     T = w.seqlen
-    y = torch.empty((w.batch, T, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
+    yshape = (w.batch, T, w.heads, w.headdim) if down else (w.batch, T, w.heads, w.rank, w.headdim)
+    y = torch.empty(yshape, dtype=tt["x"].dtype, device="cuda")
     nws = m3.mamba3_prefill_workspace_bytes(d, T)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
     m3.mamba3_prefill_gated(d, T, tt["x"], tt["B"], tt["C"], tt["dt"], tt["lam"], tt["theta"], tt["A"], tt["D"],
-                            zt, gwt, eps, s, y, ws)
+                            zt, gwt, eps, s, y, ws, down=dwt)
     torch.cuda.synchronize()
     if pairs is None:
         pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
@@ -340,12 +347,18 @@ def check_prefill_gated(w, seed, eps=1e-5, pairs=None, disc=0, st=None):
         w.batch, w.heads, w.headdim, w.dstate, w.rank)
     y_ref, (h_ref, bp_ref, xp_ref) = oracle.prefill(**oracle_args(ex, pairs), state=state_slice(st_ex, pairs),
                                                    disc=disc)
-    g_ref = oracle.gated_rmsnorm(y_ref, np.moveaxis(z_ex[bs, :, hs], 0, 1)[None], gw_ex[hs], eps)
+    zs = np.moveaxis(z_ex[bs, :, hs], 0, 1)[None]
+    if down:
+        folded = oracle.rank_down_projection(y_ref, dw_ex[hs])[..., None, :]
+        g_ref = oracle.gated_rmsnorm(folded, zs[..., None, :], gw_ex[hs], eps)[..., 0, :]
+    else:
+        g_ref = oracle.gated_rmsnorm(y_ref, zs, gw_ex[hs], eps)
     g_gpu = np.moveaxis(to_np(y)[bs, :, hs], 0, 1)[None]
     tol = tol_for(w.io_dtype)
     eg = relerr(g_gpu, g_ref)
     eh = relerr(to_np(s.h)[bs, hs][None], h_ref)
-    print(f"[gated {w.name} seed={seed} T={T} Q={w.chunk} eps={eps}] rel-L2 out={eg:.3e} h={eh:.3e}", flush=True)
+    print(f"[gated{' down' if down else ''} {w.name} seed={seed} T={T} Q={w.chunk} eps={eps}] rel-L2 out={eg:.3e} "
+          f"h={eh:.3e}", flush=True)
     assert eg <= tol, eg
     assert eh <= tol, eh
     assert np.array_equal(to_np(s.B_prev)[bs, hs][None], bp_ref)
@@ -393,7 +406,7 @@ def test_prefill_gated_full_size_sampled():
     check_prefill_gated(w, seed=960, pairs=chains)
 
 
-def check_decode_gated(w, seed, eps=1e-5, steps=2, pairs=None):
+def check_decode_gated(w, seed, eps=1e-5, steps=2, pairs=None, down=False):
     d = dims_of(w)
     st0 = syn.draw_state(w, seed + 500)
     s = make_state(w, st0)
@@ -404,20 +417,26 @@ def check_decode_gated(w, seed, eps=1e-5, steps=2, pairs=None):
     cur = state_slice(exact_state(st0, w.io_dtype), pairs)
     ex, tt = inputs_on_gpu(w, seed, seqlen=steps)
     tol = tol_for(w.io_dtype)
+    dw_ex, dwt = down_on_gpu(w, seed + 3) if down else (None, None)
     for k in range(steps):
-        z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 100 * k + 7, decode=True)
+        z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 100 * k + 7, decode=True, folded=down)
         tok = {key: (v[:, k].contiguous() if v.dim() >= 3 else v) for key, v in tt.items()}
-        y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
+        yshape = (w.batch, w.heads, w.headdim) if down else (w.batch, w.heads, w.rank, w.headdim)
+        y = torch.empty(yshape, dtype=tt["x"].dtype, device="cuda")
         m3.mamba3_decode_step_gated(d, tok["x"], tok["B"], tok["C"], tok["dt"], tok["lam"], tok["theta"],
-                                    tok["A"], tok["D"], zt, gwt, eps, s, y)
+                                    tok["A"], tok["D"], zt, gwt, eps, s, y, down=dwt)
         torch.cuda.synchronize()
         args = oracle_args(ex, pairs)
         y_ref, cur = oracle.decode_step(args["x"][:, k], args["Bm"][:, k], args["Cm"][:, k], args["dt"][:, k],
                                         args["lam"][:, k], args["theta"][:, k], args["A"], args["D"], cur)
-        g_ref = oracle.gated_rmsnorm(y_ref, z_ex[bs, hs][None], gw_ex[hs], eps)
+        if down:
+            folded = oracle.rank_down_projection(y_ref, dw_ex[hs])[..., None, :]
+            g_ref = oracle.gated_rmsnorm(folded, z_ex[bs, hs][None][..., None, :], gw_ex[hs], eps)[..., 0, :]
+        else:
+            g_ref = oracle.gated_rmsnorm(y_ref, z_ex[bs, hs][None], gw_ex[hs], eps)
         eg = relerr(to_np(y)[bs, hs][None], g_ref)
         eh = relerr(to_np(s.h)[bs, hs][None], cur[0])
-        print(f"[gated decode {w.name} step {k}] rel-L2 out={eg:.3e} h={eh:.3e}", flush=True)
+        print(f"[gated{' down' if down else ''} decode {w.name} step {k}] rel-L2 out={eg:.3e} h={eh:.3e}", flush=True)
         assert eg <= tol and eh <= tol, (eg, eh)
         assert np.array_equal(to_np(s.B_prev)[bs, hs][None], cur[1])
         assert np.array_equal(to_np(s.x_prev)[bs, hs][None], cur[2])
@@ -437,3 +456,50 @@ def test_decode_gated_full_size_sampled(name):
     rng = np.random.default_rng(11)
     pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(16)]
     check_decode_gated(w, seed=990, eps=1e-3, pairs=pairs)
+
+
+# ---------------------------------------------------------------------------
+# MIMO rank down-projection folded into the output store (then the epilogue),
+# against oracle.rank_down_projection + oracle.gated_rmsnorm of the oracle's y
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("io,P,N,R,T,Q", [
+    ("bf16", 64, 64, 4, 130, 64),   # MIMO rank 4: 16-token tiles, ragged tail
+    ("bf16", 64, 128, 2, 100, 32),
+    ("f32", 32, 32, 2, 70, 32),
+    ("f32", 16, 16, 4, 40, 16),     # 4 fp32 granules per row
+    ("bf16", 128, 32, 4, 48, 16),   # 16 granules per row
+    ("bf16", 64, 128, 1, 90, 64),   # rank 1: a per-channel scale
+])
+def test_prefill_down_shapes(io, P, N, R, T, Q):
+    w = W("tiny_siso_f32", batch=2, heads=3, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=T, chunk=Q)
+    check_prefill_gated(w, seed=1200 + P + N + R + T, down=True)
+
+
+def test_prefill_down_segment_path():
+    w = W("tiny_siso_f32", batch=1, heads=2, headdim=64, dstate=64, rank=4, io_dtype="bf16", seqlen=16 * 80,
+          chunk=64)
+    assert m3.mamba3_prefill_workspace_bytes(dims_of(w), w.seqlen) > 0
+    check_prefill_gated(w, seed=1250, down=True, st=syn.draw_state(w, 1251))
+
+
+def test_prefill_down_full_size_sampled():
+    w = syn.WORKLOADS["mimo_r4_t4096"]
+    rng = np.random.default_rng(8)
+    chains = sorted({(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(3)})
+    check_prefill_gated(w, seed=1260, pairs=chains, down=True)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("P,N,R", [(64, 64, 4), (128, 64, 4), (32, 32, 2), (16, 16, 4), (64, 128, 1),
+                                   (128, 128, 2)])
+def test_decode_down(io, P, N, R):
+    w = W("tiny_siso_f32", batch=3, heads=4, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=1)
+    check_decode_gated(w, seed=1300 + P + N + R, down=True)
+
+
+def test_decode_down_full_size_sampled():
+    w = syn.WORKLOADS["decode_mimo_r4_n64"]
+    rng = np.random.default_rng(12)
+    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(16)]
+    check_decode_gated(w, seed=1350, pairs=pairs, down=True)
