@@ -7,4 +7,5 @@ from .mamba3_oracle import (  # noqa: F401
     zero_state, discretize, rot_pairs, prefill, decode_step,
     prefill_rotated_frame, prefill_complex, prefill_chunked,
     EXP_TRAPEZOID, DECAYED_TRAPEZOID, EXP_EULER, gated_rmsnorm, rank_down_projection,
+    bc_rmsnorm,
 )

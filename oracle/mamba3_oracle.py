@@ -338,6 +338,24 @@ def prefill_chunked(x, Bm, Cm, dt, lam, theta, A, D, state=None, chunk=64, disc=
     return y, (h_out, Bp_out, xp_out)
 
 
+def bc_rmsnorm(v, weight, eps):
+    """BC normalisation: RMSNorm of the input and output projections B and C.
+
+    ai-flow-lab.com Mamba-3 summary, section "実装とカーネル最適化" (BC/QK
+    normalisation: the QKNorm of attention carried over to the SSM's B and C),
+    and lilting.ch Mamba-3 article, the paragraph on other changes (a QKNorm
+    layer added for training stability) and the comparison table's
+    normalisation row.  Each (token, head, rank) row of N state channels is
+    normalised by its root mean square and scaled per channel by the head's
+    weight, before the scan uses it (and so before any rotation):
+        out[..., h, r, n] = weight[h, n] * v[..., h, r, n] / sqrt(mean_n v[..., h, r, :]^2 + eps)
+    v: (..., H, R, N); weight: (H, N); eps: scalar >= 0.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return np.asarray(weight, dtype=np.float64)[:, None, :] * v / np.sqrt(ms + eps)
+
+
 def rank_down_projection(y, down):
     """MIMO read-out: the R rank outputs of a (token, head) folded into one row
     of P channels.

@@ -641,3 +641,76 @@ def test_rank_down_pins_catch_planted_mistake(bad, monkeypatch):
     monkeypatch.setattr(oracle, "rank_down_projection", bad)
     with pytest.raises(AssertionError):
         test_rank_down_worked_example()
+
+
+# ---------------------------------------------------------------------------
+# BC normalisation (RMSNorm of B and C rows before the scan)
+# ---------------------------------------------------------------------------
+
+def test_bc_rmsnorm_worked_example():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "bc_rmsnorm_worked.json")))
+    v = np.array(g["v"])[None, None, :]      # (H=1, R=1, N=4)
+    w = np.array(g["weight"])[None, :]
+    for case in g["cases"]:
+        out = oracle.bc_rmsnorm(v, w, case["eps"])
+        assert np.max(np.abs(out[0, 0] - np.array(case["out"]))) < case["tolerance"]
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.5])
+def test_bc_rmsnorm_matches_torch(eps):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(31)
+    b, T, H, R, N = 2, 3, 4, 2, 32
+    v = rng.standard_normal((b, T, H, R, N)) * 2.5
+    w = rng.standard_normal((H, N))
+    out = oracle.bc_rmsnorm(v, w, eps)
+    tv, tw = torch.from_numpy(v), torch.from_numpy(w)
+    ref = torch.stack([torch.nn.functional.rms_norm(tv[:, :, h], (N,), weight=tw[h], eps=eps) for h in range(H)],
+                      dim=2)
+    assert relerr(out, ref.numpy()) < 1e-13
+
+
+def test_bc_rmsnorm_unit_rows_and_weights_are_identity():
+    """Rows that already have unit RMS, unit weights and eps = 0: the prefill
+    with normalised B and C equals the plain prefill."""
+    rng = np.random.default_rng(32)
+    b, T, H, R, P, N = 1, 9, 2, 2, 4, 6
+    Bm = rng.standard_normal((b, T, H, R, N))
+    Cm = rng.standard_normal((b, T, H, R, N))
+    Bm /= np.sqrt(np.mean(Bm * Bm, axis=-1, keepdims=True))
+    Cm /= np.sqrt(np.mean(Cm * Cm, axis=-1, keepdims=True))
+    ones = np.ones((H, N))
+    assert relerr(oracle.bc_rmsnorm(Bm, ones, 0.0), Bm) < 1e-15
+    assert relerr(oracle.bc_rmsnorm(Cm, ones, 0.0), Cm) < 1e-15
+
+
+def test_bc_rmsnorm_scale_invariant():
+    rng = np.random.default_rng(33)
+    v = rng.standard_normal((5, 3, 2, 16))
+    w = rng.standard_normal((3, 16))
+    c = rng.uniform(0.01, 100.0, (5, 3, 2, 1))
+    assert relerr(oracle.bc_rmsnorm(c * v, w, 0.0), oracle.bc_rmsnorm(v, w, 0.0)) < 1e-13
+
+
+def _bad_bc_axis(v, weight, eps):
+    """Normalised over the ranks instead of the state channels."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.asarray(weight)[:, None, :] * v / np.sqrt(np.mean(v * v, axis=-2, keepdims=True) + eps)
+
+
+def _bad_bc_eps_outside(v, weight, eps):
+    """eps added to the root instead of the mean square."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.asarray(weight)[:, None, :] * v / (np.sqrt(np.mean(v * v, axis=-1, keepdims=True)) + eps)
+
+
+@pytest.mark.parametrize("bad", [_bad_bc_axis, _bad_bc_eps_outside])
+def test_bc_rmsnorm_pins_catch_planted_mistake(bad, monkeypatch):
+    monkeypatch.setattr(oracle, "bc_rmsnorm", bad)
+    caught = 0
+    for fn in (test_bc_rmsnorm_worked_example, lambda: test_bc_rmsnorm_matches_torch(0.5)):
+        try:
+            fn()
+        except AssertionError:
+            caught += 1
+    assert caught > 0
