@@ -117,7 +117,7 @@ def committed_traffic(workload_name):
 
 
 class Prefill:
-    def __init__(self, w, seed, long_memory=False, disc="exp_trapezoid", gated=False, down=False):
+    def __init__(self, w, seed, long_memory=False, disc="exp_trapezoid", gated=False, down=False, bcnorm=False):
         import torch
         import state_space_sequence_prefill_amd as m3
         from state_space_sequence_prefill_amd import synthetic as syn
@@ -131,13 +131,24 @@ class Prefill:
         self.ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
         self.nlaunch = 1 if not nws else 3
         self.gate = syn.draw_gate_torch(w, seed + 1, folded=down) if gated or down else None
+        self.bcnorm = None
+        if bcnorm:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(seed + 2)
+            self.bcnorm = tuple(torch.rand((w.heads, w.dstate), generator=g, device="cuda") + 0.5
+                                for _ in range(2)) + (1e-6,)
 
     def step(self, ev=None):
         i = self.inp
         self.m3.m3_state_zero(self.d, self.state)
         if ev is not None:
             ev[0].record()
-        if self.gate is None:
+        if self.bcnorm is not None:
+            gate = None if self.gate is None else (self.gate[0], self.gate[1], 1e-5)
+            self.m3.mamba3_prefill_ex(self.d, self.w.seqlen, i["x"], i["B"], i["C"], i["dt"], i["lam"], i["theta"],
+                                      i["A"], i["D"], self.state, self.y, bcnorm=self.bcnorm, gate=gate,
+                                      workspace=self.ws)
+        elif self.gate is None:
             self.m3.mamba3_prefill(self.d, self.w.seqlen, i["x"], i["B"], i["C"], i["dt"], i["lam"], i["theta"],
                                    i["A"], i["D"], self.state, self.y, self.ws)
         else:
@@ -165,7 +176,7 @@ class Prefill:
         return wall / steps * 1e3, kern_ms
 
 
-def time_decode(w, seed, steps=1000, flush_steps=20, gated=False, down=False):
+def time_decode(w, seed, steps=1000, flush_steps=20, gated=False, down=False, bcnorm=False):
     import torch
     import state_space_sequence_prefill_amd as m3
     from state_space_sequence_prefill_amd import synthetic as syn
@@ -190,9 +201,18 @@ def time_decode(w, seed, steps=1000, flush_steps=20, gated=False, down=False):
         z, gw = syn.draw_gate_torch(w, seed + 2)
         z = z[:, 0].contiguous()
 
+    nb = None
+    if bcnorm:
+        gg = torch.Generator(device="cuda")
+        gg.manual_seed(seed + 3)
+        nb = tuple(torch.rand((w.heads, w.dstate), generator=gg, device="cuda") + 0.5 for _ in range(2)) + (1e-6,)
+
     def one(j):
         s = sets[j % nset]
-        if gated:
+        if bcnorm:
+            m3.mamba3_decode_step_ex(d, s["x"], s["B"], s["C"], s["dt"], s["lam"], s["theta"], s["A"], s["D"], st, y,
+                                     bcnorm=nb, gate=(z, gw, 1e-5) if gated else None)
+        elif gated:
             m3.mamba3_decode_step_gated(d, s["x"], s["B"], s["C"], s["dt"], s["lam"], s["theta"], s["A"], s["D"],
                                         z, gw, 1e-5, st, y, down=dw)
         else:
@@ -235,8 +255,9 @@ def time_decode(w, seed, steps=1000, flush_steps=20, gated=False, down=False):
         tot += a.elapsed_time(b)
     us_flush = tot * 1e3 / flush_steps
     nb = decode_bytes(w) + (gate_bytes(w, 1) if gated else 0) + (down_bytes_delta(w, 1) if down else 0)
+    nb += 2 * w.heads * w.dstate * 4 if bcnorm else 0
     return {
-        "workload": w.name + ("_down_gated" if down else "_gated" if gated else ""), "batch": w.batch, "heads": w.heads, "headdim": w.headdim, "dstate": w.dstate,
+        "workload": w.name + ("_bcnorm" if bcnorm else "") + ("_down_gated" if down else "_gated" if gated else ""), "batch": w.batch, "heads": w.heads, "headdim": w.headdim, "dstate": w.dstate,
         "rank": w.rank, "us_per_step_graph": round(us_graph, 2), "steps_graph": reps * per_graph,
         "us_per_step_flushed": round(us_flush, 2), "bytes_per_step": nb,
         "hbm_GBs_graph": round(nb / us_graph / 1e3, 1), "hbm_frac_graph": round(nb / us_graph / 1e3 / HBM_PEAK_GBS, 4),
@@ -485,6 +506,24 @@ def main():
         extra["decode_mimo_r4_n64_down_gated"] = time_decode(syn.WORKLOADS["decode_mimo_r4_n64"], seed=7,
                                                              flush_steps=5, down=True)
         torch.cuda.empty_cache()
+        # BC normalisation in the prefill prep (plain and gated y) and in the
+        # decode step (gated y); the weights add 2 H N fp32 to the bytes
+        for gated in (False, True):
+            tag = f"{w.name}_bcnorm" + ("_gated" if gated else "")
+            log(f"bench: prefill {tag}")
+            p = Prefill(w, seed=1006, gated=gated, bcnorm=True)
+            ms, kms = p.time(max(3, args.steps // 2), 2)
+            nbb = nbytes + (gate_bytes(w, w.seqlen) if gated else 0) + 2 * w.heads * w.dstate * 4
+            extra[tag] = {"ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                          "Mtokens_per_s": round(w.batch * w.seqlen / ms / 1e3, 3), "algorithmic_bytes": nbb,
+                          "hbm_frac": round(nbb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del p
+            torch.cuda.empty_cache()
+        for name in ("decode_mimo_r4_n64", "decode_siso_n128"):
+            log(f"bench: bcnorm gated decode {name}")
+            extra[f"{name}_bcnorm_gated"] = time_decode(syn.WORKLOADS[name], seed=7, flush_steps=5, gated=True,
+                                                        bcnorm=True)
+            torch.cuda.empty_cache()
         line["extra"] = extra
 
     if not args.no_cpu_baseline:

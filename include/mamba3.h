@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 3
+#define M3_ABI_VERSION 4
 
 typedef enum {
   M3_OK = 0,
@@ -214,6 +214,41 @@ int mamba3_decode_step_gated(const m3_dims* dims, const void* x, const void* B, 
                              const float* dt, const float* lam, const float* theta,
                              const float* A, const float* D, const m3_gate* gate, m3_state* state,
                              void* y, void* stream);
+
+/* BC normalisation (ai-flow-lab.com Mamba-3 summary, section
+ * "実装とカーネル最適化": BC/QK normalisation, the QKNorm of attention applied
+ * to the SSM's B and C; lilting.ch Mamba-3 article, comparison table,
+ * normalisation row).  Before the scan uses them (and before any rotation),
+ * every (token, head, rank) row of N channels of B and of C is normalised by
+ * its RMS and scaled per channel:
+ *   B'[n] = b_weight[head][n] * B[n] / sqrt(mean_n B[n]^2 + eps),
+ *   C'[n] = c_weight[head][n] * C[n] / sqrt(mean_n C[n]^2 + eps).
+ * The pending B_prev in the state stays the raw B of the last token and is
+ * normalised the same way where the recurrence uses it.
+ *   b_weight, c_weight  fp32 (heads, N), device pointers, 16-byte aligned
+ *   eps                 >= 0 */
+typedef struct {
+  const float* b_weight;
+  const float* c_weight;
+  float eps;
+} m3_bcnorm;
+
+/* mamba3_prefill with optional BC normalisation (bcnorm, NULL: none) and an
+ * optional output epilogue (gate, NULL: the raw scan output, as
+ * mamba3_prefill; otherwise as mamba3_prefill_gated).  Same errors as those
+ * two, plus M3_ERR_NULL / M3_ERR_ALIGN for bcnorm's weights, M3_ERR_SHAPE for
+ * a negative or NaN bcnorm->eps, and M3_ERR_UNSUPPORTED for sizes whose
+ * normalising prefill tiles do not fit (fp32 shapes served only by the
+ * single-role kernel; bf16 with N = 64 and P = 16). */
+int mamba3_prefill_ex(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                      const float* dt, const float* lam, const float* theta, const float* A, const float* D,
+                      const m3_bcnorm* bcnorm, const m3_gate* gate, m3_state* state, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* mamba3_decode_step with optional BC normalisation and output epilogue. */
+int mamba3_decode_step_ex(const m3_dims* dims, const void* x, const void* B, const void* C, const float* dt,
+                          const float* lam, const float* theta, const float* A, const float* D,
+                          const m3_bcnorm* bcnorm, const m3_gate* gate, m3_state* state, void* y, void* stream);
 
 #ifdef __cplusplus
 }

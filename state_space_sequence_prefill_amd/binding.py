@@ -35,7 +35,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "m3_abi_version", "m3_last_error", "m3_state_bytes", "m3_state_zero", "m3_state_load",
     "m3_state_readout", "mamba3_prefill_workspace_bytes", "mamba3_prefill", "mamba3_decode_step",
-    "mamba3_prefill_gated", "mamba3_decode_step_gated",
+    "mamba3_prefill_gated", "mamba3_decode_step_gated", "mamba3_prefill_ex", "mamba3_decode_step_ex",
 )
 
 
@@ -60,6 +60,10 @@ class m3_gate(ctypes.Structure):
                 ("down", ctypes.c_void_p)]
 
 
+class m3_bcnorm(ctypes.Structure):
+    _fields_ = [("b_weight", ctypes.c_void_p), ("c_weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -73,6 +77,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         D, S, G = ctypes.POINTER(m3_dims), ctypes.POINTER(m3_state), ctypes.POINTER(m3_gate)
+        NB = ctypes.POINTER(m3_bcnorm)
         L.m3_abi_version.restype = ctypes.c_int
         L.m3_abi_version.argtypes = []
         L.m3_last_error.restype = ctypes.c_char_p
@@ -95,6 +100,10 @@ def lib():
         L.mamba3_prefill_gated.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, G, S, vp, vp, sz, vp]
         L.mamba3_decode_step_gated.restype = ctypes.c_int
         L.mamba3_decode_step_gated.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, G, S, vp, vp]
+        L.mamba3_prefill_ex.restype = ctypes.c_int
+        L.mamba3_prefill_ex.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, NB, G, S, vp, vp, sz, vp]
+        L.mamba3_decode_step_ex.restype = ctypes.c_int
+        L.mamba3_decode_step_ex.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, NB, G, S, vp, vp]
         _lib = L
     return _lib
 
@@ -324,3 +333,43 @@ def _decode_args(dims, x, B, C, dt, lam, theta, A, D, y, no_rank=False):
     ]
     py = _ptr(y, "y", (d.batch, Hh, P) if no_rank else (d.batch, Hh, R, P), io)
     return args, py
+
+
+def _bcnorm(dims, bcnorm):
+    """m3_bcnorm from (b_weight, c_weight, eps) with fp32 (heads, N) weights, or None."""
+    if bcnorm is None:
+        return None
+    bw, cw, eps = bcnorm
+    f32 = _torch().float32
+    return m3_bcnorm(_ptr(bw, "b_weight", (dims.heads, dims.dstate), f32),
+                     _ptr(cw, "c_weight", (dims.heads, dims.dstate), f32), float(eps))
+
+
+def mamba3_prefill_ex(dims, seqlen, x, B, C, dt, lam, theta, A, D, state, y, bcnorm=None, gate=None,
+                      workspace=None, stream=None):
+    """mamba3_prefill with optional BC normalisation ``bcnorm = (b_weight,
+    c_weight, eps)`` (weights fp32 (heads, N)) and optional output epilogue
+    ``gate = (z, weight, eps)`` or ``(z, weight, eps, down)`` (as in
+    mamba3_prefill_gated)."""
+    down = gate[3] if gate is not None and len(gate) > 3 else None
+    args, py = _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y, down is not None)
+    g = _gate(dims, gate[0], gate[1], gate[2], (dims.batch, int(seqlen)), down) if gate is not None else None
+    nb = _bcnorm(dims, bcnorm)
+    ws, wsb = _workspace(workspace)
+    cs = state.c_struct()
+    _check(lib().mamba3_prefill_ex(ctypes.byref(dims), int(seqlen), *args, None if nb is None else ctypes.byref(nb),
+                                   None if g is None else ctypes.byref(g), ctypes.byref(cs), py, ws, wsb,
+                                   _stream(stream)))
+
+
+def mamba3_decode_step_ex(dims, x, B, C, dt, lam, theta, A, D, state, y, bcnorm=None, gate=None, stream=None):
+    """mamba3_decode_step with optional BC normalisation and output epilogue
+    (arguments as in mamba3_prefill_ex)."""
+    down = gate[3] if gate is not None and len(gate) > 3 else None
+    args, py = _decode_args(dims, x, B, C, dt, lam, theta, A, D, y, down is not None)
+    g = _gate(dims, gate[0], gate[1], gate[2], (dims.batch,), down) if gate is not None else None
+    nb = _bcnorm(dims, bcnorm)
+    cs = state.c_struct()
+    _check(lib().mamba3_decode_step_ex(ctypes.byref(dims), *args, None if nb is None else ctypes.byref(nb),
+                                       None if g is None else ctypes.byref(g), ctypes.byref(cs), py,
+                                       _stream(stream)))

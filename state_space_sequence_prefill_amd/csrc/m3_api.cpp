@@ -240,10 +240,26 @@ int check_gate(const m3_gate* gate, const void** gz, const float** gw, float* ge
   return M3_OK;
 }
 
+// BC-normalisation argument checks (bcnorm may be NULL: no normalisation).
+int check_bcnorm(const m3_bcnorm* bc, const float** nbw, const float** ncw, float* neps) {
+  *nbw = nullptr;
+  *ncw = nullptr;
+  *neps = 0.f;
+  if (!bc) return M3_OK;
+  int st;
+  if ((st = check_ptr(bc->b_weight, "bcnorm.b_weight")) != M3_OK) return st;
+  if ((st = check_ptr(bc->c_weight, "bcnorm.c_weight")) != M3_OK) return st;
+  if (!(bc->eps >= 0.f)) return fail(M3_ERR_SHAPE, "bcnorm.eps must be >= 0 (got %g)", (double)bc->eps);
+  *nbw = bc->b_weight;
+  *ncw = bc->c_weight;
+  *neps = bc->eps;
+  return M3_OK;
+}
+
 int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
                  const float* dt, const float* lam, const float* theta, const float* A, const float* D,
-                 const m3_gate* gate, bool gated, m3_state* state, void* y, void* workspace,
-                 size_t workspace_bytes, void* stream, const char* what) {
+                 const m3_bcnorm* bcnorm, const m3_gate* gate, bool gated, m3_state* state, void* y,
+                 void* workspace, size_t workspace_bytes, void* stream, const char* what) {
   m3::Dims m;
   int st = check_dims(dims, true, &m);
   if (st != M3_OK) return st;
@@ -255,9 +271,19 @@ int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void*
   float geps = 0.f;
   if (gated) {
     if ((st = check_gate(gate, &gz, &gw, &geps, &gdown)) != M3_OK) return st;
-    if (!m3::prefill_gated_supported(m))
+    if (!m3::prefill_pc_path_supported(m))
       return fail(M3_ERR_UNSUPPORTED, "the gated epilogue needs the producer/consumer prefill kernel, whose "
                                       "tiles do not fit for these sizes");
+  }
+  const float *nbw = nullptr, *ncw = nullptr;
+  float neps = 0.f;
+  if ((st = check_bcnorm(bcnorm, &nbw, &ncw, &neps)) != M3_OK) return st;
+  if (nbw) {
+    m3::Dims e = m;
+    e.Q = m3::prefill_tile_chunk(m);
+    if (!m3::prefill_pc_bcnorm_supported(e))
+      return fail(M3_ERR_UNSUPPORTED, "the BC normalisation needs the producer/consumer prefill kernel, whose "
+                                      "tiles with the normalisation do not fit for these sizes");
   }
   if (seqlen == 0) return ok();
   m.Q = m3::prefill_tile_chunk(m);
@@ -295,6 +321,9 @@ int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void*
   a.gw = gw;
   a.geps = geps;
   a.gdown = gdown;
+  a.nbw = nbw;
+  a.ncw = ncw;
+  a.neps = neps;
   a.seqlen = seqlen;
   a.nseg = nseg;
   a.seg_chunks = sc;
@@ -314,8 +343,8 @@ int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void*
 }
 
 int decode_impl(const m3_dims* dims, const void* x, const void* B, const void* C, const float* dt,
-                const float* lam, const float* theta, const float* A, const float* D, const m3_gate* gate,
-                bool gated, m3_state* state, void* y, void* stream, const char* what) {
+                const float* lam, const float* theta, const float* A, const float* D, const m3_bcnorm* bcnorm,
+                const m3_gate* gate, bool gated, m3_state* state, void* y, void* stream, const char* what) {
   m3::Dims m;
   int st = check_dims(dims, false, &m);
   if (st != M3_OK) return st;
@@ -325,6 +354,9 @@ int decode_impl(const m3_dims* dims, const void* x, const void* B, const void* C
   const float* gdown = nullptr;
   float geps = 0.f;
   if (gated && (st = check_gate(gate, &gz, &gw, &geps, &gdown)) != M3_OK) return st;
+  const float *nbw = nullptr, *ncw = nullptr;
+  float neps = 0.f;
+  if ((st = check_bcnorm(bcnorm, &nbw, &ncw, &neps)) != M3_OK) return st;
   const void* ptrs[] = {x, B, C, dt, lam, theta, A, D, y};
   const char* names[] = {"x", "B", "C", "dt", "lam", "theta", "A", "D", "y"};
   for (int i = 0; i < 9; ++i)
@@ -347,6 +379,9 @@ int decode_impl(const m3_dims* dims, const void* x, const void* B, const void* C
   a.gw = gw;
   a.geps = geps;
   a.gdown = gdown;
+  a.nbw = nbw;
+  a.ncw = ncw;
+  a.neps = neps;
   return hip_status(m3::launch_decode(m, a, static_cast<hipStream_t>(stream)), what);
 }
 
@@ -358,7 +393,7 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
                    const float* dt, const float* lam, const float* theta, const float* A,
                    const float* D, m3_state* state, void* y, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, nullptr, false, state, y, workspace,
+  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, nullptr, nullptr, false, state, y, workspace,
                       workspace_bytes, stream, "mamba3_prefill");
 }
 
@@ -366,22 +401,37 @@ int mamba3_prefill_gated(const m3_dims* dims, int32_t seqlen, const void* x, con
                          const float* dt, const float* lam, const float* theta, const float* A,
                          const float* D, const m3_gate* gate, m3_state* state, void* y, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, gate, true, state, y, workspace,
+  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, nullptr, gate, true, state, y, workspace,
                       workspace_bytes, stream, "mamba3_prefill_gated");
+}
+
+int mamba3_prefill_ex(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                      const float* dt, const float* lam, const float* theta, const float* A, const float* D,
+                      const m3_bcnorm* bcnorm, const m3_gate* gate, m3_state* state, void* y, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, bcnorm, gate, gate != nullptr, state, y,
+                      workspace, workspace_bytes, stream, "mamba3_prefill_ex");
 }
 
 int mamba3_decode_step(const m3_dims* dims, const void* x, const void* B, const void* C,
                        const float* dt, const float* lam, const float* theta, const float* A,
                        const float* D, m3_state* state, void* y, void* stream) {
-  return decode_impl(dims, x, B, C, dt, lam, theta, A, D, nullptr, false, state, y, stream,
+  return decode_impl(dims, x, B, C, dt, lam, theta, A, D, nullptr, nullptr, false, state, y, stream,
                      "mamba3_decode_step");
 }
 
 int mamba3_decode_step_gated(const m3_dims* dims, const void* x, const void* B, const void* C,
                              const float* dt, const float* lam, const float* theta, const float* A,
                              const float* D, const m3_gate* gate, m3_state* state, void* y, void* stream) {
-  return decode_impl(dims, x, B, C, dt, lam, theta, A, D, gate, true, state, y, stream,
+  return decode_impl(dims, x, B, C, dt, lam, theta, A, D, nullptr, gate, true, state, y, stream,
                      "mamba3_decode_step_gated");
+}
+
+int mamba3_decode_step_ex(const m3_dims* dims, const void* x, const void* B, const void* C, const float* dt,
+                          const float* lam, const float* theta, const float* A, const float* D,
+                          const m3_bcnorm* bcnorm, const m3_gate* gate, m3_state* state, void* y, void* stream) {
+  return decode_impl(dims, x, B, C, dt, lam, theta, A, D, bcnorm, gate, gate != nullptr, state, y, stream,
+                     "mamba3_decode_step_ex");
 }
 
 }  // extern "C"

@@ -210,7 +210,14 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
                                 reinterpret_cast<const uint4*>(x),
                                 reinterpret_cast<const uint4*>(a.theta + (size_t)head * (N / 2))};
   const int gstart[6] = {0, gB, 2 * gB, 3 * gB, 3 * gB + gX, 3 * gB + 2 * gX};
-  // output epilogue operands first: the wait below then covers them as well
+  // BC-normalisation weights of this lane's 4 columns, and the output
+  // epilogue operands, first: the wait below then covers them as well
+  const bool bcn = a.nbw != nullptr;
+  float4 gwb = make_float4(1.f, 1.f, 1.f, 1.f), gwc = gwb;
+  if (bcn) {
+    gwb = *reinterpret_cast<const float4*>(a.nbw + (size_t)hh * N + 4 * n4);
+    gwc = *reinterpret_cast<const float4*>(a.ncw + (size_t)hh * N + 4 * n4);
+  }
   const bool gated = a.gz != nullptr;
   DecodeGate<IO, R> gate;
   if (gated)
@@ -265,6 +272,21 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
     load4(sBp + r * N + 4 * n4, Bp[r]);
     load4(sBc + r * N + 4 * n4, Bn[r]);
     load4(sCc + r * N + 4 * n4, Cn[r]);
+    if (bcn) {
+      // BC normalisation: row sums over the LPR lanes of a state row (each
+      // holds 4 of the N columns), then RMS scale and column weights
+      auto norm = [&](float (&v)[4], const float4& gw) {
+        const float ss = lane_group_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3], LPR);
+        const float sc = rsqrtf(ss * (1.0f / N) + a.neps);
+        v[0] *= gw.x * sc;
+        v[1] *= gw.y * sc;
+        v[2] *= gw.z * sc;
+        v[3] *= gw.w * sc;
+      };
+      norm(Bp[r], gwb);
+      norm(Bn[r], gwb);
+      norm(Cn[r], gwc);
+    }
     rot2(Bp[r][0], Bp[r][1], c0, s0);
     rot2(Bp[r][2], Bp[r][3], c1, s1);
 #pragma unroll

@@ -120,6 +120,27 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   float* sXk = sBk + 4 * kKG * N;                          // [4 kKG][P]
   float* sCf = sXk + 4 * kKG * P;                          // [R][N]
 
+  // ---- 1b. BC normalisation: RMS scales of the 3R rows B_prev, B, C (wave w
+  //          takes rows w, w + waves, ...; lane l columns l and l + 64)
+  const bool bcn = a.nbw != nullptr;
+  float* const sScl = reinterpret_cast<float*>(dsm + L::bytes(P));  // [3R], padded to 16 floats
+  if (bcn) {
+    const int nw = nthr / kWave;
+    for (int j = wave; j < 3 * R; j += nw) {
+      const IO* row = sBp + j * N;  // B_prev, B, C rows are contiguous
+      float ss = 0.f;
+      for (int n = lane; n < N; n += kWave) {
+        const float v = to_f32(row[n]);
+        ss += v * v;
+      }
+      ss = lane_group_sum(ss, kWave);
+      if (lane == 0) sScl[j] = rsqrtf(ss * (1.0f / N) + a.neps);
+    }
+    __syncthreads();
+  }
+  const float* nwB = bcn ? a.nbw + (size_t)hh * N : nullptr;
+  const float* nwC = bcn ? a.ncw + (size_t)hh * N : nullptr;
+
   // ---- 2. derived fp32 operands (whole workgroup)
   {
     const float alpha = expf(dt * Ah);
@@ -138,10 +159,14 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
         const int j = n >> 1;
         float s, co;
         sincosf(sTh[j], &s, &co);
-        const float b0 = to_f32(sBp[k * N + 2 * j]), b1 = to_f32(sBp[k * N + 2 * j + 1]);
+        float b0 = to_f32(sBp[k * N + 2 * j]), b1 = to_f32(sBp[k * N + 2 * j + 1]);
+        if (bcn) {
+          b0 *= nwB[2 * j] * sScl[k];
+          b1 *= nwB[2 * j + 1] * sScl[k];
+        }
         v = beta * ((n & 1) ? (s * b0 + co * b1) : (co * b0 - s * b1));
       } else if (k < 2 * R) {
-        v = gamma * to_f32(sBc[(k - R) * N + n]);
+        v = gamma * to_f32(sBc[(k - R) * N + n]) * (bcn ? nwB[n] * sScl[k] : 1.f);
       }
       sBk[e] = v;
     }
@@ -150,7 +175,8 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
       const int k = e / P, p = e % P;
       sXk[e] = k < R ? to_f32(sXp[k * P + p]) : (k < 2 * R ? to_f32(sXc[(k - R) * P + p]) : 0.f);
     }
-    for (int e = tid; e < R * N; e += nthr) sCf[e] = to_f32(sCc[e]);
+    for (int e = tid; e < R * N; e += nthr)
+      sCf[e] = to_f32(sCc[e]) * (bcn ? nwC[e % N] * sScl[2 * R + e / N] : 1.f);
   }
   __syncthreads();
 
@@ -180,7 +206,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   }
   // ---- 4. y: lanes g = 0 hold Y^T[r = i][p = 16pb + c] for r < R
   //         (gated: the fp32 outputs go to LDS behind the derived operands)
-  float* const sYg = reinterpret_cast<float*>(dsm + L::bytes(P));
+  float* const sYg = reinterpret_cast<float*>(dsm + L::bytes(P) + 64);
   if (g == 0) {
     IO* y = static_cast<IO*>(a.y) + (size_t)head * R * P + 16 * pb + c;
 #pragma unroll
@@ -211,7 +237,8 @@ template <typename IO, int N, int R>
 hipError_t launch_mimo_t(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   const int waves = d.P / 16;
   const dim3 grid(d.batch * d.heads), block(waves * kWave);
-  const size_t lds = MimoLds<IO, N, R>::bytes(d.P) + (a.gz ? (size_t)R * d.P * sizeof(float) : 0);
+  // derived operands, then 16 floats of BC-norm scales, then the gated outputs
+  const size_t lds = MimoLds<IO, N, R>::bytes(d.P) + 64 + (a.gz ? (size_t)R * d.P * sizeof(float) : 0);
   if (MimoLds<IO, N, R>::granules(d.P) <= waves * kWave)
     hipLaunchKernelGGL((decode_mimo_kernel<IO, N, R, 1>), grid, block, lds, s, a, d.heads, d.P);
   else

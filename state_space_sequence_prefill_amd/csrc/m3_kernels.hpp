@@ -33,6 +33,9 @@ struct DecodeArgs {
   const float* gw;
   float geps;
   const float* gdown;
+  const float* nbw;  // BC normalisation, as in PrefillArgs
+  const float* ncw;
+  float neps;
 };
 
 // Arguments of one prefill pass over tokens [0, seqlen) of every chain.
@@ -57,6 +60,12 @@ struct PrefillArgs {
   const float* gw;
   float geps;
   const float* gdown;
+  // BC normalisation of the B and C rows before the scan (weights (heads, N)
+  // each, applied to the pending B_prev as well, which stays raw in the
+  // state); nbw == nullptr: none
+  const float* nbw;
+  const float* ncw;
+  float neps;
   int seqlen;
   // Segment path (long prompts, few chains).  nseg == 1: plain fused pass.
   int nseg;        // number of segments the sequence is split into
@@ -80,8 +89,9 @@ bool prefill_supported(const Dims& d);
 // Producer/consumer prefill (m3_prefill_pc.hip): used for every pass whose
 // double-buffered tiles fit; `mode` 0 fused, 1 segment summaries, 2 segments.
 bool prefill_pc_supported(const Dims& d);
-// Whether the gated epilogue is available for these dims (producer/consumer path).
-bool prefill_gated_supported(const Dims& d);
+// Whether the producer/consumer kernel serves these dims at some tile height:
+// the gated epilogue and the BC normalisation live only there.
+bool prefill_pc_path_supported(const Dims& d);
 // Chunk length the prefill kernels tile with (<= d.Q; see m3_prefill.hip).
 int prefill_tile_chunk(const Dims& d);
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
@@ -89,5 +99,13 @@ hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s,
 // and through the rank down-projection and the epilogue (m3_prefill_pc_down.hip).
 hipError_t launch_prefill_pc_gated(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
 hipError_t launch_prefill_pc_down(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
+// The three variants with the BC normalisation in the producers' prep
+// (m3_prefill_pc_bcnorm*.hip); epi 0 plain, 1 gated, 2 down-projected + gated.
+hipError_t launch_prefill_pc_bcnorm(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks, int epi);
+hipError_t launch_prefill_pc_bcnorm_gated(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
+hipError_t launch_prefill_pc_bcnorm_down(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);
+// Whether the BC-normalisation instances serve these dims (their LDS holds
+// the norm's weights and partial sums on top of the plain tiles).
+bool prefill_pc_bcnorm_supported(const Dims& d);
 
 }  // namespace m3

@@ -637,13 +637,32 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a, int ba
   const long long elem = (long long)gw * per_wave + sub;         // over chains * P * N/2
   const long long nelem = (long long)chains * P * (N / 2);
   const bool active = elem < nelem;
-  const long long el = active ? elem : 0;
+  const long long el = active ? elem : nelem - 1;  // past the end: the last element's chain
   const int chain = (int)(el / ((long long)P * (N / 2)));
   const int rem = (int)(el % ((long long)P * (N / 2)));
   const int p = rem / (N / 2), j = rem % (N / 2);
   const int hh = chain % H;
   const size_t seg_stride = (size_t)chains;
 
+  // BC normalisation of the pending B_prev rows: a wave's elements all belong
+  // to one chain (P * N/2 is a multiple of the elements per wave), so the
+  // wave sums each row's squares together (lane l: columns l, l + 64).
+  float bscale[4] = {1.f, 1.f, 1.f, 1.f};
+  if (a.nbw) {
+    const IO* Bp = static_cast<const IO*>(a.B_prev) + (size_t)chain * R * N;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // R <= 4
+      if (r < R) {
+        float ss = 0.f;
+        for (int n = lane; n < N; n += 64) {
+          const float v = to_f32(Bp[r * N + n]);
+          ss += v * v;
+        }
+        ss = lane_group_sum(ss, 64);
+        bscale[r] = rsqrtf(ss / (float)N + a.neps);
+      }
+    }
+  }
   // E_0 from the state (only the lane of segment 0 needs it).
   float e0r = 0.f, e0i = 0.f;
   if (active && gseg == 0) {
@@ -657,10 +676,15 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a, int ba
     e0i = alpha0 * hp[1];
     const IO* Bp = static_cast<const IO*>(a.B_prev) + (size_t)chain * R * N;
     const IO* Xp = static_cast<const IO*>(a.x_prev) + (size_t)chain * R * P;
-    for (int r = 0; r < R; ++r) {
-      const float xp = beta0 * to_f32(Xp[r * P + p]);
-      e0r += xp * to_f32(Bp[r * N + 2 * j]);
-      e0i += xp * to_f32(Bp[r * N + 2 * j + 1]);
+    const float g0 = a.nbw ? a.nbw[(size_t)hh * N + 2 * j] : 1.f;
+    const float g1 = a.nbw ? a.nbw[(size_t)hh * N + 2 * j + 1] : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < R) {
+        const float xp = beta0 * to_f32(Xp[r * P + p]) * bscale[r];
+        e0r += xp * g0 * to_f32(Bp[r * N + 2 * j]);
+        e0i += xp * g1 * to_f32(Bp[r * N + 2 * j + 1]);
+      }
     }
   }
   // Map of segment g (g < nseg-1): (L_g, Phi_g, W_g); identity elsewhere.
@@ -735,7 +759,8 @@ hipError_t launch_fused_t(const Dims& d, const PrefillArgs& a, hipStream_t st) {
   kp.Q = d.Q;
   const int chains = d.batch * d.heads;
   const bool pc = prefill_pc_supported(d);
-  if (a.gz && !pc) return hipErrorInvalidValue;  // the epilogue lives in the producer/consumer kernel
+  // the epilogue and the BC normalisation live in the producer/consumer kernel
+  if ((a.gz || a.nbw) && !pc) return hipErrorInvalidValue;
   auto pass = [&](int mode, int nblocks) -> hipError_t {
     if (pc) return launch_prefill_pc(d, a, st, mode, nblocks);
     kp.mode = mode;
@@ -822,7 +847,7 @@ int prefill_tile_chunk(const Dims& d) {
   return d.Q;
 }
 
-bool prefill_gated_supported(const Dims& d) {
+bool prefill_pc_path_supported(const Dims& d) {
   Dims e = d;
   e.Q = prefill_tile_chunk(d);
   return prefill_pc_supported(e);

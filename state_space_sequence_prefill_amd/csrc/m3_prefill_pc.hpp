@@ -60,8 +60,9 @@ __device__ __forceinline__ int pc_remap_block(int bid, int nblocks) {
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
 
-// LDS layout for <IO, N, P> with tiles of `rows` (token, rank) rows.
-template <typename IO, int N, int P>
+// LDS layout for <IO, N, P> with tiles of `rows` (token, rank) rows; BCN
+// adds the BC normalisation's weights and partial sums of squares.
+template <typename IO, int N, int P, bool BCN = false>
 struct PcLds {
   static constexpr int E = sizeof(IO);
   static constexpr int PAD = 16 / E;
@@ -80,8 +81,17 @@ struct PcLds {
   // output tile: the consumer waves' y slices meet here and leave as whole rows
   __host__ __device__ static constexpr size_t y_bytes(int rows) { return (size_t)rows * (P + PAD) * E; }
   static constexpr size_t kCoefBytes = 64 * 20 + 16;  // one coefficient slot (Q <= 64)
+  // BC normalisation: a row's N columns are spread over norm_groups(rows)
+  // producer lane groups, whose partial sums of squares meet here
+  // ([B, C][group][rows]), after the weights of B and C (2 N floats)
+  __host__ __device__ static constexpr int norm_groups(int rows) {
+    return (N / 8) * rows / 256 > 1 ? (N / 8) * rows / 256 : 1;
+  }
+  __host__ __device__ static constexpr size_t norm_bytes(int rows) {
+    return BCN ? (size_t)2 * N * 4 + (size_t)2 * norm_groups(rows) * rows * 4 : 0;
+  }
   __host__ __device__ static constexpr size_t bytes(int rows) {
-    return 2 * buf_bytes(rows) + sm_bytes(rows) + y_bytes(rows) + 3 * kCoefBytes + (N / 2) * 4;
+    return 2 * buf_bytes(rows) + sm_bytes(rows) + y_bytes(rows) + 3 * kCoefBytes + (N / 2) * 4 + norm_bytes(rows);
   }
 };
 
@@ -125,9 +135,12 @@ enum PcEpi : int {
   kEpiDown = 2,   // rank down-projection (a.gdown) to (batch, T, H, P), then the same epilogue per (token, head)
 };
 
-template <typename IO, int N, int P, int EPI>
+// BCN: B and C rows are RMS-normalised and scaled per channel (a.nbw, a.ncw,
+// a.neps) as the producers build the tiles; the pending B_prev of the entry
+// state likewise.
+template <typename IO, int N, int P, int EPI, bool BCN>
 __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) {
-  using L = PcLds<IO, N, P>;
+  using L = PcLds<IO, N, P, BCN>;
   using Lim = PcLimits<IO, N, P>;
   constexpr int NB = N / 16, PB = P / 16;
   constexpr int NK = L::NK, LDN = L::LDN, PAD = L::PAD;
@@ -175,6 +188,8 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   IO* const sY = reinterpret_cast<IO*>(smem + 2 * bufStride + smStride);
   char* const coefBase = smem + 2 * bufStride + smStride + yStride;
   float* const sSeg = reinterpret_cast<float*>(coefBase + 3 * coefStride);
+  float* const sGw = sSeg + N / 2;         // BCN: weights of B (N) and C (N)
+  float* const sPart = sGw + 2 * N;        // BCN: [B, C][group][rows_pad] partial sums
   auto getbuf = [&](int ck) {
     char* p = smem + (size_t)(ck & 1) * bufStride;
     PcBuf<IO, N, P> r;
@@ -318,6 +333,43 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         }
       }
     };
+    // BC normalisation, first half: the sums of squares of this thread's row
+    // pieces of the chunk held in `rs`, summed over the GW lanes that share
+    // the rows, into sPart (one float4 of 4 rows per lane group).  The other
+    // half reads them back while building the chunk's tiles.
+    const int NG = npg / GW;  // lane groups per row
+    auto norm_partials = [&](const PcRaw<IO, MI, MX>& rs) {
+      if constexpr (BCN) {
+#pragma unroll
+        for (int m = 0; m < MI; ++m) {
+          float pb[4], pc[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float v[8];
+            rs.b[m][k].unpack(v);
+            float sb = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sb += v[e] * v[e];
+            pb[k] = lane_group_sum(sb, GW);
+            pc[k] = 0.f;
+            if (has_y) {  // segment summaries never read C
+              rs.c[m][k].unpack(v);
+              float sc = 0.f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sc += v[e] * v[e];
+              pc[k] = lane_group_sum(sc, GW);
+            }
+          }
+          if (ist[m] && (lane & (GW - 1)) == 0) {
+            const int grp = ipg[m] / GW;
+            *reinterpret_cast<float4*>(sPart + (size_t)grp * rows_pad + 4 * irg[m]) =
+                make_float4(pb[0], pb[1], pb[2], pb[3]);
+            *reinterpret_cast<float4*>(sPart + (size_t)(NG + grp) * rows_pad + 4 * irg[m]) =
+                make_float4(pc[0], pc[1], pc[2], pc[3]);
+          }
+        }
+      }
+    };
     auto load_dt = [&](int ck) {  // dt, lam of chunk ck (lane = token) and of the token after it
       const int c0 = ck * Q, Lc = chunk_len(ck);
       const int t = lane < Lc ? lane : Lc - 1;
@@ -412,6 +464,23 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             ph[k][j] = base[j] + th[0][j] + (kq >= 1 ? th[1][j] : 0.f) + (kq >= 2 ? th[2][j] : 0.f) +
                        (kq >= 3 ? th[3][j] : 0.f);
         }
+        // BC normalisation, second half: this item's 4 row scales and 8
+        // column weights of B and C
+        float sclB[4] = {1.f, 1.f, 1.f, 1.f}, sclC[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (BCN) {
+          float4 tb = make_float4(0.f, 0.f, 0.f, 0.f), tc = tb;
+          for (int grp = 0; grp < NG; ++grp) {
+            const float4 u = *reinterpret_cast<const float4*>(sPart + (size_t)grp * rows_pad + 4 * rg);
+            const float4 w = *reinterpret_cast<const float4*>(sPart + (size_t)(NG + grp) * rows_pad + 4 * rg);
+            tb.x += u.x; tb.y += u.y; tb.z += u.z; tb.w += u.w;
+            tc.x += w.x; tc.y += w.y; tc.z += w.z; tc.w += w.w;
+          }
+          const float inN = 1.0f / N;
+          sclB[0] = rsqrtf(tb.x * inN + a.neps); sclB[1] = rsqrtf(tb.y * inN + a.neps);
+          sclB[2] = rsqrtf(tb.z * inN + a.neps); sclB[3] = rsqrtf(tb.w * inN + a.neps);
+          sclC[0] = rsqrtf(tc.x * inN + a.neps); sclC[1] = rsqrtf(tc.y * inN + a.neps);
+          sclC[2] = rsqrtf(tc.z * inN + a.neps); sclC[3] = rsqrtf(tc.w * inN + a.neps);
+        }
         float bt[4][8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -422,6 +491,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           const bool valid = t < Lc;
           float bv[8];
           rs.b[m][k].unpack(bv);
+          if constexpr (BCN) {  // column weights read where used (registers are scarce here)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] *= sGw[8 * pg + e] * sclB[k];
+          }
           float cs4[4], sn4[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -439,6 +512,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           if (ist[m] && has_y) {
             float cv[8];
             rs.c[m][k].unpack(cv);
+            if constexpr (BCN) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) cv[e] *= sGw[N + 8 * pg + e] * sclC[k];
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) rot2(cv[2 * j], cv[2 * j + 1], cs4[j], -sn4[j]);
             store8(bf.sB + rho * LDN + 8 * pg, bv);
@@ -501,7 +578,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // consumers' shared score tile of chunk i-1 (other buffers); the first
     // barrier ends both, and the coefficient work and the next loads then
     // overlap the consumers' outputs and state update.
-    auto step = [&](int i, PcRaw<IO, MI, MX>& rs) {
+    auto step = [&](int i, PcRaw<IO, MI, MX>& rs, const PcRaw<IO, MI, MX>& rsn) {
       build_tiles(i, rs);
       __syncthreads();
       const int n1 = i + 1 < ck1 ? i + 1 : i;  // clamped: past the end the data is reloaded, not used
@@ -513,8 +590,15 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         load_dt(n2);
       }
       load_chunk(n2, rs);
+      // BCN: row sums of the next chunk (its loads were issued a step ago;
+      // the in-order counter leaves the loads just issued in flight)
+      norm_partials(rsn);
       __syncthreads();
     };
+    if constexpr (BCN) {
+      for (int j = pt; j < 2 * N; j += kProdThreads)
+        sGw[j] = j < N ? a.nbw[(size_t)hh * N + j] : a.ncw[(size_t)hh * N + j - N];
+    }
     if (ck0 < ck1) {
       // prologue: coefficients of the first chunk, then the first prefetches
       const int n1 = ck0 + 1 < ck1 ? ck0 + 1 : ck0;
@@ -525,16 +609,17 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       load_chunk(ck0, rsA);
       if (pw == 0) load_dt(n1);
       load_chunk(n1, rsB);
+      norm_partials(rsA);
     }
     __syncthreads();
     // the pair loop has no conditional loads, so the wait counts the compiler
     // derives around its back edge stay exact (only the batch consumed waits)
     int i = ck0;
     for (; i + 1 < ck1; i += 2) {
-      step(i, rsA);
-      step(i + 1, rsB);
+      step(i, rsA, rsB);
+      step(i + 1, rsB, rsA);
     }
-    if (i < ck1) step(i, rsA);
+    if (i < ck1) step(i, rsA, rsB);
     __syncthreads();
     __syncthreads();
   } else {
@@ -554,6 +639,29 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         alpha0 = expf(dt0 * Ah);
         beta0 = input_weights(dt0, lm0, alpha0, a.disc).x;
       }
+      // BCN: RMS scales of the pending B_prev rows (lane (g, c) sums its
+      // columns 16 nb + 4 g + i; the four g lanes complete the row)
+      float bsc[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (BCN) {
+        if (mode == kPcFused) {
+          const IO* Bp = static_cast<const IO*>(a.B_prev) + (size_t)chain * R * N;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {  // R <= 4
+            if (r < R) {
+              float ss = 0.f;
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                float bp[4];
+                load4(Bp + r * N + 16 * nb + 4 * g, bp);
+                ss += bp[0] * bp[0] + bp[1] * bp[1] + bp[2] * bp[2] + bp[3] * bp[3];
+              }
+              ss += shfl_xor(ss, 16);
+              ss += shfl_xor(ss, 32);
+              bsc[r] = rsqrtf(ss * (1.0f / N) + a.neps);
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int u = 0; u < PBW; ++u) {
         const int pb = cw + kConsWaves * u;
@@ -570,12 +678,16 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
               const IO* Xp = static_cast<const IO*>(a.x_prev) + (size_t)chain * R * P;
 #pragma unroll
               for (int i4 = 0; i4 < 4; ++i4) v[i4] = alpha0 * h0[i4];
-              for (int r = 0; r < R; ++r) {
-                float bp[4];
-                load4(Bp + r * N + n0, bp);
-                const float xp = beta0 * to_f32(Xp[r * P + p]);
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) v[i4] += xp * bp[i4];
+              for (int r = 0; r < 4; ++r) {  // R <= 4
+                if (r < R) {
+                  float bp[4];
+                  load4(Bp + r * N + n0, bp);
+                  const float xp = beta0 * to_f32(Xp[r * P + p]) * bsc[r];
+#pragma unroll
+                  for (int i4 = 0; i4 < 4; ++i4)
+                    v[i4] += xp * bp[i4] * (BCN ? a.nbw[(size_t)hh * N + n0 + i4] : 1.f);
+                }
               }
             } else if (mode == kPcSegment) {
               load4(a.seg_state + (((size_t)seg * kp.batch * H + chain) * P + p) * N + n0, v);
@@ -909,12 +1021,13 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   }
 }
 
-template <typename IO, int N, int P, int EPI>
+template <typename IO, int N, int P, int EPI, bool BCN>
 hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int mode, int nblocks) {
-  const size_t lds = PcLds<IO, N, P>::bytes(PcLimits<IO, N, P>::kMaxRows);
+  const size_t lds = PcLds<IO, N, P, BCN>::bytes(PcLimits<IO, N, P>::kMaxRows);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;  // (the host checks this first)
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI, BCN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -928,33 +1041,33 @@ hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int 
   kp.Q = d.Q;
   kp.mode = mode;
   kp.nblocks = nblocks;
-  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
+  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI, BCN>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
   return hipGetLastError();
 }
 
-template <typename IO, int N, int EPI>
+template <typename IO, int N, int EPI, bool BCN>
 hipError_t pc_p(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nb) {
   switch (d.P) {
-    case 16: return launch_pc_t<IO, N, 16, EPI>(d, a, s, mode, nb);
-    case 32: return launch_pc_t<IO, N, 32, EPI>(d, a, s, mode, nb);
-    case 64: return launch_pc_t<IO, N, 64, EPI>(d, a, s, mode, nb);
-    default: return launch_pc_t<IO, N, 128, EPI>(d, a, s, mode, nb);
+    case 16: return launch_pc_t<IO, N, 16, EPI, BCN>(d, a, s, mode, nb);
+    case 32: return launch_pc_t<IO, N, 32, EPI, BCN>(d, a, s, mode, nb);
+    case 64: return launch_pc_t<IO, N, 64, EPI, BCN>(d, a, s, mode, nb);
+    default: return launch_pc_t<IO, N, 128, EPI, BCN>(d, a, s, mode, nb);
   }
 }
 
-template <typename IO, int EPI>
+template <typename IO, int EPI, bool BCN>
 hipError_t pc_n(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nb) {
   switch (d.N) {
-    case 16: return pc_p<IO, 16, EPI>(d, a, s, mode, nb);
-    case 32: return pc_p<IO, 32, EPI>(d, a, s, mode, nb);
-    case 64: return pc_p<IO, 64, EPI>(d, a, s, mode, nb);
-    default: return pc_p<IO, 128, EPI>(d, a, s, mode, nb);
+    case 16: return pc_p<IO, 16, EPI, BCN>(d, a, s, mode, nb);
+    case 32: return pc_p<IO, 32, EPI, BCN>(d, a, s, mode, nb);
+    case 64: return pc_p<IO, 64, EPI, BCN>(d, a, s, mode, nb);
+    default: return pc_p<IO, 128, EPI, BCN>(d, a, s, mode, nb);
   }
 }
 
-template <int EPI>
+template <int EPI, bool BCN>
 hipError_t launch_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks) {
-  return d.bf16 ? pc_n<bf16, EPI>(d, a, s, mode, nblocks) : pc_n<float, EPI>(d, a, s, mode, nblocks);
+  return d.bf16 ? pc_n<bf16, EPI, BCN>(d, a, s, mode, nblocks) : pc_n<float, EPI, BCN>(d, a, s, mode, nblocks);
 }
 
 template <typename IO>
@@ -968,6 +1081,22 @@ int pc_max_rows(const Dims& d) {
     M3_CASE(128, 16) M3_CASE(128, 32) M3_CASE(128, 64) M3_CASE(128, 128)
 #undef M3_CASE
     default: return 0;
+  }
+}
+
+// Whether the BC-normalisation instance of <IO, N, P> fits the LDS (its
+// weights and partial sums come on top of the plain instance's tiles).
+template <typename IO>
+bool pc_bcn_fits(const Dims& d) {
+  switch (d.N * 1000 + d.P) {
+#define M3_CASE(NN, PP) \
+  case NN * 1000 + PP: return PcLds<IO, NN, PP, true>::bytes(PcLimits<IO, NN, PP>::kMaxRows) <= 160 * 1024;
+    M3_CASE(16, 16) M3_CASE(16, 32) M3_CASE(16, 64) M3_CASE(16, 128)
+    M3_CASE(32, 16) M3_CASE(32, 32) M3_CASE(32, 64) M3_CASE(32, 128)
+    M3_CASE(64, 16) M3_CASE(64, 32) M3_CASE(64, 64) M3_CASE(64, 128)
+    M3_CASE(128, 16) M3_CASE(128, 32) M3_CASE(128, 64) M3_CASE(128, 128)
+#undef M3_CASE
+    default: return false;
   }
 }
 

@@ -8,7 +8,7 @@
 namespace m3 {
 
 hipError_t launch_prefill_pc_down(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks) {
-  return launch_pc<kEpiDown>(d, a, s, mode, nblocks);
+  return launch_pc<kEpiDown, false>(d, a, s, mode, nblocks);
 }
 
 }  // namespace m3

@@ -16,7 +16,8 @@ A_raw, D.  The output gate (``draw_gate``, its own seed) draws z ~ N(0, 1)
 (same layout as x, or without the rank axis when the ranks are folded) and
 then the per-head channel weights ~ U(0.5, 1.5); the rank down-projection
 (``draw_down``, its own seed) draws weights ~ U(-1, 1) per (head, rank,
-channel).  Values are drawn in float64 and then cast to the I/O dtype by
+channel); the BC normalisation (``draw_bcnorm``, its own seed) draws the
+channel weights of B, then of C, ~ U(0.5, 1.5) per (head, state channel).  Values are drawn in float64 and then cast to the I/O dtype by
 round-to-nearest-even; the exact cast values are what every consumer sees.
 
 The named workloads mirror the pages' 1.5B-scale Mamba-3 layers (32 heads of
@@ -98,6 +99,12 @@ def draw_gate(w: Workload, seed: int, seqlen=None, decode: bool = False, folded:
     z = rng.standard_normal(lead + ((H, P) if folded else (H, R, P)))
     weight = rng.uniform(0.5, 1.5, (H, P))
     return z, weight
+
+
+def draw_bcnorm(w: Workload, seed: int):
+    """BC-normalisation channel weights of B and of C, (H,N) each, fp64."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(0.5, 1.5, (w.heads, w.dstate)), rng.uniform(0.5, 1.5, (w.heads, w.dstate))
 
 
 def draw_down(w: Workload, seed: int):

@@ -38,8 +38,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version():
     # version 2 added m3_dims.disc (the discretisation rule); version 3 the
-    # gated entry points and m3_gate
-    assert B.m3_abi_version() == 3
+    # gated entry points and m3_gate; version 4 m3_bcnorm and the _ex calls
+    assert B.m3_abi_version() == 4
 
 
 def test_dims_struct_matches_header():
@@ -253,3 +253,66 @@ def test_gated_prefill_needs_the_producer_consumer_kernel():
 
 def test_gated_zero_seqlen_is_a_noop():
     assert call_prefill_gated(dims(), B.m3_gate(FAKE, FAKE, 0.0), seqlen=0, ptrs=[None] * 9) == B.M3_OK
+
+
+# ---------------------------------------------------------------------------
+# _ex entry points (BC normalisation + optional epilogue)
+# ---------------------------------------------------------------------------
+
+def test_bcnorm_struct_matches_header():
+    hdr = open(HEADER).read()
+    body = re.search(r"typedef struct \{([^}]*)\} m3_bcnorm;", hdr).group(1)
+    names = re.findall(r"(\w+)\s*;", body)
+    assert names == [f for f, _ in B.m3_bcnorm._fields_]
+    assert ctypes.sizeof(B.m3_bcnorm) == 24
+
+
+def call_prefill_ex(d, bc, gate=None, seqlen=16, ptrs=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return B.lib().mamba3_prefill_ex(ctypes.byref(d), seqlen, *p[:8], None if bc is None else ctypes.byref(bc),
+                                     None if gate is None else ctypes.byref(gate), ctypes.byref(fake_state()), p[8],
+                                     None, 0, None)
+
+
+def call_decode_ex(d, bc, gate=None, ptrs=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return B.lib().mamba3_decode_step_ex(ctypes.byref(d), *p[:8], None if bc is None else ctypes.byref(bc),
+                                         None if gate is None else ctypes.byref(gate), ctypes.byref(fake_state()),
+                                         p[8], None)
+
+
+@pytest.mark.parametrize("call", [call_prefill_ex, call_decode_ex])
+def test_bcnorm_argument_checks(call):
+    d = dims()
+    assert call(d, B.m3_bcnorm(None, FAKE, 1e-6)) == B.M3_ERR_NULL
+    assert call(d, B.m3_bcnorm(FAKE, None, 1e-6)) == B.M3_ERR_NULL
+    assert call(d, B.m3_bcnorm(FAKE + 4, FAKE, 1e-6)) == B.M3_ERR_ALIGN
+    assert call(d, B.m3_bcnorm(FAKE, FAKE + 8, 1e-6)) == B.M3_ERR_ALIGN
+    assert call(d, B.m3_bcnorm(FAKE, FAKE, -1.0)) == B.M3_ERR_SHAPE
+    assert call(d, B.m3_bcnorm(FAKE, FAKE, float("nan"))) == B.M3_ERR_SHAPE
+    assert "bcnorm.eps" in B.m3_last_error()
+    # the gate is still checked, and the other arguments
+    assert call(d, B.m3_bcnorm(FAKE, FAKE, 0.0), B.m3_gate(None, FAKE, 0.0)) == B.M3_ERR_NULL
+    p = [FAKE] * 9
+    p[1] = None
+    assert call(d, B.m3_bcnorm(FAKE, FAKE, 0.0), ptrs=p) == B.M3_ERR_NULL
+
+
+def test_prefill_ex_without_options_is_the_plain_call():
+    d = dims()
+    assert call_prefill_ex(d, None, seqlen=0, ptrs=[None] * 9) == B.M3_OK
+    assert call_prefill_ex(dims(dstate=15), None) == B.M3_ERR_UNSUPPORTED
+
+
+def test_bcnorm_prefill_support():
+    ok = B.m3_bcnorm(FAKE, FAKE, 1e-6)
+    # served: every bf16 shape of the headline families, with and without a gate
+    for r, n, c in ((1, 128, 64), (2, 128, 64), (4, 64, 64), (4, 128, 32)):
+        assert call_prefill_ex(dims(rank=r, dstate=n, chunk=c), ok, seqlen=0) == B.M3_OK
+        assert call_prefill_ex(dims(rank=r, dstate=n, chunk=c), ok, B.m3_gate(FAKE, FAKE, 0.0), seqlen=0) == B.M3_OK
+    # bf16 N = 64, P = 16: the norm's partial sums do not fit beside the tiles
+    assert call_prefill_ex(dims(dstate=64, headdim=16), ok, seqlen=0) == B.M3_ERR_UNSUPPORTED
+    assert call_prefill_ex(dims(dstate=64, headdim=16), None, seqlen=0) == B.M3_OK
+    # fp32 shapes that only the single-role kernel serves
+    assert call_prefill_ex(dims(io_dtype="f32", dstate=128, headdim=128, rank=2, chunk=16), ok,
+                           seqlen=0) == B.M3_ERR_UNSUPPORTED

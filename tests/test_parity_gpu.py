@@ -503,3 +503,181 @@ def test_decode_down_full_size_sampled():
     rng = np.random.default_rng(12)
     pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(16)]
     check_decode_gated(w, seed=1350, pairs=pairs, down=True)
+
+
+# ---------------------------------------------------------------------------
+# BC normalisation in the prep (mamba3_prefill_ex / mamba3_decode_step_ex),
+# alone and with the epilogue, against the oracle run on bc_rmsnorm'd B and C
+# (the pending B_prev stays raw in the state and is normalised at its use)
+# ---------------------------------------------------------------------------
+
+BC_EPS = 1e-6
+
+
+def bcnorm_on_gpu(w, seed):
+    gb, gc = syn.draw_bcnorm(w, seed)
+    gb, gc = syn.round_io(gb, "f32"), syn.round_io(gc, "f32")
+    return gb, gc, to_gpu(gb, "f32", "wb"), to_gpu(gc, "f32", "wc")
+
+
+def check_prefill_ex(w, seed, epi="plain", st=None, pairs=None, disc=0, eps_bc=BC_EPS):
+    ex, tt = inputs_on_gpu(w, seed)
+    gb, gc, gbt, gct = bcnorm_on_gpu(w, seed + 8000)
+    down = epi == "down"
+    gate = None
+    if epi != "plain":
+        z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 7000, folded=down)
+        dw_ex, dwt = down_on_gpu(w, seed + 7100) if down else (None, None)
+        gate = (zt, gwt, 1e-5) + ((dwt,) if down else ())
+    s = make_state(w, st)
+    d = dims_of(w, disc)
+    T = w.seqlen
+    yshape = (w.batch, T, w.heads, w.headdim) if down else (w.batch, T, w.heads, w.rank, w.headdim)
+    y = torch.empty(yshape, dtype=tt["x"].dtype, device="cuda")
+    nws = m3.mamba3_prefill_workspace_bytes(d, T)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    m3.mamba3_prefill_ex(d, T, tt["x"], tt["B"], tt["C"], tt["dt"], tt["lam"], tt["theta"], tt["A"], tt["D"], s, y,
+                         bcnorm=(gbt, gct, eps_bc), gate=gate, workspace=ws)
+    torch.cuda.synchronize()
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    st_ex = exact_state(st, w.io_dtype) if st is not None else oracle.zero_state(
+        w.batch, w.heads, w.headdim, w.dstate, w.rank)
+    args = oracle_args(ex, pairs)
+    args["Bm"] = oracle.bc_rmsnorm(args["Bm"], gb[hs], eps_bc)
+    args["Cm"] = oracle.bc_rmsnorm(args["Cm"], gc[hs], eps_bc)
+    h0, bp0, xp0 = state_slice(st_ex, pairs)
+    bp0 = oracle.bc_rmsnorm(bp0, gb[hs], eps_bc)
+    y_ref, (h_ref, _, xp_ref) = oracle.prefill(**args, state=(h0, bp0, xp0), disc=disc)
+    if epi == "gate":
+        y_ref = oracle.gated_rmsnorm(y_ref, np.moveaxis(z_ex[bs, :, hs], 0, 1)[None], gw_ex[hs], 1e-5)
+    elif down:
+        folded = oracle.rank_down_projection(y_ref, dw_ex[hs])[..., None, :]
+        zs = np.moveaxis(z_ex[bs, :, hs], 0, 1)[None][..., None, :]
+        y_ref = oracle.gated_rmsnorm(folded, zs, gw_ex[hs], 1e-5)[..., 0, :]
+    y_gpu = np.moveaxis(to_np(y)[bs, :, hs], 0, 1)[None]
+    tol = tol_for(w.io_dtype)
+    ey = relerr(y_gpu, y_ref)
+    eh = relerr(to_np(s.h)[bs, hs][None], h_ref)
+    print(f"[bcnorm {epi} {w.name} seed={seed} T={T} Q={w.chunk}] rel-L2 y={ey:.3e} h={eh:.3e}", flush=True)
+    assert ey <= tol, ey
+    assert eh <= tol, eh
+    # the pending pair is the raw last token
+    assert np.array_equal(to_np(s.B_prev)[bs, hs][None], ex["B"][bs, T - 1, hs][None])
+    assert np.array_equal(to_np(s.x_prev)[bs, hs][None], xp_ref)
+
+
+@pytest.mark.parametrize("io,P,N,R,T,Q", [
+    ("f32", 16, 16, 1, 64, 16),
+    ("bf16", 64, 128, 1, 200, 64),   # the headline family, ragged tail
+    ("bf16", 64, 64, 4, 130, 64),    # MIMO rank 4: 16-token tiles
+    ("f32", 32, 32, 2, 100, 32),
+    ("bf16", 128, 32, 1, 96, 32),
+    ("f32", 64, 128, 1, 70, 16),     # 16 pair groups per row over the producer waves
+])
+def test_prefill_bcnorm_shapes(io, P, N, R, T, Q):
+    w = W("tiny_siso_f32", batch=2, heads=3, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=T, chunk=Q)
+    check_prefill_ex(w, seed=1400 + P + N + R + T)
+
+
+def test_prefill_bcnorm_state_and_eps():
+    """A non-zero entry state (its raw pending B_prev normalised at use) and a
+    large eps."""
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=32, dstate=64, rank=2, io_dtype="f32", seqlen=77, chunk=32)
+    check_prefill_ex(w, seed=1450, st=syn.draw_state(w, 1451), eps_bc=0.5)
+
+
+@pytest.mark.parametrize("epi", ["gate", "down"])
+def test_prefill_bcnorm_with_epilogue(epi):
+    w = W("tiny_siso_f32", batch=2, heads=3, headdim=64, dstate=64, rank=4, io_dtype="bf16", seqlen=100, chunk=64)
+    check_prefill_ex(w, seed=1460, epi=epi, st=syn.draw_state(w, 1461))
+
+
+def test_prefill_bcnorm_segment_path():
+    w = W("tiny_siso_f32", batch=1, heads=2, headdim=64, dstate=128, rank=1, io_dtype="bf16", seqlen=64 * 40,
+          chunk=64)
+    assert m3.mamba3_prefill_workspace_bytes(dims_of(w), w.seqlen) > 0
+    check_prefill_ex(w, seed=1470, st=syn.draw_state(w, 1471))
+
+
+@pytest.mark.parametrize("disc", [1, 2])
+def test_prefill_bcnorm_discretisation_rules(disc):
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=32, dstate=32, rank=1, io_dtype="f32", seqlen=90, chunk=32)
+    check_prefill_ex(w, seed=1480 + disc, disc=disc)
+
+
+def test_prefill_bcnorm_full_size_sampled():
+    w = syn.WORKLOADS["siso_1p5b_t4096"]
+    rng = np.random.default_rng(9)
+    chains = sorted({(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(3)})
+    check_prefill_ex(w, seed=1490, pairs=chains, epi="gate")
+
+
+def check_decode_ex(w, seed, epi="plain", steps=2, pairs=None, eps_bc=BC_EPS):
+    d = dims_of(w)
+    st0 = syn.draw_state(w, seed + 500)
+    s = make_state(w, st0)
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    bs = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    h, bp_raw, xp = state_slice(exact_state(st0, w.io_dtype), pairs)
+    gb, gc, gbt, gct = bcnorm_on_gpu(w, seed + 9)
+    ex, tt = inputs_on_gpu(w, seed, seqlen=steps)
+    tol = tol_for(w.io_dtype)
+    down = epi == "down"
+    dw_ex, dwt = down_on_gpu(w, seed + 3) if down else (None, None)
+    for k in range(steps):
+        gate = None
+        if epi != "plain":
+            z_ex, gw_ex, zt, gwt = gate_on_gpu(w, seed + 100 * k + 7, decode=True, folded=down)
+            gate = (zt, gwt, 1e-5) + ((dwt,) if down else ())
+        tok = {key: (v[:, k].contiguous() if v.dim() >= 3 else v) for key, v in tt.items()}
+        yshape = (w.batch, w.heads, w.headdim) if down else (w.batch, w.heads, w.rank, w.headdim)
+        y = torch.empty(yshape, dtype=tt["x"].dtype, device="cuda")
+        m3.mamba3_decode_step_ex(d, tok["x"], tok["B"], tok["C"], tok["dt"], tok["lam"], tok["theta"], tok["A"],
+                                 tok["D"], s, y, bcnorm=(gbt, gct, eps_bc), gate=gate)
+        torch.cuda.synchronize()
+        args = oracle_args(ex, pairs)
+        Braw = args["Bm"][:, k]
+        y_ref, (h, _, xp) = oracle.decode_step(args["x"][:, k], oracle.bc_rmsnorm(Braw, gb[hs], eps_bc),
+                                               oracle.bc_rmsnorm(args["Cm"][:, k], gc[hs], eps_bc), args["dt"][:, k],
+                                               args["lam"][:, k], args["theta"][:, k], args["A"], args["D"],
+                                               (h, oracle.bc_rmsnorm(bp_raw, gb[hs], eps_bc), xp))
+        bp_raw = Braw
+        if epi == "gate":
+            y_ref = oracle.gated_rmsnorm(y_ref, z_ex[bs, hs][None], gw_ex[hs], 1e-5)
+        elif down:
+            folded = oracle.rank_down_projection(y_ref, dw_ex[hs])[..., None, :]
+            y_ref = oracle.gated_rmsnorm(folded, z_ex[bs, hs][None][..., None, :], gw_ex[hs], 1e-5)[..., 0, :]
+        ey = relerr(to_np(y)[bs, hs][None], y_ref)
+        eh = relerr(to_np(s.h)[bs, hs][None], h)
+        print(f"[bcnorm {epi} decode {w.name} step {k}] rel-L2 y={ey:.3e} h={eh:.3e}", flush=True)
+        assert ey <= tol and eh <= tol, (ey, eh)
+        assert np.array_equal(to_np(s.B_prev)[bs, hs][None], bp_raw)
+        assert np.array_equal(to_np(s.x_prev)[bs, hs][None], xp)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("P,N,R", [(16, 16, 1), (64, 128, 1), (128, 128, 1), (32, 32, 2), (64, 64, 4),
+                                   (128, 64, 4)])
+def test_decode_bcnorm(io, P, N, R):
+    w = W("tiny_siso_f32", batch=3, heads=4, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=1)
+    check_decode_ex(w, seed=1500 + P + N + R)
+
+
+@pytest.mark.parametrize("epi", ["gate", "down"])
+@pytest.mark.parametrize("R,N", [(1, 128), (4, 64)])
+def test_decode_bcnorm_with_epilogue(epi, R, N):
+    w = W("tiny_siso_f32", batch=3, heads=4, headdim=64, dstate=N, rank=R, io_dtype="bf16", seqlen=1)
+    check_decode_ex(w, seed=1550 + R, epi=epi)
+
+
+@pytest.mark.parametrize("name", ["decode_mimo_r4_n64", "decode_siso_n128"])
+def test_decode_bcnorm_full_size_sampled(name):
+    w = syn.WORKLOADS[name]
+    rng = np.random.default_rng(13)
+    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(16)]
+    check_decode_ex(w, seed=1590, pairs=pairs, epi="gate")
