@@ -115,6 +115,25 @@ template <typename IO> struct Raw8 {
       for (int k = 0; k < 8; ++k) o[k] = __uint_as_float(w[k]);
     }
   }
+  // Sum of the squares of the 8 elements, straight from the raw words (bf16:
+  // v_dot2c_f32_bf16 on each pair, exact products, fp32 sums), so no
+  // unpacked copies are formed that the compiler could keep alive for a
+  // later unpack of the same registers.
+  __device__ __forceinline__ float sumsq() const {
+    float s = 0.f;
+    if constexpr (sizeof(IO) == 2) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w[k]);
+        s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s = fmaf(__uint_as_float(w[k]), __uint_as_float(w[k]), s);
+    }
+    return s;
+  }
 };
 
 

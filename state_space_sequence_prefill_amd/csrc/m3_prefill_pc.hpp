@@ -345,20 +345,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           float pb[4], pc[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            float v[8];
-            rs.b[m][k].unpack(v);
-            float sb = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sb += v[e] * v[e];
-            pb[k] = lane_group_sum(sb, GW);
-            pc[k] = 0.f;
-            if (has_y) {  // segment summaries never read C
-              rs.c[m][k].unpack(v);
-              float sc = 0.f;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) sc += v[e] * v[e];
-              pc[k] = lane_group_sum(sc, GW);
-            }
+            pb[k] = lane_group_sum(rs.b[m][k].sumsq(), GW);
+            // segment summaries never read C
+            pc[k] = has_y ? lane_group_sum(rs.c[m][k].sumsq(), GW) : 0.f;
           }
           if (ist[m] && (lane & (GW - 1)) == 0) {
             const int grp = ipg[m] / GW;
