@@ -42,6 +42,14 @@ struct MimoLds {
   __host__ __device__ static constexpr size_t bytes(int P) {
     return raw_bytes(P) + (size_t)N * 4 + (size_t)4 * kKG * N * 4 + (size_t)4 * kKG * P * 4 + (size_t)R * N * 4;
   }
+  // state staging: the P x N fp32 state passes through LDS (rows padded by 4
+  // floats) between coalesced HBM runs and the MFMA lane layout
+  static constexpr int kLdSt = N + 4;
+  __host__ __device__ static constexpr size_t stage_bytes(int P) { return (size_t)P * kLdSt * 4; }
+  // everything: derived operands, 16 floats of BC-norm scales, staging, gated outputs
+  __host__ __device__ static constexpr size_t total_bytes(int P, bool gated) {
+    return bytes(P) + 64 + stage_bytes(P) + (gated ? (size_t)R * P * 4 : 0);
+  }
 };
 constexpr int kMimoMaxGranulesPerThread = 3;
 
@@ -62,7 +70,15 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   const IO* Cc_ = static_cast<const IO*>(a.C) + (size_t)head * R * N;
   IO* Bp_ = static_cast<IO*>(a.B_prev) + (size_t)head * R * N;
   IO* xp_ = static_cast<IO*>(a.x_prev) + (size_t)head * R * P;
-  float* hrow = a.h + (size_t)head * P * N + (size_t)(16 * pb + c) * N + 4 * g;
+  // this wave's 16 state rows are 16 N contiguous floats: they move between
+  // HBM and the LDS staging rows in whole 1 KiB runs (lane l, run j: float4
+  // l + 64 j), and between staging and registers in the MFMA layout
+  float* const hwave = a.h + (size_t)head * P * N + (size_t)(16 * pb) * N;
+  float* const sSt = reinterpret_cast<float*>(dsm + L::bytes(P) + 64) + (size_t)(16 * pb) * L::kLdSt;
+  auto stage_off = [&](int j) {  // staging offset of float4 lane + 64 j of the wave's rows
+    const int f = lane + 64 * j;
+    return (f / (N / 4)) * L::kLdSt + 4 * (f % (N / 4));
+  };
 
   // ---- 1. operand granules, then the state tiles (vmcnt retires in order:
   //         the wait below covers the operands, the state stays in flight)
@@ -97,7 +113,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   __builtin_amdgcn_sched_barrier(0);
   float4 hv[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) hv[nb] = *reinterpret_cast<const float4*>(hrow + 16 * nb);
+  for (int j = 0; j < NB; ++j) hv[j] = *reinterpret_cast<const float4*>(hwave + 4 * (lane + 64 * j));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < KG; ++k) {
@@ -138,6 +154,9 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
     }
     __syncthreads();
   }
+  // the state runs into the staging rows (visible after the next barrier)
+#pragma unroll
+  for (int j = 0; j < NB; ++j) *reinterpret_cast<float4*>(sSt + stage_off(j)) = hv[j];
   const float* nwB = bcn ? a.nbw + (size_t)hh * N : nullptr;
   const float* nwC = bcn ? a.ncw + (size_t)hh * N : nullptr;
 
@@ -185,6 +204,9 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
 #pragma unroll
   for (int q = 0; q < kKG; ++q) bx[q] = sXk[(4 * q + g) * P + 16 * pb + c];
   f32x4m yacc = {0.f, 0.f, 0.f, 0.f};
+  // lane (g, c) of tile nb: state row 16 pb + c, columns 16 nb + 4 g .. + 3
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) hv[nb] = *reinterpret_cast<const float4*>(sSt + c * L::kLdSt + 16 * nb + 4 * g);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float4 cs = *reinterpret_cast<const float4*>(sCS + 8 * nb + 2 * g);  // pairs 8nb+2g, +1
@@ -195,7 +217,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
 #pragma unroll
     for (int q = 0; q < kKG; ++q)
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sBk[(4 * q + g) * N + 16 * nb + c], bx[q], acc, 0, 0, 0);
-    *reinterpret_cast<float4*>(hrow + 16 * nb) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(sSt + c * L::kLdSt + 16 * nb + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     // readout: K index g <-> n = 16nb + 4g + i for the i-th product
     float4 cr = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < R) cr = *reinterpret_cast<const float4*>(sCf + c * N + 16 * nb + 4 * g);
@@ -204,9 +226,14 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
     yacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cr.z, acc[2], yacc, 0, 0, 0);
     yacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cr.w, acc[3], yacc, 0, 0, 0);
   }
+  // the new state leaves the staging rows in whole runs
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    *reinterpret_cast<float4*>(hwave + 4 * (lane + 64 * j)) = *reinterpret_cast<const float4*>(sSt + stage_off(j));
   // ---- 4. y: lanes g = 0 hold Y^T[r = i][p = 16pb + c] for r < R
-  //         (gated: the fp32 outputs go to LDS behind the derived operands)
-  float* const sYg = reinterpret_cast<float*>(dsm + L::bytes(P) + 64);
+  //         (gated: the fp32 outputs go to LDS behind the staging rows)
+  float* const sYg = reinterpret_cast<float*>(dsm + L::bytes(P) + 64 + L::stage_bytes(P));
   if (g == 0) {
     IO* y = static_cast<IO*>(a.y) + (size_t)head * R * P + 16 * pb + c;
 #pragma unroll
@@ -237,8 +264,16 @@ template <typename IO, int N, int R>
 hipError_t launch_mimo_t(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   const int waves = d.P / 16;
   const dim3 grid(d.batch * d.heads), block(waves * kWave);
-  // derived operands, then 16 floats of BC-norm scales, then the gated outputs
-  const size_t lds = MimoLds<IO, N, R>::bytes(d.P) + 64 + (a.gz ? (size_t)R * d.P * sizeof(float) : 0);
+  const size_t lds = MimoLds<IO, N, R>::total_bytes(d.P, a.gz != nullptr);
+  static bool attr_set = false;
+  if (!attr_set) {
+    for (const void* f : {reinterpret_cast<const void*>(&decode_mimo_kernel<IO, N, R, 1>),
+                          reinterpret_cast<const void*>(&decode_mimo_kernel<IO, N, R, kMimoMaxGranulesPerThread>)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+    }
+    attr_set = true;
+  }
   if (MimoLds<IO, N, R>::granules(d.P) <= waves * kWave)
     hipLaunchKernelGGL((decode_mimo_kernel<IO, N, R, 1>), grid, block, lds, s, a, d.heads, d.P);
   else
