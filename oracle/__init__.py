@@ -9,3 +9,4 @@ from .mamba3_oracle import (  # noqa: F401
     EXP_TRAPEZOID, DECAYED_TRAPEZOID, EXP_EULER, gated_rmsnorm, rank_down_projection,
     bc_rmsnorm,
 )
+from .mamba3_backward import prefill_backward, forward_torch  # noqa: F401
