@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 4
+#define M3_ABI_VERSION 5
 
 typedef enum {
   M3_OK = 0,
@@ -249,6 +249,45 @@ int mamba3_prefill_ex(const m3_dims* dims, int32_t seqlen, const void* x, const 
 int mamba3_decode_step_ex(const m3_dims* dims, const void* x, const void* B, const void* C, const float* dt,
                           const float* lam, const float* theta, const float* A, const float* D,
                           const m3_bcnorm* bcnorm, const m3_gate* gate, m3_state* state, void* y, void* stream);
+
+/* Backward pass of mamba3_prefill (training): the gradients of
+ *   L = sum_t <dy_t, y_t> + <dh_final, h_T>
+ * with respect to every input of a prefill that started from `state0`
+ * (lilting.ch Mamba-3 article, "アーキテクチャ改善" 1-3; the exact derivative
+ * of the recurrence that mamba3_prefill computes, under dims->disc).  All
+ * gradients are fp32 device arrays in the layouts of the quantities they
+ * belong to; dA and dD are summed over the batch.  The pending pair of the
+ * final state is a copy of the last token's (B, x): a caller with cotangents
+ * for it adds them to dB and dx of that token. */
+typedef struct {
+  float* dx;       /* (batch, seqlen, heads, R, P) */
+  float* dB;       /* (batch, seqlen, heads, R, N) */
+  float* dC;       /* (batch, seqlen, heads, R, N) */
+  float* ddt;      /* (batch, seqlen, heads) */
+  float* dlam;     /* (batch, seqlen, heads) */
+  float* dtheta;   /* (batch, seqlen, heads, N/2) */
+  float* dA;       /* (heads) */
+  float* dD;       /* (heads) */
+  float* dh0;      /* (batch, heads, P, N): of state0.h */
+  float* dB_prev;  /* (batch, heads, R, N): of state0.B_prev */
+  float* dx_prev;  /* (batch, heads, R, P): of state0.x_prev */
+} m3_grads;
+
+/* Workspace of mamba3_prefill_backward: the state's entry value at every
+ * sub-chunk of 16 / R tokens plus per-chain partial sums,
+ * batch * heads * (ceil(seqlen R / 16) + 1) * P * N * 4 bytes and a little. */
+int mamba3_prefill_backward_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* bytes);
+
+/* x, B, C, dt, lam, theta, A, D as given to mamba3_prefill; state0 the state
+ * the prefill started from (read only); dy (io dtype, y's layout) the
+ * cotangent of y; dh_final (fp32 (batch, heads, P, N)) that of the final h,
+ * or NULL for zero.  dims->chunk is ignored.  Errors as mamba3_prefill, plus
+ * M3_ERR_NULL / M3_ERR_ALIGN for grads and its arrays, M3_ERR_UNSUPPORTED for
+ * P * N > 8192, and M3_ERR_WORKSPACE for a short workspace. */
+int mamba3_prefill_backward(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                            const float* dt, const float* lam, const float* theta, const float* A,
+                            const float* D, const m3_state* state0, const void* dy, const float* dh_final,
+                            const m3_grads* grads, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

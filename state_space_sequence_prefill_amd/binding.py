@@ -36,7 +36,10 @@ EXPORTED = (
     "m3_abi_version", "m3_last_error", "m3_state_bytes", "m3_state_zero", "m3_state_load",
     "m3_state_readout", "mamba3_prefill_workspace_bytes", "mamba3_prefill", "mamba3_decode_step",
     "mamba3_prefill_gated", "mamba3_decode_step_gated", "mamba3_prefill_ex", "mamba3_decode_step_ex",
+    "mamba3_prefill_backward_workspace_bytes", "mamba3_prefill_backward",
 )
+
+GRAD_FIELDS = ("dx", "dB", "dC", "ddt", "dlam", "dtheta", "dA", "dD", "dh0", "dB_prev", "dx_prev")
 
 
 class M3Error(RuntimeError):
@@ -62,6 +65,10 @@ class m3_gate(ctypes.Structure):
 
 class m3_bcnorm(ctypes.Structure):
     _fields_ = [("b_weight", ctypes.c_void_p), ("c_weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+class m3_grads(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in GRAD_FIELDS]
 
 
 _lib = None
@@ -100,6 +107,11 @@ def lib():
         L.mamba3_prefill_gated.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, G, S, vp, vp, sz, vp]
         L.mamba3_decode_step_gated.restype = ctypes.c_int
         L.mamba3_decode_step_gated.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, G, S, vp, vp]
+        L.mamba3_prefill_backward_workspace_bytes.restype = ctypes.c_int
+        L.mamba3_prefill_backward_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(sz)]
+        L.mamba3_prefill_backward.restype = ctypes.c_int
+        L.mamba3_prefill_backward.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp,
+                                              ctypes.POINTER(m3_grads), vp, sz, vp]
         L.mamba3_prefill_ex.restype = ctypes.c_int
         L.mamba3_prefill_ex.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, NB, G, S, vp, vp, sz, vp]
         L.mamba3_decode_step_ex.restype = ctypes.c_int
@@ -373,3 +385,37 @@ def mamba3_decode_step_ex(dims, x, B, C, dt, lam, theta, A, D, state, y, bcnorm=
     _check(lib().mamba3_decode_step_ex(ctypes.byref(dims), *args, None if nb is None else ctypes.byref(nb),
                                        None if g is None else ctypes.byref(g), ctypes.byref(cs), py,
                                        _stream(stream)))
+
+
+def mamba3_prefill_backward_workspace_bytes(dims, seqlen):
+    n = ctypes.c_size_t()
+    _check(lib().mamba3_prefill_backward_workspace_bytes(ctypes.byref(dims), int(seqlen), ctypes.byref(n)))
+    return n.value
+
+
+def grad_shapes(dims, seqlen):
+    """Shapes of the fp32 gradient arrays mamba3_prefill_backward writes."""
+    d, T = dims, int(seqlen)
+    b, H, R, P, N = d.batch, d.heads, d.rank, d.headdim, d.dstate
+    return {"dx": (b, T, H, R, P), "dB": (b, T, H, R, N), "dC": (b, T, H, R, N), "ddt": (b, T, H),
+            "dlam": (b, T, H), "dtheta": (b, T, H, N // 2), "dA": (H,), "dD": (H,), "dh0": (b, H, P, N),
+            "dB_prev": (b, H, R, N), "dx_prev": (b, H, R, P)}
+
+
+def mamba3_prefill_backward(dims, seqlen, x, B, C, dt, lam, theta, A, D, state0, dy, grads, dh_final=None,
+                            workspace=None, stream=None):
+    """Gradients of <dy, y> + <dh_final, h_T> for a prefill from `state0`
+    (State, read only).  `grads` is a dict of fp32 GPU tensors with the shapes
+    grad_shapes(dims, seqlen) gives; `workspace` a uint8 GPU tensor of at least
+    mamba3_prefill_backward_workspace_bytes(dims, seqlen) bytes."""
+    torch = _torch()
+    d = dims
+    args, _ = _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, None)
+    pdy = _ptr(dy, "dy", (d.batch, int(seqlen), d.heads, d.rank, d.headdim), _io_torch_dtype(d))
+    pdh = _ptr(dh_final, "dh_final", (d.batch, d.heads, d.headdim, d.dstate), torch.float32)
+    shapes = grad_shapes(dims, seqlen)
+    g = m3_grads(*(_ptr(grads[f], f, shapes[f], torch.float32) for f in GRAD_FIELDS))
+    ws, wsb = _workspace(workspace)
+    cs = state0.c_struct()
+    _check(lib().mamba3_prefill_backward(ctypes.byref(d), int(seqlen), *args, ctypes.byref(cs), pdy, pdh,
+                                         ctypes.byref(g), ws, wsb, _stream(stream)))

@@ -434,5 +434,81 @@ int mamba3_decode_step_ex(const m3_dims* dims, const void* x, const void* B, con
                      "mamba3_decode_step_ex");
 }
 
+int mamba3_prefill_backward_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* bytes) {
+  m3::Dims m;
+  int st = check_dims(dims, false, &m);
+  if (st != M3_OK) return st;
+  if (!bytes) return fail(M3_ERR_NULL, "bytes is NULL");
+  if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
+  if (!m3::backward_supported(m))
+    return fail(M3_ERR_UNSUPPORTED, "the backward pass needs headdim * dstate <= 8192 (got %d)", m.P * m.N);
+  *bytes = seqlen > 0 ? m3::backward_workspace_bytes(m, seqlen) : 0;
+  return ok();
+}
+
+int mamba3_prefill_backward(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                            const float* dt, const float* lam, const float* theta, const float* A,
+                            const float* D, const m3_state* state0, const void* dy, const float* dh_final,
+                            const m3_grads* grads, void* workspace, size_t workspace_bytes, void* stream) {
+  m3::Dims m;
+  int st = check_dims(dims, false, &m);
+  if (st != M3_OK) return st;
+  if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
+  if (!m3::backward_supported(m))
+    return fail(M3_ERR_UNSUPPORTED, "the backward pass needs headdim * dstate <= 8192 (got %d)", m.P * m.N);
+  if (!state0) return fail(M3_ERR_NULL, "state0 is NULL");
+  if ((st = check_ptr(state0->h, "state0.h")) != M3_OK) return st;
+  if ((st = check_ptr(state0->B_prev, "state0.B_prev")) != M3_OK) return st;
+  if ((st = check_ptr(state0->x_prev, "state0.x_prev")) != M3_OK) return st;
+  if (!grads) return fail(M3_ERR_NULL, "grads is NULL");
+  const void* gp[] = {grads->dx, grads->dB, grads->dC, grads->ddt, grads->dlam, grads->dtheta,
+                      grads->dA, grads->dD, grads->dh0, grads->dB_prev, grads->dx_prev};
+  const char* gn[] = {"grads.dx", "grads.dB", "grads.dC", "grads.ddt", "grads.dlam", "grads.dtheta",
+                      "grads.dA", "grads.dD", "grads.dh0", "grads.dB_prev", "grads.dx_prev"};
+  for (int i = 0; i < 11; ++i)
+    if ((st = check_ptr(gp[i], gn[i])) != M3_OK) return st;
+  if (dh_final && (st = check_ptr(dh_final, "dh_final")) != M3_OK) return st;
+  if (seqlen == 0) return fail(M3_ERR_SHAPE, "seqlen 0: there is nothing to differentiate");
+  const void* ptrs[] = {x, B, C, dt, lam, theta, A, D, dy};
+  const char* names[] = {"x", "B", "C", "dt", "lam", "theta", "A", "D", "dy"};
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_ptr(ptrs[i], names[i])) != M3_OK) return st;
+  const size_t need = m3::backward_workspace_bytes(m, seqlen);
+  if (workspace_bytes < need)
+    return fail(M3_ERR_WORKSPACE, "workspace of %zu bytes < required %zu", workspace_bytes, need);
+  if ((st = check_ptr(workspace, "workspace")) != M3_OK) return st;
+  m3::BackwardArgs a;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt = dt;
+  a.lam = lam;
+  a.theta = theta;
+  a.A = A;
+  a.D = D;
+  a.h = state0->h;
+  a.B_prev = state0->B_prev;
+  a.x_prev = state0->x_prev;
+  a.dy = dy;
+  a.dh_final = dh_final;
+  a.dx = grads->dx;
+  a.dB = grads->dB;
+  a.dC = grads->dC;
+  a.ddt = grads->ddt;
+  a.dlam = grads->dlam;
+  a.dtheta = grads->dtheta;
+  a.dA = grads->dA;
+  a.dD = grads->dD;
+  a.dh0 = grads->dh0;
+  a.dB_prev = grads->dB_prev;
+  a.dx_prev = grads->dx_prev;
+  a.part = static_cast<float*>(workspace);
+  a.ckpt = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    align256((size_t)m.batch * m.heads * 2 * sizeof(float)));
+  a.seqlen = seqlen;
+  a.disc = m.disc;
+  return hip_status(m3::launch_backward(m, a, static_cast<hipStream_t>(stream)), "mamba3_prefill_backward");
+}
+
 }  // extern "C"
 

@@ -38,6 +38,38 @@ struct DecodeArgs {
   float neps;
 };
 
+// Arguments of the backward pass (mamba3_prefill_backward).
+struct BackwardArgs {
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* theta;
+  const float* A;
+  const float* D;
+  const float* h;        // entry state of the prefill (lab frame)
+  const void* B_prev;    // its pending pair
+  const void* x_prev;
+  const void* dy;        // cotangent of y (I/O dtype, y's layout)
+  const float* dh_final; // cotangent of the final h, or nullptr
+  float* dx;             // gradients, fp32, in the inputs' layouts
+  float* dB;
+  float* dC;
+  float* ddt;
+  float* dlam;
+  float* dtheta;
+  float* dA;             // (heads)
+  float* dD;             // (heads)
+  float* dh0;            // (batch, heads, P, N)
+  float* dB_prev;        // (batch, heads, R, N)
+  float* dx_prev;        // (batch, heads, R, P)
+  float* ckpt;           // workspace: sub-chunk entry values
+  float* part;           // workspace: per-chain dA, dD
+  int seqlen;
+  int disc;
+};
+
 // Arguments of one prefill pass over tokens [0, seqlen) of every chain.
 struct PrefillArgs {
   const void* x;
@@ -92,6 +124,10 @@ bool prefill_pc_supported(const Dims& d);
 // Whether the producer/consumer kernel serves these dims at some tile height:
 // the gated epilogue and the BC normalisation live only there.
 bool prefill_pc_path_supported(const Dims& d);
+// Backward pass (m3_backward.hip).
+bool backward_supported(const Dims& d);
+size_t backward_workspace_bytes(const Dims& d, int seqlen);
+hipError_t launch_backward(const Dims& d, const BackwardArgs& a, hipStream_t s);
 // Chunk length the prefill kernels tile with (<= d.Q; see m3_prefill.hip).
 int prefill_tile_chunk(const Dims& d);
 hipError_t launch_prefill_pc(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, int nblocks);

@@ -38,8 +38,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version():
     # version 2 added m3_dims.disc (the discretisation rule); version 3 the
-    # gated entry points and m3_gate; version 4 m3_bcnorm and the _ex calls
-    assert B.m3_abi_version() == 4
+    # gated entry points and m3_gate; version 4 m3_bcnorm and the _ex calls;
+    # version 5 the backward pass and m3_grads
+    assert B.m3_abi_version() == 5
 
 
 def test_dims_struct_matches_header():
@@ -316,3 +317,63 @@ def test_bcnorm_prefill_support():
     # fp32 shapes that only the single-role kernel serves
     assert call_prefill_ex(dims(io_dtype="f32", dstate=128, headdim=128, rank=2, chunk=16), ok,
                            seqlen=0) == B.M3_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+def test_grads_struct_matches_header():
+    hdr = open(HEADER).read()
+    body = re.search(r"typedef struct \{([^}]*)\} m3_grads;", hdr).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\*\s*(\w+)\s*;", body)
+    assert names == [f for f, _ in B.m3_grads._fields_] == list(B.GRAD_FIELDS)
+    assert ctypes.sizeof(B.m3_grads) == 11 * 8
+
+
+def call_backward(d, seqlen=32, ptrs=None, grads=None, ws=FAKE, wsb=1 << 40, dh=None, state=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    g = B.m3_grads(*([FAKE] * 11)) if grads is None else grads
+    st = fake_state() if state is None else state
+    return B.lib().mamba3_prefill_backward(ctypes.byref(d), seqlen, *p[:8], ctypes.byref(st), p[8], dh,
+                                           ctypes.byref(g), ws, wsb, None)
+
+
+def test_backward_workspace_size():
+    d = dims(batch=2, heads=3, headdim=64, dstate=128, rank=1)
+    n = B.mamba3_prefill_backward_workspace_bytes(d, 100)
+    assert n == 2 * 3 * (7 + 1) * 64 * 128 * 4 + 256   # 16-token sub-chunks
+    d4 = dims(batch=1, heads=1, headdim=64, dstate=64, rank=4)
+    assert B.mamba3_prefill_backward_workspace_bytes(d4, 9) == (3 + 1) * 64 * 64 * 4 + 256  # 4-token sub-chunks
+    assert B.mamba3_prefill_backward_workspace_bytes(d, 0) == 0
+
+
+def test_backward_argument_checks():
+    d = dims()
+    for i in range(11):
+        g = [FAKE] * 11
+        g[i] = None
+        assert call_backward(d, grads=B.m3_grads(*g)) == B.M3_ERR_NULL
+        g[i] = FAKE + 4
+        assert call_backward(d, grads=B.m3_grads(*g)) == B.M3_ERR_ALIGN
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert call_backward(d, ptrs=p) == B.M3_ERR_NULL
+    assert call_backward(d, dh=FAKE + 4) == B.M3_ERR_ALIGN
+    assert call_backward(d, wsb=16) == B.M3_ERR_WORKSPACE
+    assert call_backward(d, ws=None) == B.M3_ERR_NULL
+    assert call_backward(d, seqlen=0) == B.M3_ERR_SHAPE
+    assert call_backward(d, seqlen=-3) == B.M3_ERR_SHAPE
+    st = fake_state()
+    st.h = None
+    assert call_backward(d, state=st) == B.M3_ERR_NULL
+    assert B.lib().mamba3_prefill_backward(ctypes.byref(d), 8, *([FAKE] * 8), None, FAKE, None,
+                                           ctypes.byref(B.m3_grads(*([FAKE] * 11))), FAKE, 1 << 40,
+                                           None) == B.M3_ERR_NULL
+
+
+def test_backward_size_limit():
+    assert call_backward(dims(headdim=128, dstate=128)) == B.M3_ERR_UNSUPPORTED
+    assert "8192" in B.m3_last_error()
