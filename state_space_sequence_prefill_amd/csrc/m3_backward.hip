@@ -31,16 +31,16 @@
 namespace m3 {
 namespace {
 
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 512;
 constexpr int kRows = 16;  // (token, rank) rows per sub-chunk
 
 struct BwdLds {
   // floats
   static size_t bytes(int P, int N) {
     const size_t pn = (size_t)P * N;
-    return 4 * (2 * pn                   // E, G (then dE)
-                + (size_t)kRows * P * 3  // X, dY, G Bt
-                + (size_t)kRows * N * 5  // Bt, Ct, dBt, dCt, carried part of dCt
+    return 4 * (2 * pn + P               // E, G (then dE; rows padded by one)
+                + (size_t)kRows * P * 3 + kRows  // X (padded), dY, G Bt
+                + (size_t)kRows * N * 5 + kRows  // Bt (padded), Ct, dBt, dCt, carried part of dCt
                 + 4 * kRows * kRows      // S, Pm, M, dM
                 + (size_t)kRows * (N / 2) * 2  // phi, dphi
                 + (N / 2)                // dphi_end
@@ -50,7 +50,7 @@ struct BwdLds {
 };
 
 // per-token scalar slots (sTk[slot * 16 + t])
-enum { kA = 0, kAl, kBe, kGa, kL, kW, kEl, kDlc, kDw, kDga, kDbe, kDl, kNumTk };
+enum { kA = 0, kAl, kBe, kGa, kL, kW, kEl, kDlc, kDw, kDt, kLm, kNumTk };
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = lane_group_sum(v, kWave);
@@ -87,13 +87,16 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
   const int PN = P * N;
   const float Ah = a.A[hh], Dh = a.D[hh];
 
+  // rows of G, Bt and X are padded by one float: their column-wise reads (lanes
+  // over p or over rows) then fall in distinct banks
+  const int LDG = N + 1, LDB = N + 1, LDX = P + 1;
   float* sE = sm;
   float* sG = sE + PN;
-  float* sX = sG + PN;
-  float* sdY = sX + kRows * P;
+  float* sX = sG + P * LDG;
+  float* sdY = sX + kRows * LDX;
   float* sGB = sdY + kRows * P;
   float* sBt = sGB + kRows * P;
-  float* sCt = sBt + kRows * N;
+  float* sCt = sBt + kRows * LDB;
   float* sdBt = sCt + kRows * N;
   float* sdCt = sdBt + kRows * N;
   float* sCcar = sdCt + kRows * N;
@@ -126,58 +129,88 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
   const IO* Xp0 = static_cast<const IO*>(a.x_prev) + (size_t)chain * R * P;
   const float* h0 = a.h + (size_t)chain * PN;
 
+  // P x N fp32 between the workspace and LDS in 16-byte runs, all loads of a
+  // thread issued before their stores (a load per loop trip would wait for
+  // each one in turn)
+  constexpr int kMaxV = 8192 / 4 / kBwdThreads;  // float4s per thread at P N = 8192
+  auto ld_state = [&](float* dst, const float* src) {
+    float4 v[kMaxV];
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {  // clamped duplicates past the end, never stored
+      const int e = tid + i * kBwdThreads;
+      v[i] = reinterpret_cast<const float4*>(src)[e < PN / 4 ? e : PN / 4 - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {
+      const int e = tid + i * kBwdThreads;
+      if (e < PN / 4) reinterpret_cast<float4*>(dst)[e] = v[i];
+    }
+  };
+  auto st_state = [&](float* dst, const float* src) {
+#pragma unroll
+    for (int i = 0; i < kMaxV; ++i) {
+      const int e = tid + i * kBwdThreads;
+      if (e < PN / 4) reinterpret_cast<float4*>(dst)[e] = reinterpret_cast<const float4*>(src)[e];
+    }
+  };
+
   // ---- per-sub-chunk coefficients: token scalars, l, w, mask, angles ----
+  // (wave 0, lane t = token: decays, weights; every thread: angle loads)
   auto coefs = [&](int c) {
     const int t0 = c * Qb, L = min(Qb, T - t0);
     const bool nxt = t0 + L < T;
-    if (tid < L) {
-      const int t = t0 + tid;
-      const float dt = DTg[(size_t)t * H], lm = LMg[(size_t)t * H];
+    // the angles of the sub-chunk, all loads in flight together
+    for (int e = tid; e < Qb * NH; e += kBwdThreads) {
+      const int t = e / NH, j = e % NH;
+      sPhi[e] = t < L ? THg[(size_t)(t0 + t) * tokTh + j] : 0.f;
+    }
+    if (tid < kWave) {
+      const int t = tid;
+      const bool v = t < L;
+      // token t0 + L (the next one) in lane L: its decay and beta are folded in
+      const bool vn = t == L && nxt;
+      const int tg = t0 + (t < L ? t : L);
+      const float dt = (v || vn) ? DTg[(size_t)tg * H] : 0.f;
+      const float lm = (v || vn) ? LMg[(size_t)tg * H] : 0.f;
       const float al = expf(dt * Ah);
       const float2 bg = input_weights(dt, lm, al, a.disc);
-      sTk[kA * 16 + tid] = dt * Ah;
-      sTk[kAl * 16 + tid] = al;
-      sTk[kBe * 16 + tid] = bg.x;
-      sTk[kGa * 16 + tid] = bg.y;
-    }
-    if (tid == 0) {
-      float an = 0.f, bn = 0.f;
-      if (nxt) {
-        const float dt = DTg[(size_t)(t0 + L) * H], lm = LMg[(size_t)(t0 + L) * H];
-        an = dt * Ah;
-        bn = input_weights(dt, lm, expf(an), a.disc).x;
+      const float av = dt * Ah;
+      // l_t = sum_{0<s<=t} a_s over the sub-chunk
+      const float l = wave_inclusive_scan((v && t > 0) ? av : 0.f);
+      const float lE = __shfl(l, L - 1, kWave) + __shfl(av, L, kWave);  // (lane L holds 0 without a next token)
+      const float l_up = __shfl_down(l, 1, kWave);
+      const float be_up = __shfl_down(bg.x, 1, kWave);
+      if (v) {
+        float w = bg.y * expf(lE - l);
+        w += (t + 1 < L) ? be_up * expf(lE - l_up) : be_up;  // the next token's beta has weight e^{lE - lE}
+        sTk[kA * 16 + t] = av;
+        sTk[kDt * 16 + t] = dt;
+        sTk[kLm * 16 + t] = lm;
+        sTk[kAl * 16 + t] = al;
+        sTk[kBe * 16 + t] = bg.x;
+        sTk[kGa * 16 + t] = bg.y;
+        sTk[kL * 16 + t] = l;
+        sTk[kEl * 16 + t] = expf(l);
+        sTk[kW * 16 + t] = w;
       }
-      sMisc[1] = an;
-      sMisc[2] = bn;
-      sMisc[3] = nxt ? 1.f : 0.f;
+      if (t == L) {
+        sMisc[0] = lE;
+        sMisc[1] = vn ? av : 0.f;
+        sMisc[2] = vn ? bg.x : 0.f;
+        sMisc[3] = vn ? 1.f : 0.f;
+        sMisc[4] = dt;
+        sMisc[5] = lm;
+      }
     }
-    // angles: inclusive prefix over the sub-chunk's tokens, per pair
+    __syncthreads();
+    // inclusive angle prefix per pair; trapezoid mask over token pairs (q, k), k <= q
     for (int j = tid; j < NH; j += kBwdThreads) {
       float acc = 0.f;
       for (int t = 0; t < L; ++t) {
-        acc += THg[(size_t)(t0 + t) * tokTh + j];
+        acc += sPhi[t * NH + j];
         sPhi[t * NH + j] = acc;
       }
     }
-    __syncthreads();
-    if (tid == 0) {
-      float l = 0.f;
-      for (int t = 0; t < L; ++t) {
-        if (t > 0) l += sTk[kA * 16 + t];
-        sTk[kL * 16 + t] = l;
-        sTk[kEl * 16 + t] = expf(l);
-      }
-      const float lE = l + sMisc[1];
-      sMisc[0] = lE;
-      for (int k = 0; k < L; ++k) {
-        float w = sTk[kGa * 16 + k] * expf(lE - sTk[kL * 16 + k]);
-        if (k + 1 < L) w += sTk[kBe * 16 + k + 1] * expf(lE - sTk[kL * 16 + k + 1]);
-        else w += sMisc[2];  // beta of the next token (zero without one), weight e^{lE - lE}
-        sTk[kW * 16 + k] = w;
-      }
-    }
-    __syncthreads();
-    // trapezoid mask over token pairs (q, k), k <= q
     for (int e = tid; e < Qb * Qb; e += kBwdThreads) {
       const int q = e / Qb, k = e % Qb;
       float m = 0.f;
@@ -197,7 +230,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
       const int rho = e / P, p = e % P;
       const bool ok = rho < nr;
       const size_t o = (size_t)(t0 + rho / R) * tokX + (rho % R) * P + p;
-      sX[e] = ok ? to_f32(Xg[o]) : 0.f;
+      sX[rho * LDX + p] = ok ? to_f32(Xg[o]) : 0.f;
       if (with_c) sdY[e] = ok ? to_f32(dYg[o]) : 0.f;
     }
     for (int e = tid; e < kRows * NH; e += kBwdThreads) {
@@ -217,8 +250,8 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
           c1 = -u0 * sn + u1 * cs;
         }
       }
-      sBt[rho * N + 2 * j] = b0;
-      sBt[rho * N + 2 * j + 1] = b1;
+      sBt[rho * LDB + 2 * j] = b0;
+      sBt[rho * LDB + 2 * j + 1] = b1;
       if (with_c) {
         sCt[rho * N + 2 * j] = c0;
         sCt[rho * N + 2 * j + 1] = c1;
@@ -243,6 +276,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
     coefs(c);
     load_rows(c, false);
     __syncthreads();
+    st_state(ck + (size_t)c * PN, sE);
     const int L = min(Qb, T - c * Qb);
     const float elE = expf(sMisc[0]);
     // checkpoint, then E <- Rot(phi_end) [e^{lE} E + sum_rows w X (x) Bt]
@@ -250,14 +284,12 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
       const int p = e / NH, j = e % NH;
       const int i0 = p * N + 2 * j;
       float h0v = sE[i0], h1v = sE[i0 + 1];
-      ck[(size_t)c * PN + i0] = h0v;
-      ck[(size_t)c * PN + i0 + 1] = h1v;
       h0v *= elE;
       h1v *= elE;
       for (int rho = 0; rho < L * R; ++rho) {
-        const float wx = sTk[kW * 16 + rho / R] * sX[rho * P + p];
-        h0v += wx * sBt[rho * N + 2 * j];
-        h1v += wx * sBt[rho * N + 2 * j + 1];
+        const float wx = sTk[kW * 16 + rho / R] * sX[rho * LDX + p];
+        h0v += wx * sBt[rho * LDB + 2 * j];
+        h1v += wx * sBt[rho * LDB + 2 * j + 1];
       }
       float sn, cs;
       sincosf(sPhi[(L - 1) * NH + j], &sn, &cs);
@@ -266,47 +298,49 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
     }
     __syncthreads();
   }
-  // h_T (the last entry value's successor) in slot nsub; dE <- dh_final
-  for (int e = tid; e < PN; e += kBwdThreads) {
-    ck[(size_t)nsub * PN + e] = sE[e];
-    sG[e] = a.dh_final ? a.dh_final[(size_t)chain * PN + e] : 0.f;
-  }
+  // sE keeps h_T (the successor entry value of the last sub-chunk); dE <- dh_final
+  for (int e = tid; e < PN; e += kBwdThreads)
+    sG[(e / N) * LDG + e % N] = a.dh_final ? a.dh_final[(size_t)chain * PN + e] : 0.f;
   __syncthreads();
 
   // ================= reverse sweep =================
   float* red = sMisc + 8;
   float dD_acc = 0.f, dA_acc = 0.f;  // thread 0 keeps the chain's dA; every thread its dD share
+  // thread 0: gradients of a sub-chunk's first token stay pending until the
+  // sub-chunk before it (walked next) has added its share
+  float pend_ddt = 0.f, pend_dlam = 0.f;
   for (int c = nsub - 1; c >= 0; --c) {
     const int t0 = c * Qb, L = min(Qb, T - t0);
     const int nr = L * R;
     coefs(c);
     load_rows(c, true);
-    for (int e = tid; e < PN; e += kBwdThreads) sE[e] = ck[(size_t)c * PN + e];
     __syncthreads();
     // G = Rot(-phi_end) dE_next, and the end angle's gradient
     // dphi_end[j] = sum_p (dE1 E'0 - dE0 E'1) with E' the next entry value
+    // (still in sE: the previous step's entry value, or h_T)
     for (int j = tid; j < NH; j += kBwdThreads) {
       float sn, cs;
       sincosf(sPhi[(L - 1) * NH + j], &sn, &cs);
       float acc = 0.f;
-      const float* En = ck + (size_t)(c + 1) * PN;
       for (int p = 0; p < P; ++p) {
-        const int i0 = p * N + 2 * j;
-        const float d0 = sG[i0], d1 = sG[i0 + 1];
-        acc += d1 * En[i0] - d0 * En[i0 + 1];
-        sG[i0] = d0 * cs + d1 * sn;
-        sG[i0 + 1] = -d0 * sn + d1 * cs;
+        const int i0 = p * N + 2 * j, ig = p * LDG + 2 * j;
+        const float d0 = sG[ig], d1 = sG[ig + 1];
+        acc += d1 * sE[i0] - d0 * sE[i0 + 1];
+        sG[ig] = d0 * cs + d1 * sn;
+        sG[ig + 1] = -d0 * sn + d1 * cs;
       }
       sDphiE[j] = acc;
     }
+    __syncthreads();
+    ld_state(sE, ck + (size_t)c * PN);
     __syncthreads();
     // scores S = Ct Bt^T, Pm = dY X^T (rows x rows)
     for (int e = tid; e < kRows * kRows; e += kBwdThreads) {
       const int q = e / kRows, k = e % kRows;
       float s = 0.f, pm = 0.f;
       if (q < nr && k < nr) {
-        for (int n = 0; n < N; ++n) s += sCt[q * N + n] * sBt[k * N + n];
-        for (int p = 0; p < P; ++p) pm += sdY[q * P + p] * sX[k * P + p];
+        for (int n = 0; n < N; ++n) s += sCt[q * N + n] * sBt[k * LDB + n];
+        for (int p = 0; p < P; ++p) pm += sdY[q * P + p] * sX[k * LDX + p];
       }
       sS[e] = s;
       sPm[e] = pm;
@@ -328,7 +362,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
       const int k = e / P, p = e % P;
       float gb = 0.f, v = 0.f;
       if (k < nr) {
-        for (int n = 0; n < N; ++n) gb += sG[p * N + n] * sBt[k * N + n];
+        for (int n = 0; n < N; ++n) gb += sG[p * LDG + n] * sBt[k * LDB + n];
         const int tk = k / R;
         for (int q = 0; q < nr; ++q) v += sM[(q / R) * Qb + tk] * sS[q * kRows + k] * sdY[q * P + p];
         v += Dh * sdY[e] + sTk[kW * 16 + tk] * gb;
@@ -344,14 +378,14 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
         const int tq = q / R;
         for (int k = 0; k < nr; ++k) {
           const float mq = sM[tq * Qb + k / R];
-          dc += mq * sPm[q * kRows + k] * sBt[k * N + n];
+          dc += mq * sPm[q * kRows + k] * sBt[k * LDB + n];
           const float mk = sM[(k / R) * Qb + tq];
           db += mk * sPm[k * kRows + q] * sCt[k * N + n];
         }
         float ed = 0.f, gx = 0.f;
         for (int p = 0; p < P; ++p) {
           ed += sE[p * N + n] * sdY[q * P + p];
-          gx += sG[p * N + n] * sX[q * P + p];
+          gx += sG[p * LDG + n] * sX[q * LDX + p];
         }
         car = sTk[kEl * 16 + tq] * ed;
         dc += car;
@@ -363,8 +397,8 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
     }
     // <G, E> (the end decay's gradient) and <dY, X> (D's)
     float ge = 0.f, yx = 0.f;
-    for (int e = tid; e < PN; e += kBwdThreads) ge += sG[e] * sE[e];
-    for (int e = tid; e < kRows * P; e += kBwdThreads) yx += sdY[e] * sX[e];
+    for (int e = tid; e < PN; e += kBwdThreads) ge += sG[(e / N) * LDG + e % N] * sE[e];
+    for (int e = tid; e < kRows * P; e += kBwdThreads) yx += sdY[e] * sX[(e / P) * LDX + e % P];
     const float sumGE = block_sum(ge, red);
     dD_acc += yx;
     __syncthreads();
@@ -373,9 +407,9 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
       const float elE = expf(sMisc[0]);
       for (int e = tid; e < PN; e += kBwdThreads) {
         const int p = e / N, n = e % N;
-        float v = elE * sG[e];
+        float v = elE * sG[p * LDG + n];
         for (int q = 0; q < nr; ++q) v += sTk[kEl * 16 + q / R] * sdY[q * P + p] * sCt[q * N + n];
-        sG[e] = v;
+        sG[p * LDG + n] = v;
       }
     }
     // rows back to the lab frame (dB, dC), angle gradients per (token, pair)
@@ -400,7 +434,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
       if (t < L) {
         for (int r = 0; r < R; ++r) {
           const int q = t * R + r;
-          d += sdBt[q * N + 2 * j] * sBt[q * N + 2 * j + 1] - sdBt[q * N + 2 * j + 1] * sBt[q * N + 2 * j];
+          d += sdBt[q * N + 2 * j] * sBt[q * LDB + 2 * j + 1] - sdBt[q * N + 2 * j + 1] * sBt[q * LDB + 2 * j];
           d += sdCt[q * N + 2 * j] * sCt[q * N + 2 * j + 1] - sdCt[q * N + 2 * j + 1] * sCt[q * N + 2 * j];
         }
       }
@@ -413,7 +447,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
       for (int r = 0; r < R; ++r) {
         const int q = t * R + r;
         for (int n = lane; n < N; n += kWave) dlc += sCcar[q * N + n] * sCt[q * N + n];
-        for (int p = lane; p < P; p += kWave) dw += sX[q * P + p] * sGB[q * P + p];
+        for (int p = lane; p < P; p += kWave) dw += sX[q * LDX + p] * sGB[q * P + p];
       }
       dlc = lane_group_sum(dlc, kWave);
       dw = lane_group_sum(dw, kWave);
@@ -431,67 +465,63 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
         dTHg[(size_t)(t0 + t) * tokTh + j] = acc;
       }
     }
-    // token scalars (one thread: at most 16 tokens)
-    if (tid == 0) {
+    // token scalars, lane t of wave 0 = token t.  With the pairs' and the
+    // weights' terms collected per token,
+    //   dgamma_t = sum_{q>=t} dM(q,t) e^{l_q-l_t} + dw_t e^{lE-l_t}
+    //   dbeta_t  = sum_{q>=t} dM(q,t-1) e^{l_q-l_t} + dw_{t-1} e^{lE-l_t}   (t >= 1)
+    //   dl_t     = (carried part) + sum_{k<=t} dM(t,k) M(t,k) - gamma_t dgamma_t - beta_t dbeta_t
+    //   dlE      = e^{lE} <G, E> + sum_k dw_k (w_k - [k = L-1] beta_next)
+    // and the log-decays' sums l_t = sum_{0<s<=t} a_s, lE = l_{L-1} + a_next.
+    if (tid < kWave) {
+      const int t = tid;
+      const bool v = t < L;
       const float lE = sMisc[0];
       const bool nxt = sMisc[3] != 0.f;
-      float dl[16], dga[16], dbe[16];
-      for (int t = 0; t < L; ++t) {
-        dl[t] = sTk[kDlc * 16 + t];
-        dga[t] = 0.f;
-        dbe[t] = 0.f;
-      }
-      float dlE = expf(lE) * sumGE;
-      float dbn = 0.f;
-      for (int q = 0; q < L; ++q) {
-        const float lq = sTk[kL * 16 + q];
-        for (int k = 0; k <= q; ++k) {
-          const float dm = sdM[q * Qb + k];
-          const float e1 = expf(lq - sTk[kL * 16 + k]);
-          dga[k] += dm * e1;
-          dl[q] += dm * sM[q * Qb + k];
-          dl[k] -= dm * sTk[kGa * 16 + k] * e1;
-          if (k < q) {
-            const float e2 = expf(lq - sTk[kL * 16 + k + 1]);
-            dbe[k + 1] += dm * e2;
-            dl[k + 1] -= dm * sTk[kBe * 16 + k + 1] * e2;
-          }
+      float dga = 0.f, dbe = 0.f, dl = 0.f, dwt = 0.f, wpart = 0.f;
+      if (v) {
+        const float lt = sTk[kL * 16 + t];
+        dwt = sTk[kDw * 16 + t];
+        for (int q = t; q < L; ++q) {
+          const float e = expf(sTk[kL * 16 + q] - lt);
+          dga += sdM[q * Qb + t] * e;
+          if (t >= 1) dbe += sdM[q * Qb + t - 1] * e;
         }
+        dga += dwt * expf(lE - lt);
+        if (t >= 1) dbe += sTk[kDw * 16 + t - 1] * expf(lE - lt);
+        float dlq = sTk[kDlc * 16 + t];
+        for (int k = 0; k <= t; ++k) dlq += sdM[t * Qb + k] * sM[t * Qb + k];
+        dl = dlq - sTk[kGa * 16 + t] * dga - (t >= 1 ? sTk[kBe * 16 + t] * dbe : 0.f);
+        wpart = dwt * (sTk[kW * 16 + t] - (t == L - 1 ? sMisc[2] : 0.f));
       }
-      for (int k = 0; k < L; ++k) {
-        const float dw = sTk[kDw * 16 + k];
-        const float e1 = expf(lE - sTk[kL * 16 + k]);
-        dga[k] += dw * e1;
-        dlE += dw * sTk[kGa * 16 + k] * e1;
-        dl[k] -= dw * sTk[kGa * 16 + k] * e1;
-        if (k + 1 < L) {
-          const float e2 = expf(lE - sTk[kL * 16 + k + 1]);
-          dbe[k + 1] += dw * e2;
-          dlE += dw * sTk[kBe * 16 + k + 1] * e2;
-          dl[k + 1] -= dw * sTk[kBe * 16 + k + 1] * e2;
-        } else if (nxt) {
-          dbn += dw;  // beta of the next token, weight e^{lE - lE} = 1
-        }
-      }
-      // log-decays: l_t = sum_{0<s<=t} a_s, lE = l_{L-1} + a_next
-      float rc = 0.f;
-      for (int t = L - 1; t >= 0; --t) {
-        rc += dl[t];
+      const float dlE = expf(lE) * sumGE + lane_group_sum(wpart, kWave);
+      const float dbn = __shfl(dwt, L - 1, kWave);  // beta of the next token, weight e^{lE - lE} = 1
+      const float pre = wave_inclusive_scan(dl);
+      const float rc = lane_group_sum(dl, kWave) - pre + dl;  // sum_{s >= t} dl_s
+      float gdt = 0.f, glm = 0.f, dAp = 0.f;
+      if (v) {
         const float da = t > 0 ? rc + dlE : 0.f;
-        const int tg = t0 + t;
-        const float dt = DTg[(size_t)tg * H], lm = LMg[(size_t)tg * H];
+        const float dt = sTk[kDt * 16 + t], lm = sTk[kLm * 16 + t];
         const DCoef dc = dcoef(dt, lm, Ah, a.disc);
-        dDTg[(size_t)tg * H] = Ah * da + dc.bdt * dbe[t] + dc.gdt * dga[t];
-        dLMg[(size_t)tg * H] = dc.blam * dbe[t] + dc.glam * dga[t];
-        dA_acc += dt * da + dc.bA * dbe[t];
+        gdt = Ah * da + dc.bdt * dbe + dc.gdt * dga;
+        glm = dc.blam * dbe + dc.glam * dga;
+        dAp = dt * da + dc.bA * dbe;
+        if (t > 0) {
+          dDTg[(size_t)(t0 + t) * H] = gdt;
+          dLMg[(size_t)(t0 + t) * H] = glm;
+        }
       }
-      if (nxt) {  // the next token's decay and previous-input weight entered here
-        const int tg = t0 + L;
-        const float dt = DTg[(size_t)tg * H], lm = LMg[(size_t)tg * H];
-        const DCoef dc = dcoef(dt, lm, Ah, a.disc);
-        dDTg[(size_t)tg * H] += Ah * dlE + dc.bdt * dbn;
-        dLMg[(size_t)tg * H] += dc.blam * dbn;
-        dA_acc += dt * dlE + dc.bA * dbn;
+      dAp = lane_group_sum(dAp, kWave);
+      if (t == 0) {
+        if (nxt) {  // the next token's decay and previous-input weight entered here
+          const float dt = sMisc[4], lm = sMisc[5];
+          const DCoef dc = dcoef(dt, lm, Ah, a.disc);
+          dDTg[(size_t)(t0 + L) * H] = pend_ddt + Ah * dlE + dc.bdt * dbn;
+          dLMg[(size_t)(t0 + L) * H] = pend_dlam + dc.blam * dbn;
+          dA_acc += dt * dlE + dc.bA * dbn;
+        }
+        pend_ddt = gdt;
+        pend_dlam = glm;
+        dA_acc += dAp;
       }
     }
     __syncthreads();
@@ -504,7 +534,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
     float dh_part = 0.f, du_part = 0.f;
     for (int e = tid; e < PN; e += kBwdThreads) {
       const int p = e / N, n = e % N;
-      const float g = sG[e];
+      const float g = sG[p * LDG + n];
       a.dh0[(size_t)chain * PN + e] = al0 * g;
       dh_part += g * h0[e];
       float u = 0.f;
@@ -516,21 +546,21 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs a, i
     for (int e = tid; e < R * P; e += kBwdThreads) {  // dx_prev[r][p] = beta_0 sum_n dE[p][n] B_prev[r][n]
       const int r = e / P, p = e % P;
       float v = 0.f;
-      for (int n = 0; n < N; ++n) v += sG[p * N + n] * to_f32(Bp0[r * N + n]);
+      for (int n = 0; n < N; ++n) v += sG[p * LDG + n] * to_f32(Bp0[r * N + n]);
       a.dx_prev[(size_t)chain * R * P + e] = be0 * v;
     }
     for (int e = tid; e < R * N; e += kBwdThreads) {  // dB_prev[r][n] = beta_0 sum_p dE[p][n] x_prev[r][p]
       const int r = e / N, n = e % N;
       float v = 0.f;
-      for (int p = 0; p < P; ++p) v += sG[p * N + n] * to_f32(Xp0[r * P + p]);
+      for (int p = 0; p < P; ++p) v += sG[p * LDG + n] * to_f32(Xp0[r * P + p]);
       a.dB_prev[(size_t)chain * R * N + e] = be0 * v;
     }
     const float dsum = block_sum(dD_acc, red);
     if (tid == 0) {
       const DCoef dc = dcoef(dt0, lm0, Ah, a.disc);
       const float da0 = al0 * sh;
-      a.ddt[(size_t)b * T * H + hh] += Ah * da0 + dc.bdt * su;
-      a.dlam[(size_t)b * T * H + hh] += dc.blam * su;
+      a.ddt[(size_t)b * T * H + hh] = pend_ddt + Ah * da0 + dc.bdt * su;
+      a.dlam[(size_t)b * T * H + hh] = pend_dlam + dc.blam * su;
       dA_acc += dt0 * da0 + dc.bA * su;
       a.part[(size_t)chain * 2] = dA_acc;
       a.part[(size_t)chain * 2 + 1] = dsum;
