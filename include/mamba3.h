@@ -273,17 +273,22 @@ typedef struct {
   float* dx_prev;  /* (batch, heads, R, P): of state0.x_prev */
 } m3_grads;
 
-/* Workspace of mamba3_prefill_backward: the state's entry value at every
- * sub-chunk of 16 / R tokens plus per-chain partial sums,
- * batch * heads * (ceil(seqlen R / 16) + 1) * P * N * 4 bytes and a little. */
+/* Workspace of mamba3_prefill_backward: with units of 64 / R tokens and
+ * U = ceil(seqlen R / 64) units per chain, two P x N fp32 slots per unit (the
+ * state's entry value and the adjoint after the unit) and one per chain (the
+ * adjoint of the entry value), batch * heads * (2 U + 1) * P * N * 4 bytes,
+ * then per-unit scalars: each of e^{lE} (U), the end angle's (cos, sin)
+ * (U N), the first-token terms (2 U), the unit sums (2 U) and the chain sums
+ * (2), times batch * heads * 4 bytes, rounded up to 256 bytes. */
 int mamba3_prefill_backward_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* bytes);
 
 /* x, B, C, dt, lam, theta, A, D as given to mamba3_prefill; state0 the state
  * the prefill started from (read only); dy (io dtype, y's layout) the
  * cotangent of y; dh_final (fp32 (batch, heads, P, N)) that of the final h,
  * or NULL for zero.  dims->chunk is ignored.  Errors as mamba3_prefill, plus
- * M3_ERR_NULL / M3_ERR_ALIGN for grads and its arrays, M3_ERR_UNSUPPORTED for
- * P * N > 8192, and M3_ERR_WORKSPACE for a short workspace. */
+ * M3_ERR_NULL / M3_ERR_ALIGN for grads and its arrays, M3_ERR_UNSUPPORTED
+ * unless R is 1, 2 or 4 and P, N are multiples of 16 with P, N <= 128 and
+ * P * N <= 8192, and M3_ERR_WORKSPACE for a short workspace. */
 int mamba3_prefill_backward(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
                             const float* dt, const float* lam, const float* theta, const float* A,
                             const float* D, const m3_state* state0, const void* dy, const float* dh_final,

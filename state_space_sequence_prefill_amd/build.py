@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmamba3.so")
 SOURCES = ["m3_api.cpp", "m3_state.hip", "m3_decode.hip", "m3_decode_mimo.hip", "m3_prefill.hip", "m3_prefill_pc.hip",
            "m3_prefill_pc_gated.hip", "m3_prefill_pc_down.hip", "m3_prefill_pc_bcnorm.hip",
-           "m3_prefill_pc_bcnorm_gated.hip", "m3_prefill_pc_bcnorm_down.hip", "m3_backward.hip"]
+           "m3_prefill_pc_bcnorm_gated.hip", "m3_prefill_pc_bcnorm_down.hip", "m3_backward.hip",
+           "m3_backward_bf16.hip", "m3_backward_f32.hip"]
 ARCH = "gfx950"
 
 

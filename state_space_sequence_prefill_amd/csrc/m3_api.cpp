@@ -441,7 +441,8 @@ int mamba3_prefill_backward_workspace_bytes(const m3_dims* dims, int32_t seqlen,
   if (!bytes) return fail(M3_ERR_NULL, "bytes is NULL");
   if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
   if (!m3::backward_supported(m))
-    return fail(M3_ERR_UNSUPPORTED, "the backward pass needs headdim * dstate <= 8192 (got %d)", m.P * m.N);
+    return fail(M3_ERR_UNSUPPORTED, "the backward pass needs R in {1, 2, 4}, headdim and dstate multiples of 16 "
+                "with headdim * dstate <= 8192 (got R %d, %d x %d)", m.R, m.P, m.N);
   *bytes = seqlen > 0 ? m3::backward_workspace_bytes(m, seqlen) : 0;
   return ok();
 }
@@ -455,7 +456,8 @@ int mamba3_prefill_backward(const m3_dims* dims, int32_t seqlen, const void* x, 
   if (st != M3_OK) return st;
   if (seqlen < 0) return fail(M3_ERR_SHAPE, "seqlen %d < 0", seqlen);
   if (!m3::backward_supported(m))
-    return fail(M3_ERR_UNSUPPORTED, "the backward pass needs headdim * dstate <= 8192 (got %d)", m.P * m.N);
+    return fail(M3_ERR_UNSUPPORTED, "the backward pass needs R in {1, 2, 4}, headdim and dstate multiples of 16 "
+                "with headdim * dstate <= 8192 (got R %d, %d x %d)", m.R, m.P, m.N);
   if (!state0) return fail(M3_ERR_NULL, "state0 is NULL");
   if ((st = check_ptr(state0->h, "state0.h")) != M3_OK) return st;
   if ((st = check_ptr(state0->B_prev, "state0.B_prev")) != M3_OK) return st;
@@ -502,9 +504,7 @@ int mamba3_prefill_backward(const m3_dims* dims, int32_t seqlen, const void* x, 
   a.dh0 = grads->dh0;
   a.dB_prev = grads->dB_prev;
   a.dx_prev = grads->dx_prev;
-  a.part = static_cast<float*>(workspace);
-  a.ckpt = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    align256((size_t)m.batch * m.heads * 2 * sizeof(float)));
+  a.ws = workspace;
   a.seqlen = seqlen;
   a.disc = m.disc;
   return hip_status(m3::launch_backward(m, a, static_cast<hipStream_t>(stream)), "mamba3_prefill_backward");

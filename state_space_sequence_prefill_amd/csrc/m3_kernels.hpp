@@ -64,8 +64,7 @@ struct BackwardArgs {
   float* dh0;            // (batch, heads, P, N)
   float* dB_prev;        // (batch, heads, R, N)
   float* dx_prev;        // (batch, heads, R, P)
-  float* ckpt;           // workspace: sub-chunk entry values
-  float* part;           // workspace: per-chain dA, dD
+  void* ws;              // workspace (mamba3_prefill_backward_workspace_bytes)
   int seqlen;
   int disc;
 };

@@ -343,9 +343,12 @@ def call_backward(d, seqlen=32, ptrs=None, grads=None, ws=FAKE, wsb=1 << 40, dh=
 def test_backward_workspace_size():
     d = dims(batch=2, heads=3, headdim=64, dstate=128, rank=1)
     n = B.mamba3_prefill_backward_workspace_bytes(d, 100)
-    assert n == 2 * 3 * (7 + 1) * 64 * 128 * 4 + 256   # 16-token sub-chunks
-    d4 = dims(batch=1, heads=1, headdim=64, dstate=64, rank=4)
-    assert B.mamba3_prefill_backward_workspace_bytes(d4, 9) == (3 + 1) * 64 * 64 * 4 + 256  # 4-token sub-chunks
+    # 2 units of 64 tokens: two P x N slots per unit and one per chain, then
+    # e^{lE}, (cos, sin) of the end angle, two pairs of unit sums, the chain sums
+    small = 256 + 6 * 2 * 64 * 2 * 4 + 256 + 256 + 256
+    assert n == 6 * (2 * 2 + 1) * 64 * 128 * 4 + small
+    d4 = dims(batch=1, heads=1, headdim=64, dstate=64, rank=4)   # one unit of 16 tokens
+    assert B.mamba3_prefill_backward_workspace_bytes(d4, 9) == 3 * 64 * 64 * 4 + 5 * 256
     assert B.mamba3_prefill_backward_workspace_bytes(d, 0) == 0
 
 
@@ -377,3 +380,7 @@ def test_backward_argument_checks():
 def test_backward_size_limit():
     assert call_backward(dims(headdim=128, dstate=128)) == B.M3_ERR_UNSUPPORTED
     assert "8192" in B.m3_last_error()
+    # the matrix-core tiles are 16 wide
+    assert call_backward(dims(headdim=24, dstate=64)) == B.M3_ERR_UNSUPPORTED
+    assert call_backward(dims(headdim=64, dstate=40)) == B.M3_ERR_UNSUPPORTED
+    assert call_backward(dims(headdim=64, dstate=64, rank=8)) == B.M3_ERR_UNSUPPORTED
