@@ -21,7 +21,9 @@ only a few warm-up steps the timed region measures the clock ramp.  The same JSO
                    prefill throughput, the headline shape under the other two
                    discretisation rules, and the gated entry points (pre-gate
                    grouped RMSNorm fused into the store of y) on the headline
-                   prefill and both decode shapes.
+                   prefill and both decode shapes, BC normalisation, the MIMO
+                   rank down-projection, and the backward pass (all gradients)
+                   on the SISO and MIMO prefill shapes.
 Prints exactly one JSON line (rank 0).
 """
 
@@ -64,6 +66,30 @@ def prefill_flops(w):
     """Chunked-form FLOPs (full tiles): per token-head 4 R N P + 2 Q R^2 (N + P)."""
     th = w.batch * w.seqlen * w.heads
     return th * (4 * w.rank * w.dstate * w.headdim + 2 * w.chunk * w.rank ** 2 * (w.dstate + w.headdim))
+
+
+def backward_bytes(w):
+    """Algorithmic HBM bytes of one backward pass: every prefill input and dy
+    read once, every gradient written once (fp32), the entry state read and
+    its gradient written once.  The workspace round trips of the unit
+    summaries are the design's own traffic and are reported beside it."""
+    io = 2 if w.io_dtype == "bf16" else 4
+    th = w.batch * w.seqlen * w.heads
+    nh = w.dstate // 2
+    reads = w.rank * (2 * w.headdim + 2 * w.dstate) * io + 8 + nh * 4
+    writes = w.rank * (w.headdim + 2 * w.dstate) * 4 + 8 + nh * 4
+    chains = w.batch * w.heads
+    state = chains * (w.headdim * w.dstate * 4 + w.rank * (w.dstate + w.headdim) * io)
+    return th * (reads + writes) + state + chains * (w.headdim * w.dstate + w.rank * (w.dstate + w.headdim)) * 4
+
+
+def backward_workspace_traffic(w):
+    """Bytes the backward moves through its workspace: the unit summaries U and
+    V are written (local), read and overwritten by E and G (scan), and read
+    (grad): eight passes over (units x P x N) fp32 per chain."""
+    qu = 64 // w.rank
+    units = (w.seqlen + qu - 1) // qu
+    return 8 * w.batch * w.heads * units * w.headdim * w.dstate * 4
 
 
 def gate_bytes(w, tokens):
@@ -174,6 +200,47 @@ class Prefill:
         wall = time.perf_counter() - t0
         kern_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
         return wall / steps * 1e3, kern_ms
+
+
+def time_backward(w, seed, steps, warmup):
+    """Time mamba3_prefill_backward (all four launches) on one workload."""
+    import torch
+    import state_space_sequence_prefill_amd as m3
+    from state_space_sequence_prefill_amd import synthetic as syn
+    d = m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype)
+    inp = syn.draw_torch(w, seed)
+    T = w.seqlen
+    state = m3.State.empty(d)
+    m3.m3_state_zero(d, state)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 1)
+    dy = torch.randn((w.batch, T, w.heads, w.rank, w.headdim), generator=g, device="cuda").to(inp["x"].dtype)
+    grads = {k: torch.empty(v, dtype=torch.float32, device="cuda") for k, v in m3.grad_shapes(d, T).items()}
+    ws = torch.empty(m3.mamba3_prefill_backward_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+
+    def run():
+        m3.mamba3_prefill_backward(d, T, inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], inp["theta"],
+                                   inp["A"], inp["D"], state, dy, grads, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nb = backward_bytes(w)
+    wt = backward_workspace_traffic(w)
+    out = {"ms_per_step": round(ms, 4), "Mtokens_per_s": round(w.batch * T / ms / 1e3, 3),
+           "algorithmic_bytes": nb, "hbm_frac": round(nb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "workspace_bytes": ws.numel(), "workspace_traffic_bytes": wt,
+           "hbm_frac_with_workspace": round((nb + wt) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del grads, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_decode(w, seed, steps=1000, flush_steps=20, gated=False, down=False, bcnorm=False):
@@ -524,6 +591,10 @@ def main():
             extra[f"{name}_bcnorm_gated"] = time_decode(syn.WORKLOADS[name], seed=7, flush_steps=5, gated=True,
                                                         bcnorm=True)
             torch.cuda.empty_cache()
+        # the backward pass (gradients of every input) on both prefill shapes
+        for name in (HEADLINE, "mimo_r4_t4096"):
+            log(f"bench: backward {name}")
+            extra[f"{name}_backward"] = time_backward(syn.WORKLOADS[name], seed=1007, steps=5, warmup=3)
         line["extra"] = extra
 
     if not args.no_cpu_baseline:

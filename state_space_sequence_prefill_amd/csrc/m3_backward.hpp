@@ -74,10 +74,16 @@ struct Lay {
   // over the banks)
 };
 
+// The unit slots (U/E, V/G) hold a P x N matrix in MFMA fragment order: the
+// 16 x 16 tile (s, nb) (rows p = 16 s + 4 g + v, columns n = 16 nb + c) is 64
+// lanes (g, c) of 4 consecutive floats (v), tiles in (s, nb) order.  A lane
+// of a C-layout accumulator stores or loads its 4 values as one 16-byte run,
+// and the scan's (p, pair) updates read and write 32-byte runs.
+
 // Workspace carved by launch_backward.
 struct BwdWs {
-  float* ckE;    // (chains, units, P, N): U_u, then E_u
-  float* ckG;    // (chains, units, P, N): V_u, then G_u
+  float* ckE;    // (chains, units, P x N in fragment order): U_u, then E_u
+  float* ckG;    // (chains, units, P x N in fragment order): V_u, then G_u
   float* dE0;    // (chains, P, N): adjoint of the entry value
   float* uel;    // (chains, units): e^{lE_u}
   float* ucs;    // (chains, units, N/2, 2): cos, sin of phi_end_u
@@ -221,30 +227,40 @@ template <typename IO, int W>
 struct RowsIn {
   static constexpr int q4 = W / 4, n = kU * q4, it = (n + kBT - 1) / kBT, LD = W + 4;
   float v[it][4];
+  static_assert(n % kBT == 0, "whole rows per pass");
+  // unconditional loads (rows past the end re-read row 0 and are zeroed):
+  // a load under a branch makes the compiler wait for it before the branch joins
   __device__ __forceinline__ void load(const IO* g, size_t tok, int rs, int L) {
 #pragma unroll
     for (int i = 0; i < it; ++i) {
       const int e = threadIdx.x + i * kBT, rho = e / q4, c4 = e % q4;
-      v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.f;
-      if (e < n && rho < (L << rs))
-        load4(g + (size_t)(rho >> rs) * tok + (rho & ((1 << rs) - 1)) * W + 4 * c4, v[i]);
+      const int rr = rho < (L << rs) ? rho : 0;
+      load4(g + (size_t)(rr >> rs) * tok + (rr & ((1 << rs) - 1)) * W + 4 * c4, v[i]);
     }
   }
-  // into LDS (row stride W + 4)
-  __device__ __forceinline__ void store(float* dst) const {
+  __device__ __forceinline__ void mask(int rs, int L) {
+#pragma unroll
+    for (int i = 0; i < it; ++i) {
+      const int rho = (threadIdx.x + i * kBT) / q4;
+      if (rho >= (L << rs)) v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.f;
+    }
+  }
+  // into LDS (row stride W + 4); rows past the end as zeros
+  __device__ __forceinline__ void store(float* dst, int rs, int L) {
+    mask(rs, L);
 #pragma unroll
     for (int i = 0; i < it; ++i) {
       const int e = threadIdx.x + i * kBT, rho = e / q4, c4 = e % q4;
-      if (e < n) *reinterpret_cast<float4*>(dst + rho * LD + 4 * c4) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+      *reinterpret_cast<float4*>(dst + rho * LD + 4 * c4) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
     }
   }
   // rotated back by the token's angle (Rot(-phi_t)) into LDS; W = N
   template <typename IOT>
-  __device__ __forceinline__ void store_rot(float* dst, const float* sPhi, int rs) {
+  __device__ __forceinline__ void store_rot(float* dst, const float* sPhi, int rs, int L) {
+    mask(rs, L);
 #pragma unroll
     for (int i = 0; i < it; ++i) {
       const int e = threadIdx.x + i * kBT, rho = e / q4, c4 = e % q4;
-      if (e >= n) continue;
       const int t = rho >> rs;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -261,13 +277,14 @@ struct RowsIn {
 
 // B and C rows rotated back with one trig per pair.
 template <typename IO, int N>
-__device__ __forceinline__ void store_rot2(RowsIn<IO, N>& b, RowsIn<IO, N>& c, const float* sPhi, int rs, float* db,
-                                           float* dc) {
+__device__ __forceinline__ void store_rot2(RowsIn<IO, N>& b, RowsIn<IO, N>& c, const float* sPhi, int rs, int L,
+                                           float* db, float* dc) {
   using RI = RowsIn<IO, N>;
+  b.mask(rs, L);
+  c.mask(rs, L);
 #pragma unroll
   for (int i = 0; i < RI::it; ++i) {
     const int e = threadIdx.x + i * kBT, rho = e / RI::q4, c4 = e % RI::q4;
-    if (e >= RI::n) continue;
     const int t = rho >> rs;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -321,8 +338,8 @@ __global__ __launch_bounds__(kBT) void local_kernel(BackwardArgs a, BwdWs ws, in
   RowsIn<IO, N> cin;
   cin.load(static_cast<const IO*>(which ? a.C : a.B) + tb * R * N, tokBC, rs, L);
   unit_coefs<NH>(ci, a.A[hh], a.disc, L, nxt, Qu, sTk, sMisc, sPhi);
-  rin.store(sR);
-  cin.template store_rot<IO>(sC, sPhi, rs);
+  rin.store(sR, rs, L);
+  cin.template store_rot<IO>(sC, sPhi, rs, L);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
@@ -346,10 +363,8 @@ __global__ __launch_bounds__(kBT) void local_kernel(BackwardArgs a, BwdWs ws, in
       acc = mfma4(wk[i] * sR[k * LDX + 16 * pb + c], sC[k * LDB + 16 * nb + c], acc);
     }
     const int n = 16 * nb + c;
-    if (which) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Og[(size_t)(16 * pb + 4 * g + v) * N + n] = acc[v];
-    } else {  // U: each (p, pair) turned by the unit's end angle
+    f32x4 o = acc;
+    if (!which) {  // U: each (p, pair) turned by the unit's end angle
       const bool odd = c & 1;
       float sn, cs;
       trig<IO>(phE[n >> 1], sn, cs);
@@ -357,9 +372,10 @@ __global__ __launch_bounds__(kBT) void local_kernel(BackwardArgs a, BwdWs ws, in
       for (int v = 0; v < 4; ++v) {
         const float mine = acc[v], other = xor1(mine);
         const float u0 = odd ? other : mine, u1 = odd ? mine : other;
-        Og[(size_t)(16 * pb + 4 * g + v) * N + n] = odd ? u0 * sn + u1 * cs : u0 * cs - u1 * sn;
+        o[v] = odd ? u0 * sn + u1 * cs : u0 * cs - u1 * sn;
       }
     }
+    reinterpret_cast<f32x4*>(Og)[(size_t)(pb * NB + nb) * 64 + lane] = o;
   }
   if (!which) {
     const size_t us = (size_t)chain * nu + u;
@@ -373,87 +389,114 @@ __global__ __launch_bounds__(kBT) void local_kernel(BackwardArgs a, BwdWs ws, in
 }
 
 // ============================ scan ============================
-// One thread per (chain, p, pair): E_u forward from the entry value, then
-// G_u backward from dh_final; the workspace slots are read (U_u, V_u) and
-// overwritten (E_u, G_u) in place.  Loads run kAhead units ahead of the
-// dependent updates.
+// One thread per (chain, 4 rows p, rotation pair): E_u forward from the entry
+// value, then G_u backward from dh_final; the slots are read (U_u, V_u) and
+// overwritten (E_u, G_u) in place, 32 contiguous bytes per thread (fragment
+// order).  Loads run kAhead units ahead of the dependent updates.
 template <typename IO>
 __global__ __launch_bounds__(kScanT) void scan_kernel(BackwardArgs a, BwdWs ws, int H, int P, int N, int R, int nu,
                                                       int bpc) {
-  constexpr int kAhead = 8;
+  constexpr int kAhead = 4;
   const int chain = blockIdx.x / bpc;
   const int e = (blockIdx.x - chain * bpc) * kScanT + threadIdx.x;
-  const int NH = N / 2, PN = P * N;
-  if (e >= PN / 2) return;
-  const int p = e / NH, j = e - p * NH;
+  const int NH = N / 2, PN = P * N, NB = N / 16;
+  if (e >= PN / 8) return;
+  const int tile = e >> 5, g = (e >> 3) & 3, c = 2 * (e & 7);
+  const int p0 = 16 * (tile / NB) + 4 * g, n = 16 * (tile % NB) + c, j = n >> 1;
+  const size_t off = ((size_t)tile * 64 + 16 * g + c) * 4;  // (v, n) then (v, n + 1)
   const int hh = chain % H, b = chain / H;
   const float Ah = a.A[hh];
   const size_t tb0 = (size_t)b * a.seqlen * H + hh;
   const float dt0 = a.dt[tb0], lm0 = a.lam[tb0];
   const float al0 = expf(dt0 * Ah), be0 = input_weights(dt0, lm0, al0, a.disc).x;
-  const int o = p * N + 2 * j;
-  const float2 hv = *reinterpret_cast<const float2*>(a.h + (size_t)chain * PN + o);
+  const float* h0 = a.h + (size_t)chain * PN;
   const IO* Bp = static_cast<const IO*>(a.B_prev) + (size_t)chain * R * N;
   const IO* Xp = static_cast<const IO*>(a.x_prev) + (size_t)chain * R * P;
-  float u0 = 0.f, u1 = 0.f;
-  for (int r = 0; r < R; ++r) {
-    const float xv = to_f32(Xp[r * P + p]);
-    u0 += xv * to_f32(Bp[r * N + 2 * j]);
-    u1 += xv * to_f32(Bp[r * N + 2 * j + 1]);
+  float E0[4], E1[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float u0 = 0.f, u1 = 0.f;
+    for (int r = 0; r < R; ++r) {
+      const float xv = to_f32(Xp[r * P + p0 + v]);
+      u0 += xv * to_f32(Bp[r * N + n]);
+      u1 += xv * to_f32(Bp[r * N + n + 1]);
+    }
+    const float2 hv = *reinterpret_cast<const float2*>(h0 + (size_t)(p0 + v) * N + n);
+    E0[v] = al0 * hv.x + be0 * u0;
+    E1[v] = al0 * hv.y + be0 * u1;
   }
-  float E0 = al0 * hv.x + be0 * u0, E1 = al0 * hv.y + be0 * u1;
-  float* cE = ws.ckE + (size_t)chain * nu * PN + o;
-  float* cG = ws.ckG + (size_t)chain * nu * PN + o;
+  float* cE = ws.ckE + (size_t)chain * nu * PN + off;
+  float* cG = ws.ckG + (size_t)chain * nu * PN + off;
   const float* uel = ws.uel + (size_t)chain * nu;
   const float2* ucs = reinterpret_cast<const float2*>(ws.ucs) + (size_t)chain * nu * NH + j;
   for (int ub = 0; ub < nu; ub += kAhead) {
-    float2 Uv[kAhead], cs[kAhead];
+    f32x4 U0[kAhead], U1[kAhead];
+    float2 cs[kAhead];
     float el[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
       const int uu = min(ub + i, nu - 1);
-      Uv[i] = *reinterpret_cast<const float2*>(cE + (size_t)uu * PN);
+      U0[i] = *reinterpret_cast<const f32x4*>(cE + (size_t)uu * PN);
+      U1[i] = *reinterpret_cast<const f32x4*>(cE + (size_t)uu * PN + 4);
       cs[i] = ucs[(size_t)uu * NH];
       el[i] = uel[uu];
     }
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
       if (ub + i < nu) {
-        *reinterpret_cast<float2*>(cE + (size_t)(ub + i) * PN) = make_float2(E0, E1);
-        const float z0 = el[i] * E0, z1 = el[i] * E1;
-        E0 = z0 * cs[i].x - z1 * cs[i].y + Uv[i].x;
-        E1 = z0 * cs[i].y + z1 * cs[i].x + Uv[i].y;
+        float* o = cE + (size_t)(ub + i) * PN;
+        *reinterpret_cast<f32x4*>(o) = f32x4{E0[0], E0[1], E0[2], E0[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{E1[0], E1[1], E1[2], E1[3]};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float z0 = el[i] * E0[v], z1 = el[i] * E1[v];
+          E0[v] = z0 * cs[i].x - z1 * cs[i].y + U0[i][v];
+          E1[v] = z0 * cs[i].y + z1 * cs[i].x + U1[i][v];
+        }
       }
     }
   }
-  float d0 = 0.f, d1 = 0.f;
+  float d0[4] = {0.f, 0.f, 0.f, 0.f}, d1[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.dh_final) {
-    const float2 v = *reinterpret_cast<const float2*>(a.dh_final + (size_t)chain * PN + o);
-    d0 = v.x;
-    d1 = v.y;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float2 hv = *reinterpret_cast<const float2*>(a.dh_final + (size_t)chain * PN + (size_t)(p0 + v) * N + n);
+      d0[v] = hv.x;
+      d1[v] = hv.y;
+    }
   }
   for (int ub = nu - 1; ub >= 0; ub -= kAhead) {
-    float2 Vv[kAhead], cs[kAhead];
+    f32x4 V0[kAhead], V1[kAhead];
+    float2 cs[kAhead];
     float el[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
       const int uu = max(ub - i, 0);
-      Vv[i] = *reinterpret_cast<const float2*>(cG + (size_t)uu * PN);
+      V0[i] = *reinterpret_cast<const f32x4*>(cG + (size_t)uu * PN);
+      V1[i] = *reinterpret_cast<const f32x4*>(cG + (size_t)uu * PN + 4);
       cs[i] = ucs[(size_t)uu * NH];
       el[i] = uel[uu];
     }
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
       if (ub - i >= 0) {
-        const float g0 = d0 * cs[i].x + d1 * cs[i].y;  // Rot(-phi_end) dE_{u+1}
-        const float g1 = -d0 * cs[i].y + d1 * cs[i].x;
-        *reinterpret_cast<float2*>(cG + (size_t)(ub - i) * PN) = make_float2(g0, g1);
-        d0 = el[i] * g0 + Vv[i].x;
-        d1 = el[i] * g1 + Vv[i].y;
+        f32x4 g0, g1;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          g0[v] = d0[v] * cs[i].x + d1[v] * cs[i].y;  // Rot(-phi_end) dE_{u+1}
+          g1[v] = -d0[v] * cs[i].y + d1[v] * cs[i].x;
+          d0[v] = el[i] * g0[v] + V0[i][v];
+          d1[v] = el[i] * g1[v] + V1[i][v];
+        }
+        float* o = cG + (size_t)(ub - i) * PN;
+        *reinterpret_cast<f32x4*>(o) = g0;
+        *reinterpret_cast<f32x4*>(o + 4) = g1;
       }
     }
   }
-  *reinterpret_cast<float2*>(ws.dE0 + (size_t)chain * PN + o) = make_float2(d0, d1);
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    *reinterpret_cast<float2*>(ws.dE0 + (size_t)chain * PN + (size_t)(p0 + v) * N + n) = make_float2(d0[v], d1[v]);
 }
 
 // ============================ grad ============================
@@ -495,7 +538,7 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   CoefIn<NH> ci;
   ci.load(a.dt + tb, a.lam + tb, a.theta + tb * NH, H, tokTh, L, nxt);
   constexpr int n4 = P * N / 4, itG = (n4 + kBT - 1) / kBT;
-  f32x4 gv[itG];
+  f32x4 gv[itG];  // fragment order: float4 e = (tile e / 64, lane e % 64)
 #pragma unroll
   for (int i = 0; i < itG; ++i) gv[i] = reinterpret_cast<const f32x4*>(Gg)[min((int)threadIdx.x + i * kBT, n4 - 1)];
   RowsIn<IO, P> xin, yin;
@@ -507,12 +550,15 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   unit_coefs<NH>(ci, Ah, a.disc, L, nxt, ly.Qu, sTk, sMisc, sPhi);
 #pragma unroll
   for (int i = 0; i < itG; ++i) {
-    const int e = threadIdx.x + i * kBT;
-    if (e < n4) *reinterpret_cast<f32x4*>(sG + ((4 * e) / N) * LDB + (4 * e) % N) = gv[i];
+    const int e = threadIdx.x + i * kBT, tile = e >> 6, ln = e & 63;
+    float* d = sG + (16 * (tile / NB) + 4 * (ln >> 4)) * LDB + 16 * (tile % NB) + (ln & 15);
+    if (e < n4)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) d[v * LDB] = gv[i][v];
   }
-  xin.store(sX);
-  yin.store(sdY);
-  store_rot2<IO, N>(bin, cin, sPhi, rs, sBt, sCt);
+  xin.store(sX, rs, L);
+  yin.store(sdY, rs, L);
+  store_rot2<IO, N>(bin, cin, sPhi, rs, L, sBt, sCt);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
@@ -650,15 +696,12 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // E (the unit's entry value) for the carried product of step 5, loaded a step ahead
-  float ev[PB][4][NB];
+  // (fragment order: lane (g, c) of tile (s, nb) holds E[16 s + 4 g + v][16 nb + c], v = 0..3)
+  f32x4 ev[PB][NB];
 #pragma unroll
   for (int s = 0; s < PB; ++s)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float* er = Eg + (size_t)(16 * s + 4 * g + v) * N + c;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) ev[s][v][nb] = er[16 * nb];
-    }
+    for (int nb = 0; nb < NB; ++nb) ev[s][nb] = reinterpret_cast<const f32x4*>(Eg)[(s * NB + nb) * 64 + lane];
   // ---- 4. GX[k][n] = X_k . G[:, n]; dBt = w GX + (M.Pm)^T Ct, rows of this
   //         block; the end angle's share through the update weights ----
   f32x4 db[NB];
@@ -729,14 +772,14 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) dc[nb] = mfma4(yb[v], ev[s][v][nb], dc[nb]);
+        for (int nb = 0; nb < NB; ++nb) dc[nb] = mfma4(yb[v], ev[s][nb][v], dc[nb]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         if ((nb & 3) != wv) continue;  // pair columns nb = wv (mod 4)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int p = 16 * s + 4 * g + v, n = 16 * nb + c;
-          const float e = ev[s][v][nb];
+          const float e = ev[s][nb][v];
           const float eo = xor1(e);
           const float gs = sG[p * LDB + n], go = sG[p * LDB + (n ^ 1)];
           ge += gs * e;
@@ -1001,7 +1044,7 @@ hipError_t launch_io_pn(const Dims& d, const BackwardArgs& a, const BwdWs& w, hi
   const int rs = d.R == 1 ? 0 : d.R == 2 ? 1 : 2;
   const int chains = d.batch * d.heads;
   const int nu = (a.seqlen + kU / d.R - 1) / (kU / d.R);
-  const int bpc = (P * N / 2 + kScanT - 1) / kScanT;
+  const int bpc = (P * N / 8 + kScanT - 1) / kScanT;
   const size_t lds_local = (size_t)(kU * (P + 4) + kU * (N + 4) + (kU / d.R) * (N / 2 + 1) + kSmall) * 4;
   const size_t lds_grad = (size_t)Lay(P, N, d.R, true).total * 4;
   const dim3 units((unsigned)chains * nu), blk(kBT);
