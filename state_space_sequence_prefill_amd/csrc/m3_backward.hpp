@@ -695,13 +695,6 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   }
 
-  // E (the unit's entry value) for the carried product of step 5, loaded a step ahead
-  // (fragment order: lane (g, c) of tile (s, nb) holds E[16 s + 4 g + v][16 nb + c], v = 0..3)
-  f32x4 ev[PB][NB];
-#pragma unroll
-  for (int s = 0; s < PB; ++s)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ev[s][nb] = reinterpret_cast<const f32x4*>(Eg)[(s * NB + nb) * 64 + lane];
   // ---- 4. GX[k][n] = X_k . G[:, n]; dBt = w GX + (M.Pm)^T Ct, rows of this
   //         block; the end angle's share through the update weights ----
   f32x4 db[NB];
@@ -748,6 +741,13 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int nb = 0; nb < NB; ++nb) db[nb] = mfma4(av, cr[16 * nb], db[nb]);
     }
 
+  // E (the unit's entry value) for the carried product of step 5, loaded here
+  // (fragment order: lane (g, c) of tile (s, nb) holds E[16 s + 4 g + v][16 nb + c], v = 0..3)
+  f32x4 ev[PB][NB];
+#pragma unroll
+  for (int s = 0; s < PB; ++s)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ev[s][nb] = reinterpret_cast<const f32x4*>(Eg)[(s * NB + nb) * 64 + lane];
   // ---- 5. PmT[k][q] = X_k . dY_q (rows q of this block, every k);
   //         carry[q][n] = dY_q . E[:, n]; dCt = e^l carry + (M.Pm) Bt;
   //         <G, E> and the end angle's share through E ----
