@@ -14,7 +14,9 @@ only a few warm-up steps the timed region measures the clock ramp.  The same JSO
                    against the MI355X HBM peak of 8 TB/s; `traffic` comes from
                    committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters when
                    they were taken on the current kernel source, else null;
-  cpu_baseline  -- the fp64 oracle timed on the host on a bounded sample;
+  cpu_baseline  -- the fp64 oracle timed on the host on a bounded sample, one
+                   thread (the value) and over all host cores (`all_cores`);
+                   the decode entries carry the oracle's ms per step;
   extra         -- decode step (256 x 32 heads, MIMO R=4 N=64 and SISO N=128;
                    1000 steps captured in a HIP graph, plus a run with a
                    512 MiB cache flush between steps), MIMO / 16K-token
@@ -361,6 +363,74 @@ def cpu_baseline(w, min_seconds=10.0):
             "seconds": round(spent, 2), "cpu": _cpu_model(), "host_cpus": os.cpu_count()}
 
 
+def _oracle_task(args):
+    """One batch row of the workload, a slice of its heads, through the
+    oracle (run in a worker process; single-threaded numpy)."""
+    name, row, h0, h1 = args
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        pass
+    import oracle
+    from state_space_sequence_prefill_amd import synthetic as syn
+    w = syn.WORKLOADS[name]
+    ex = syn.as_exact(syn.draw(w.with_(batch=1), 1001 + row), w.io_dtype)
+    sl = {k: (v[:, :, h0:h1] if v.ndim >= 3 else v[h0:h1]) for k, v in ex.items()}
+    t0 = time.perf_counter()
+    oracle.prefill(sl["x"], sl["B"], sl["C"], sl["dt"], sl["lam"], sl["theta"], sl["A"], sl["D"])
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_all_cores(w, max_workers=16):
+    """The same oracle over every batch row, each split into two head halves,
+    one task per worker process on the host's cores (at most `max_workers`,
+    the host share of one GPU); wall time of the parallel region."""
+    import multiprocessing as mp
+    workers = max(1, min(max_workers, os.cpu_count() or 1))
+    tasks = [(w.name, r, h0, h0 + w.heads // 2) for r in range(w.batch) for h0 in (0, w.heads // 2)]
+    ctx = mp.get_context("spawn")  # children never touch the GPU
+    try:
+        with ctx.Pool(workers) as pool:
+            pool.map_async(_cpu_model_noop, range(workers)).get(timeout=300)  # workers up before the clock
+            t0 = time.perf_counter()
+            per_task = pool.map_async(_oracle_task, tasks).get(timeout=600)
+            wall = time.perf_counter() - t0
+    except Exception as e:  # a worker that cannot start must not hang the bench
+        return {"error": f"{type(e).__name__}: {e}"}
+    toks = w.batch * w.seqlen
+    return {"value": round(toks / wall / 1e6, 8), "unit": "Mtokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {w.batch} batch rows, each as two halves of the {w.heads} heads, {len(tasks)} tasks over "
+                      f"{workers} processes (numpy fp64, one thread each), {wall:.1f} s wall, "
+                      f"{sum(per_task):.1f} s summed task time"}
+
+
+def _cpu_model_noop(_):
+    return 0
+
+
+def cpu_decode_ms(w, steps=3):
+    """The oracle's decode step on one decode workload (all batch x heads at
+    once, numpy fp64, one thread): milliseconds per step over `steps` steps."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import contextlib
+    import oracle
+    from state_space_sequence_prefill_amd import synthetic as syn
+    ex = syn.as_exact(syn.draw(w, 2001, seqlen=steps), w.io_dtype)
+    state = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        t0 = time.perf_counter()
+        for t in range(steps):
+            _, state = oracle.decode_step(ex["x"][:, t], ex["B"][:, t], ex["C"][:, t], ex["dt"][:, t],
+                                          ex["lam"][:, t], ex["theta"][:, t], ex["A"], ex["D"], state)
+        el = time.perf_counter() - t0
+    return round(el / steps * 1e3, 2)
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -600,6 +670,12 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(w)
+        log("bench: cpu baseline (oracle, all host cores)")
+        line["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(w)
+        if "extra" in line:
+            for name in ("decode_mimo_r4_n64", "decode_siso_n128"):
+                log(f"bench: cpu decode (oracle) {name}")
+                line["extra"][name]["cpu_oracle_ms_per_step"] = cpu_decode_ms(syn.WORKLOADS[name])
     print(json.dumps(line), flush=True)
 
 
