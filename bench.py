@@ -471,6 +471,34 @@ def profile_copy(steps):
     log(f"bench: {steps} state copies of {dst.h.numel() * 4} bytes done")
 
 
+def measured_copy_gbs(steps=20):
+    """Achieved HBM bandwidth of a plain copy on this GPU: the library's copy
+    kernel moving a 256 MiB fp32 state (m3_state_load; read + written bytes
+    over the average launch time, HIP events), beside the 8 TB/s spec."""
+    import torch
+    import state_space_sequence_prefill_amd as m3
+    d = m3.make_dims(256, 32, 64, 128, 1, 64, "bf16")
+    dst = m3.State.empty(d)
+    src = m3.State.empty(d)
+    src.h.fill_(1.0)
+    src.B_prev.zero_()
+    src.x_prev.zero_()
+    for _ in range(5):
+        m3.m3_state_load(d, dst, src.h, src.B_prev, src.x_prev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        m3.m3_state_load(d, dst, src.h, src.B_prev, src.x_prev)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    moved = 2 * (dst.h.numel() * 4 + dst.B_prev.numel() * dst.B_prev.element_size()
+                 + dst.x_prev.numel() * dst.x_prev.element_size())
+    del dst, src
+    torch.cuda.empty_cache()
+    return round(moved / (ms / 1e3) / 1e9, 1)
+
+
 def _counter_per_dispatch(run_dir, counter, kernel_substr, largest=False):
     """Mean (or, with largest, the maximum) value per dispatch of a counter
     from a rocprofv3 counter_collection.csv under run_dir."""
@@ -581,6 +609,10 @@ def main():
     }
     del pf
     torch.cuda.empty_cache()
+    log("bench: copy bandwidth")
+    cg = measured_copy_gbs()
+    line["roofline"]["measured_copy_GBs"] = cg
+    line["roofline"]["frac_of_measured_copy"] = round(achieved / cg, 4)
 
     if not args.no_extra:
         extra = {}
