@@ -28,6 +28,7 @@ namespace m3 {
 namespace {
 
 typedef float f32x4m __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4m __attribute__((ext_vector_type(4)));  // (a vector type, so the staging array stays in registers)
 
 template <typename IO, int N, int R>
 struct MimoLds {
@@ -89,10 +90,10 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   constexpr int gB = R * N * (int)sizeof(IO) / 16;
   const int gX = R * P * (int)sizeof(IO) / 16;
   const int gAll = L::granules(P);
-  const uint4* const gsrc[6] = {reinterpret_cast<const uint4*>(Bp_), reinterpret_cast<const uint4*>(Bc_),
-                                reinterpret_cast<const uint4*>(Cc_), reinterpret_cast<const uint4*>(xp_),
-                                reinterpret_cast<const uint4*>(x),
-                                reinterpret_cast<const uint4*>(a.theta + (size_t)head * (N / 2))};
+  const u32x4m* const gsrc[6] = {reinterpret_cast<const u32x4m*>(Bp_), reinterpret_cast<const u32x4m*>(Bc_),
+                                  reinterpret_cast<const u32x4m*>(Cc_), reinterpret_cast<const u32x4m*>(xp_),
+                                  reinterpret_cast<const u32x4m*>(x),
+                                  reinterpret_cast<const u32x4m*>(a.theta + (size_t)head * (N / 2))};
   const int gstart[6] = {0, gB, 2 * gB, 3 * gB, 3 * gB + gX, 3 * gB + 2 * gX};
   // output epilogue operands first: the wait below then covers them as well
   const bool gated = a.gz != nullptr;
@@ -100,12 +101,12 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   if (gated)
     gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * (a.gdown ? 1 : R) * P, a.gw + (size_t)hh * P,
                   a.gdown != nullptr, P, wave, nthr / kWave, lane);
-  uint4 gv[KG];
+  u32x4m gv[KG];
 #pragma unroll
   for (int k = 0; k < KG; ++k) {
     int e = tid + k * nthr;
     e = e < gAll ? e : gAll - 1;  // clamped duplicate, not stored
-    const uint4* src = gsrc[0] + e;
+    const u32x4m* src = gsrc[0] + e;
 #pragma unroll
     for (int q = 1; q < 6; ++q) src = e >= gstart[q] ? gsrc[q] + (e - gstart[q]) : src;
     gv[k] = *src;
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
 #pragma unroll
   for (int k = 0; k < KG; ++k) {
     const int e = tid + k * nthr;
-    if (e < gAll) reinterpret_cast<uint4*>(dsm)[e] = gv[k];
+    if (e < gAll) reinterpret_cast<u32x4m*>(dsm)[e] = gv[k];
   }
   // the old pending pair is read once the operand loads retired (at most NB
   // loads, the state's, outstanding); after the barrier it may be overwritten
