@@ -205,10 +205,11 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
   const float lam = a.lam[head];
   const float Ah = a.A[hh];
   const float Dh = a.D[hh];
-  const uint4* const gsrc[6] = {reinterpret_cast<const uint4*>(Bp_), reinterpret_cast<const uint4*>(Bc_),
-                                reinterpret_cast<const uint4*>(Cc_), reinterpret_cast<const uint4*>(xp_),
-                                reinterpret_cast<const uint4*>(x),
-                                reinterpret_cast<const uint4*>(a.theta + (size_t)head * (N / 2))};
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // (a vector type: the staging array stays in registers)
+  const u32x4* const gsrc[6] = {reinterpret_cast<const u32x4*>(Bp_), reinterpret_cast<const u32x4*>(Bc_),
+                                reinterpret_cast<const u32x4*>(Cc_), reinterpret_cast<const u32x4*>(xp_),
+                                reinterpret_cast<const u32x4*>(x),
+                                reinterpret_cast<const u32x4*>(a.theta + (size_t)head * (N / 2))};
   const int gstart[6] = {0, gB, 2 * gB, 3 * gB, 3 * gB + gX, 3 * gB + 2 * gX};
   // BC-normalisation weights of this lane's 4 columns, and the output
   // epilogue operands, first: the wait below then covers them as well
@@ -225,12 +226,12 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
                   a.gdown != nullptr, P, wave, nthr / kWave, lane);
   // KG granules per thread (the launch picks KG with KG * threads >= total);
   // every load is unconditional (clamped duplicates are not stored)
-  uint4 gv[KG];
+  u32x4 gv[KG];
 #pragma unroll
   for (int k = 0; k < KG; ++k) {
     int e = threadIdx.x + k * nthr;
     e = e < gAll ? e : gAll - 1;
-    const uint4* src = gsrc[0] + e;  // segment by selects, no branch around the load
+    const u32x4* src = gsrc[0] + e;  // segment by selects, no branch around the load
 #pragma unroll
     for (int q = 1; q < 6; ++q) src = e >= gstart[q] ? gsrc[q] + (e - gstart[q]) : src;
     gv[k] = *src;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
 #pragma unroll
   for (int k = 0; k < KG; ++k) {
     const int e = threadIdx.x + k * nthr;
-    if (e < gAll) reinterpret_cast<uint4*>(dsm)[e] = gv[k];
+    if (e < gAll) reinterpret_cast<u32x4*>(dsm)[e] = gv[k];
   }
   // The old pending pair has been read once the operand loads retired (at
   // most IT loads, the state's, still outstanding); after the barrier every
