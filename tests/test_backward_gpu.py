@@ -70,16 +70,29 @@ def check_backward(w, seed, disc=0, st=None, with_dh=True):
 
 
 @pytest.mark.parametrize("io,P,N,R,T", [
-    ("f32", 16, 16, 1, 64),      # 4 sub-chunks of 16 tokens
-    ("f32", 32, 32, 2, 50),      # 8-token sub-chunks, ragged tail
+    ("f32", 16, 16, 1, 64),      # one full unit of 64 tokens
+    ("f32", 32, 32, 2, 50),      # units of 32 tokens, ragged tail
     ("bf16", 64, 128, 1, 100),   # the headline family, ragged tail
-    ("bf16", 64, 64, 4, 37),     # MIMO rank 4: 4-token sub-chunks
-    ("f32", 16, 64, 4, 9),
+    ("bf16", 64, 64, 4, 37),     # MIMO rank 4: units of 16 tokens
+    ("f32", 16, 64, 4, 9),       # one partial unit
     ("f32", 128, 64, 2, 20),
+    ("bf16", 64, 128, 1, 197),   # four units, the last of 5 tokens
 ])
 def test_backward_shapes(io, P, N, R, T):
     w = W("tiny_siso_f32", batch=2, heads=3, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=T)
     check_backward(w, seed=2000 + P + N + R + T, st=syn.draw_state(w, 2001))
+
+
+TILE_SHAPES = [(P, N) for P in (16, 32, 64, 128) for N in (16, 32, 64, 128) if P * N <= 8192]
+
+
+@pytest.mark.parametrize("P,N", TILE_SHAPES)
+def test_backward_every_tile_shape(P, N):
+    """Every (P/16, N/16) the kernels are instantiated for, over two units
+    (one ragged), alternating the I/O dtype."""
+    io = "f32" if (P + N) % 64 else "bf16"
+    w = W("tiny_siso_f32", batch=1, heads=2, headdim=P, dstate=N, rank=1, io_dtype=io, seqlen=70)
+    check_backward(w, seed=2200 + P + N, st=syn.draw_state(w, 2201))
 
 
 @pytest.mark.parametrize("disc", [1, 2])
@@ -123,5 +136,27 @@ def test_backward_full_size_sampled():
            "dh0": g["dh0"][b:b + 1, h:h + 1]}
     errs = {k: relerr(v, ref[k]) for k, v in sel.items()}
     print("[backward full size, chain (3, 17)] " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+
+
+def test_backward_full_size_sampled_mimo():
+    """The MIMO rank-4 shape (8 x 32 chains, 4096 tokens, N 64): one chain
+    against the oracle."""
+    w = syn.WORKLOADS["mimo_r4_t4096"]
+    ex, st_ex, dy, dh, g = run_backward(w, seed=2150)
+    b, h = 5, 9
+    pairs = [(b, h)]
+    args = oracle_args(ex, pairs)
+    ref = oracle.prefill_backward(args["x"], args["Bm"], args["Cm"], args["dt"], args["lam"], args["theta"],
+                                  args["A"], args["D"], state_slice(st_ex, pairs), dy[b:b + 1, :, h:h + 1],
+                                  dh_final=dh[b:b + 1, h:h + 1])
+    sel = {k: g[k][b:b + 1, :, h:h + 1] for k in ("dx", "dB", "dC", "ddt", "dlam", "dtheta")}
+    sel["dh0"] = g["dh0"][b:b + 1, h:h + 1]
+    sel["dB_prev"] = g["dB_prev"][b:b + 1, h:h + 1]
+    sel["dx_prev"] = g["dx_prev"][b:b + 1, h:h + 1]
+    errs = {k: relerr(v, ref[k]) for k, v in sel.items() if np.linalg.norm(ref[k]) > 0}
+    print("[backward full size MIMO, chain (5, 9)] " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()),
+          flush=True)
     for k, v in errs.items():
         assert v <= TOL, (k, v)
