@@ -500,6 +500,370 @@ __global__ __launch_bounds__(kScanT) void scan_kernel(BackwardArgs a, BwdWs ws, 
 }
 
 // ============================ grad ============================
+// The compute of one unit for the wave that owns row block KB (steps 1-6 of
+// grad_kernel).  Instantiated per block so that the masked tiles (queries
+// before keys) drop out at compile time.
+template <typename IO, int PB, int NB, int KB>
+__device__ __forceinline__ void grad_body(const BackwardArgs& a, const float* Eg, float* sm, const Lay& ly, int H,
+                                          int L, int rs, float Dh, size_t tb) {
+  constexpr int P = 16 * PB, N = 16 * NB, NH = N / 2, LDX = P + 4, LDB = N + 4, LDPH = NH + 1;
+  const int R = 1 << rs;
+  float* sX = sm + ly.oX;
+  float* sdY = sm + ly.odY;
+  float* sG = sm + ly.oG;
+  float* sBt = sm + ly.oBt;
+  float* sCt = sm + ly.oCt;
+  float* sPhi = sm + ly.oPhi;
+  float* ss = sm + ly.oSm;
+  float* sTk = ss + oTk;
+  const float* tL2 = sTk + kL2 * 64;
+  const float* tBe = sTk + kBe * 64;
+  const float* tGa = sTk + kGa * 64;
+  const float* tW = sTk + kW * 64;
+  const float* tEl = sTk + kEl * 64;
+  const size_t tokBC = (size_t)H * R * N, tokX = (size_t)H * R * P;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int nrow = L << rs;
+
+  // ---- 1. scores: S[q][k] = Ct_q . Bt_k, Pm[q][k] = dY_q . X_k for the
+  //         16 columns k of this wave's block and every row q ----
+  f32x4 S[4], Pm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S[i] = Pm[i] = zero4();
+  // (row blocks qb < KB hold earlier tokens than every column: masked, skipped)
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    const f32x4 bb = ld4(sBt + (16 * KB + c) * LDB + 16 * s + 4 * g);
+    f32x4 aa[4];
+#pragma unroll
+    for (int qb = KB; qb < 4; ++qb) aa[qb] = ld4(sCt + (16 * qb + c) * LDB + 16 * s + 4 * g);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int qb = KB; qb < 4; ++qb) S[qb] = mfma4(aa[qb][v], bb[v], S[qb]);
+  }
+#pragma unroll
+  for (int s = 0; s < PB; ++s) {
+    const f32x4 bb = ld4(sX + (16 * KB + c) * LDX + 16 * s + 4 * g);
+    f32x4 aa[4];
+#pragma unroll
+    for (int qb = KB; qb < 4; ++qb) aa[qb] = ld4(sdY + (16 * qb + c) * LDX + 16 * s + 4 * g);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int qb = KB; qb < 4; ++qb) Pm[qb] = mfma4(aa[qb][v], bb[v], Pm[qb]);
+  }
+
+  // ---- 2. mask: M(q, k) = gamma_k e^{l_q - l_k} + beta_{k+1} e^{l_q - l_{k+1}} [k < q]
+  //         (token indices); dM = S . Pm gives the pairs' shares of dgamma,
+  //         dbeta (column sums) and dl (row sums); S and Pm become M.S, M.Pm ----
+  {
+    const int tk = (16 * KB + c) >> rs;
+    const int tk1 = min(tk + 1, 63);
+    const float lk = tL2[tk], lk1 = tL2[tk1], gk = tGa[tk], bk1 = tBe[tk1];
+    float cg = 0.f, cb = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      if (qb < KB) {  // masked block: no pair terms, zero row sums
+#pragma unroll
+        for (int v = 0; v < 4; v += R)
+          if (c == 0) ss[oDlp + KB * 64 + ((16 * qb + 4 * g + v) >> rs)] = 0.f;
+        continue;
+      }
+      float rl[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tq = (16 * qb + 4 * g + v) >> rs;
+        const bool on = tq < L && tk <= tq;
+        const float lq = tL2[tq];
+        const float e1 = on ? __builtin_amdgcn_exp2f(lq - lk) : 0.f;
+        const float e2 = (on && tk < tq) ? __builtin_amdgcn_exp2f(lq - lk1) : 0.f;
+        const float m = gk * e1 + bk1 * e2;
+        const float sv = S[qb][v], pv = Pm[qb][v], d = sv * pv;
+        cg += d * e1;
+        cb += d * e2;
+        rl[v] = d * m;
+        S[qb][v] = m * sv;
+        Pm[qb][v] = m * pv;
+      }
+      rank_sum4(rl, rs);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (v & (R - 1)) continue;
+        const float r = lane_group_sum(rl[v], 16);
+        if (c == 0) ss[oDlp + KB * 64 + ((16 * qb + 4 * g + v) >> rs)] = r;
+      }
+    }
+    cg += __shfl_xor(cg, 16, kWave);
+    cg += __shfl_xor(cg, 32, kWave);
+    cb += __shfl_xor(cb, 16, kWave);
+    cb += __shfl_xor(cb, 32, kWave);
+    cg = lane_group_sum(cg, R);
+    cb = lane_group_sum(cb, R);
+    if (g == 0 && (c & (R - 1)) == 0) {
+      ss[oDga + tk] = cg;
+      ss[oDbe + tk + 1] = cb;
+    }
+  }
+
+  // ---- 3. GB[k][p] = Bt_k . G_p; dw_k = X_k . GB_k;
+  //         dX = w GB + D dY + (M.S)^T dY, rows of this wave's block ----
+  {
+    f32x4 acc[PB];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) acc[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const f32x4 aa = ld4(sBt + (16 * KB + c) * LDB + 16 * s + 4 * g);
+      f32x4 bb[PB];
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb) bb[pb] = ld4(sG + (16 * pb + c) * LDB + 16 * s + 4 * g);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) acc[pb] = mfma4(aa[v], bb[pb][v], acc[pb]);
+    }
+    float dwv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dwv[v] += sX[(16 * KB + 4 * g + v) * LDX + 16 * pb + c] * acc[pb][v];
+    rank_sum4(dwv, rs);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (v & (R - 1)) continue;
+      const float r = lane_group_sum(dwv[v], 16);
+      if (c == 0) ss[oDw + ((16 * KB + 4 * g + v) >> rs)] = r;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int k = 16 * KB + 4 * g + v;
+      const float wr = tW[k >> rs];
+#pragma unroll
+      for (int pb = 0; pb < PB; ++pb) acc[pb][v] = wr * acc[pb][v] + Dh * sdY[k * LDX + 16 * pb + c];
+    }
+#pragma unroll
+    for (int qb = KB; qb < 4; ++qb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float av = S[qb][v];
+        const float* yr = sdY + (16 * qb + 4 * g + v) * LDX + c;
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) acc[pb] = mfma4(av, yr[16 * pb], acc[pb]);
+      }
+    float* dXg = a.dx + tb * R * P;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int k = 16 * KB + 4 * g + v;
+      if (k < nrow) {
+        float* o = dXg + (size_t)(k >> rs) * tokX + (k & (R - 1)) * P + c;
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) o[16 * pb] = acc[pb][v];
+      }
+    }
+  }
+
+  // ---- 4. GX[k][n] = X_k . G[:, n]; dBt = w GX + (M.Pm)^T Ct, rows of this
+  //         block; the end angle's share through the update weights ----
+  f32x4 db[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) db[i] = zero4();
+#pragma unroll
+  for (int s = 0; s < PB; ++s) {
+    const f32x4 aa = ld4(sX + (16 * KB + c) * LDX + 16 * s + 4 * g);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float* gr = sG + (16 * s + 4 * g + v) * LDB + c;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) db[nb] = mfma4(aa[v], gr[16 * nb], db[nb]);
+    }
+  }
+  {
+    float wr[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wr[v] = tW[(16 * KB + 4 * g + v) >> rs];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = 16 * nb + c;
+      float ph = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int k = 16 * KB + 4 * g + v;
+        const float gx = db[nb][v], gxo = xor1(gx);
+        ph += wr[v] * (sBt[k * LDB + n] * gxo - sBt[k * LDB + (n ^ 1)] * gx);  // even lanes: Bt0 GX1 - Bt1 GX0
+      }
+      ph += __shfl_xor(ph, 16, kWave);
+      ph += __shfl_xor(ph, 32, kWave);
+      if (g == 0 && !(c & 1)) ss[oPhB + KB * 64 + (n >> 1)] = ph;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) db[nb][v] *= wr[v];
+    }
+  }
+#pragma unroll
+  for (int qb = KB; qb < 4; ++qb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float av = Pm[qb][v];
+      const float* cr = sCt + (16 * qb + 4 * g + v) * LDB + c;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) db[nb] = mfma4(av, cr[16 * nb], db[nb]);
+    }
+
+  // E (the unit's entry value) for the carried product of step 5, loaded here
+  // (fragment order: lane (g, c) of tile (s, nb) holds E[16 s + 4 g + v][16 nb + c], v = 0..3)
+  f32x4 ev[PB][NB];
+#pragma unroll
+  for (int s = 0; s < PB; ++s)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ev[s][nb] = reinterpret_cast<const f32x4*>(Eg)[(s * NB + nb) * 64 + lane];
+  // ---- 5. PmT[k][q] = X_k . dY_q (rows q of this block, every k);
+  //         carry[q][n] = dY_q . E[:, n]; dCt = e^l carry + (M.Pm) Bt;
+  //         <G, E> and the end angle's share through E ----
+  f32x4 dc[NB];
+  {
+    f32x4 PT[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) PT[i] = zero4();
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dc[i] = zero4();
+    float ge = 0.f, pha[2] = {0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < PB; ++s) {
+      const f32x4 yb = ld4(sdY + (16 * KB + c) * LDX + 16 * s + 4 * g);
+      f32x4 xa[4];  // (key blocks kb > KB hold later tokens than every query here: masked, skipped)
+#pragma unroll
+      for (int kb = 0; kb <= KB; ++kb) xa[kb] = ld4(sX + (16 * kb + c) * LDX + 16 * s + 4 * g);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int kb = 0; kb <= KB; ++kb) PT[kb] = mfma4(xa[kb][v], yb[v], PT[kb]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dc[nb] = mfma4(yb[v], ev[s][nb][v], dc[nb]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if ((nb & 3) != KB) continue;  // pair columns nb = KB (mod 4)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int p = 16 * s + 4 * g + v, n = 16 * nb + c;
+          const float e = ev[s][nb][v];
+          const float eo = xor1(e);
+          const float gs = sG[p * LDB + n], go = sG[p * LDB + (n ^ 1)];
+          ge += gs * e;
+          pha[nb >> 2] += go * e - gs * eo;  // even lanes: G1 E0 - G0 E1
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int nb = KB + 4 * i;
+      if (nb >= NB) continue;
+      float v = pha[i];
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      if (g == 0 && !(c & 1)) ss[oPhA + ((16 * nb + c) >> 1)] = v;
+    }
+    ge = lane_group_sum(ge, kWave);
+    if (lane == 0) ss[oGE + KB] = ge;
+    // carried part of dl: e^{l_q} sum_n carry[q][n] Ct[q][n]
+    float dl4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dl4[v] += dc[nb][v] * sCt[(16 * KB + 4 * g + v) * LDB + 16 * nb + c];
+    rank_sum4(dl4, rs);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (v & (R - 1)) continue;
+      const float r = lane_group_sum(dl4[v], 16);
+      const int tq = (16 * KB + 4 * g + v) >> rs;
+      if (c == 0) ss[oDlc + tq] = tEl[tq] * r;
+    }
+    // mask of the transposed tiles: rows k = 16 kb + 4 g + v, column q = 16 KB + c
+    {
+      const int tq = (16 * KB + c) >> rs;
+      const float lq = tL2[tq];
+#pragma unroll
+      for (int kb = 0; kb <= KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tk = (16 * kb + 4 * g + v) >> rs, tk1 = min(tk + 1, 63);
+          const bool on = tq < L && tk <= tq;
+          const float e1 = on ? __builtin_amdgcn_exp2f(lq - tL2[tk]) : 0.f;
+          const float e2 = (on && tk < tq) ? __builtin_amdgcn_exp2f(lq - tL2[tk1]) : 0.f;
+          PT[kb][v] *= tGa[tk] * e1 + tBe[tk1] * e2;
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float el = tEl[(16 * KB + 4 * g + v) >> rs];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dc[nb][v] *= el;
+    }
+#pragma unroll
+    for (int kb = 0; kb <= KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float av = PT[kb][v];
+        const float* br = sBt + (16 * kb + 4 * g + v) * LDB + c;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) dc[nb] = mfma4(av, br[16 * nb], dc[nb]);
+      }
+  }
+  // <dY, X> over the unit (D's gradient)
+  {
+    float yx = 0.f;
+#pragma unroll
+    for (int i = 0; i < kU * P / kBT; ++i) {
+      const int e = threadIdx.x + i * kBT, rho = e / P, p = e % P;
+      yx += sdY[rho * LDX + p] * sX[rho * LDX + p];
+    }
+    yx = lane_group_sum(yx, kWave);
+    if (lane == 0) ss[oRed + KB] = yx;
+  }
+  __syncthreads();  // X, dY and G are dead: their space takes the angle gradients
+
+  // ---- 6. rows back to the lab frame (dB, dC); angle gradient per (token, pair) ----
+  float* sDphi = sm + ly.oX;
+  {
+    float* dBg = a.dB + tb * R * N;
+    float* dCg = a.dC + tb * R * N;
+    const bool odd = c & 1;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = 16 * nb + c, j = n >> 1;
+      float phs[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * KB + 4 * g + v, t = row >> rs;
+        const float bq = db[nb][v], bo = xor1(bq);
+        const float cq = dc[nb][v], co = xor1(cq);
+        const float d0 = odd ? bo : bq, d1 = odd ? bq : bo;
+        const float e0 = odd ? co : cq, e1 = odd ? cq : co;
+        if (row < nrow) {
+          float sn, cs;
+          trig<IO>(sPhi[t * LDPH + j], sn, cs);
+          const size_t o = (size_t)t * tokBC + (row & (R - 1)) * N + n;
+          dBg[o] = odd ? d0 * sn + d1 * cs : d0 * cs - d1 * sn;  // Rot(+phi)
+          dCg[o] = odd ? e0 * sn + e1 * cs : e0 * cs - e1 * sn;
+        }
+        const float* br = sBt + row * LDB + (n & ~1);
+        const float* cr = sCt + row * LDB + (n & ~1);
+        phs[v] = d0 * br[1] - d1 * br[0] + e0 * cr[1] - e1 * cr[0];
+      }
+      rank_sum4(phs, rs);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (v & (R - 1)) continue;
+        if (!odd) sDphi[((16 * KB + 4 * g + v) >> rs) * LDPH + j] = phs[v];
+      }
+    }
+  }
+  __syncthreads();
+
+}
+
 // One workgroup per CU (its LDS), one wave per SIMD: the whole register file
 // is this wave's.
 template <typename IO, int PB, int NB>
@@ -561,338 +925,14 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   store_rot2<IO, N>(bin, cin, sPhi, rs, L, sBt, sCt);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-  const int nrow = L << rs;
-
-  // ---- 1. scores: S[q][k] = Ct_q . Bt_k, Pm[q][k] = dY_q . X_k for the
-  //         16 columns k of this wave's block and every row q ----
-  f32x4 S[4], Pm[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) S[i] = Pm[i] = zero4();
-#pragma unroll
-  for (int s = 0; s < NB; ++s) {
-    const f32x4 bb = ld4(sBt + (16 * wv + c) * LDB + 16 * s + 4 * g);
-    f32x4 aa[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) aa[qb] = ld4(sCt + (16 * qb + c) * LDB + 16 * s + 4 * g);
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) S[qb] = mfma4(aa[qb][v], bb[v], S[qb]);
+  switch (threadIdx.x >> 6) {
+    case 0: grad_body<IO, PB, NB, 0>(a, Eg, sm, ly, H, L, rs, Dh, tb); break;
+    case 1: grad_body<IO, PB, NB, 1>(a, Eg, sm, ly, H, L, rs, Dh, tb); break;
+    case 2: grad_body<IO, PB, NB, 2>(a, Eg, sm, ly, H, L, rs, Dh, tb); break;
+    default: grad_body<IO, PB, NB, 3>(a, Eg, sm, ly, H, L, rs, Dh, tb); break;
   }
-#pragma unroll
-  for (int s = 0; s < PB; ++s) {
-    const f32x4 bb = ld4(sX + (16 * wv + c) * LDX + 16 * s + 4 * g);
-    f32x4 aa[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) aa[qb] = ld4(sdY + (16 * qb + c) * LDX + 16 * s + 4 * g);
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) Pm[qb] = mfma4(aa[qb][v], bb[v], Pm[qb]);
-  }
-
-  // ---- 2. mask: M(q, k) = gamma_k e^{l_q - l_k} + beta_{k+1} e^{l_q - l_{k+1}} [k < q]
-  //         (token indices); dM = S . Pm gives the pairs' shares of dgamma,
-  //         dbeta (column sums) and dl (row sums); S and Pm become M.S, M.Pm ----
-  {
-    const int tk = (16 * wv + c) >> rs;
-    const int tk1 = min(tk + 1, 63);
-    const float lk = tL2[tk], lk1 = tL2[tk1], gk = tGa[tk], bk1 = tBe[tk1];
-    float cg = 0.f, cb = 0.f;
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      float rl[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tq = (16 * qb + 4 * g + v) >> rs;
-        const bool on = tq < L && tk <= tq;
-        const float lq = tL2[tq];
-        const float e1 = on ? __builtin_amdgcn_exp2f(lq - lk) : 0.f;
-        const float e2 = (on && tk < tq) ? __builtin_amdgcn_exp2f(lq - lk1) : 0.f;
-        const float m = gk * e1 + bk1 * e2;
-        const float sv = S[qb][v], pv = Pm[qb][v], d = sv * pv;
-        cg += d * e1;
-        cb += d * e2;
-        rl[v] = d * m;
-        S[qb][v] = m * sv;
-        Pm[qb][v] = m * pv;
-      }
-      rank_sum4(rl, rs);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (v & (R - 1)) continue;
-        const float r = lane_group_sum(rl[v], 16);
-        if (c == 0) ss[oDlp + wv * 64 + ((16 * qb + 4 * g + v) >> rs)] = r;
-      }
-    }
-    cg += __shfl_xor(cg, 16, kWave);
-    cg += __shfl_xor(cg, 32, kWave);
-    cb += __shfl_xor(cb, 16, kWave);
-    cb += __shfl_xor(cb, 32, kWave);
-    cg = lane_group_sum(cg, R);
-    cb = lane_group_sum(cb, R);
-    if (g == 0 && (c & (R - 1)) == 0) {
-      ss[oDga + tk] = cg;
-      ss[oDbe + tk + 1] = cb;
-    }
-  }
-
-  // ---- 3. GB[k][p] = Bt_k . G_p; dw_k = X_k . GB_k;
-  //         dX = w GB + D dY + (M.S)^T dY, rows of this wave's block ----
-  {
-    f32x4 acc[PB];
-#pragma unroll
-    for (int i = 0; i < PB; ++i) acc[i] = zero4();
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      const f32x4 aa = ld4(sBt + (16 * wv + c) * LDB + 16 * s + 4 * g);
-      f32x4 bb[PB];
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb) bb[pb] = ld4(sG + (16 * pb + c) * LDB + 16 * s + 4 * g);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int pb = 0; pb < PB; ++pb) acc[pb] = mfma4(aa[v], bb[pb][v], acc[pb]);
-    }
-    float dwv[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) dwv[v] += sX[(16 * wv + 4 * g + v) * LDX + 16 * pb + c] * acc[pb][v];
-    rank_sum4(dwv, rs);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (v & (R - 1)) continue;
-      const float r = lane_group_sum(dwv[v], 16);
-      if (c == 0) ss[oDw + ((16 * wv + 4 * g + v) >> rs)] = r;
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int k = 16 * wv + 4 * g + v;
-      const float wr = tW[k >> rs];
-#pragma unroll
-      for (int pb = 0; pb < PB; ++pb) acc[pb][v] = wr * acc[pb][v] + Dh * sdY[k * LDX + 16 * pb + c];
-    }
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float av = S[qb][v];
-        const float* yr = sdY + (16 * qb + 4 * g + v) * LDX + c;
-#pragma unroll
-        for (int pb = 0; pb < PB; ++pb) acc[pb] = mfma4(av, yr[16 * pb], acc[pb]);
-      }
-    float* dXg = a.dx + tb * R * P;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int k = 16 * wv + 4 * g + v;
-      if (k < nrow) {
-        float* o = dXg + (size_t)(k >> rs) * tokX + (k & (R - 1)) * P + c;
-#pragma unroll
-        for (int pb = 0; pb < PB; ++pb) o[16 * pb] = acc[pb][v];
-      }
-    }
-  }
-
-  // ---- 4. GX[k][n] = X_k . G[:, n]; dBt = w GX + (M.Pm)^T Ct, rows of this
-  //         block; the end angle's share through the update weights ----
-  f32x4 db[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) db[i] = zero4();
-#pragma unroll
-  for (int s = 0; s < PB; ++s) {
-    const f32x4 aa = ld4(sX + (16 * wv + c) * LDX + 16 * s + 4 * g);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float* gr = sG + (16 * s + 4 * g + v) * LDB + c;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) db[nb] = mfma4(aa[v], gr[16 * nb], db[nb]);
-    }
-  }
-  {
-    float wr[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wr[v] = tW[(16 * wv + 4 * g + v) >> rs];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int n = 16 * nb + c;
-      float ph = 0.f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int k = 16 * wv + 4 * g + v;
-        const float gx = db[nb][v], gxo = xor1(gx);
-        ph += wr[v] * (sBt[k * LDB + n] * gxo - sBt[k * LDB + (n ^ 1)] * gx);  // even lanes: Bt0 GX1 - Bt1 GX0
-      }
-      ph += __shfl_xor(ph, 16, kWave);
-      ph += __shfl_xor(ph, 32, kWave);
-      if (g == 0 && !(c & 1)) ss[oPhB + wv * 64 + (n >> 1)] = ph;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) db[nb][v] *= wr[v];
-    }
-  }
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float av = Pm[qb][v];
-      const float* cr = sCt + (16 * qb + 4 * g + v) * LDB + c;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) db[nb] = mfma4(av, cr[16 * nb], db[nb]);
-    }
-
-  // E (the unit's entry value) for the carried product of step 5, loaded here
-  // (fragment order: lane (g, c) of tile (s, nb) holds E[16 s + 4 g + v][16 nb + c], v = 0..3)
-  f32x4 ev[PB][NB];
-#pragma unroll
-  for (int s = 0; s < PB; ++s)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) ev[s][nb] = reinterpret_cast<const f32x4*>(Eg)[(s * NB + nb) * 64 + lane];
-  // ---- 5. PmT[k][q] = X_k . dY_q (rows q of this block, every k);
-  //         carry[q][n] = dY_q . E[:, n]; dCt = e^l carry + (M.Pm) Bt;
-  //         <G, E> and the end angle's share through E ----
-  f32x4 dc[NB];
-  {
-    f32x4 PT[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) PT[i] = zero4();
-#pragma unroll
-    for (int i = 0; i < NB; ++i) dc[i] = zero4();
-    float ge = 0.f, pha[2] = {0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < PB; ++s) {
-      const f32x4 yb = ld4(sdY + (16 * wv + c) * LDX + 16 * s + 4 * g);
-      f32x4 xa[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) xa[kb] = ld4(sX + (16 * kb + c) * LDX + 16 * s + 4 * g);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) PT[kb] = mfma4(xa[kb][v], yb[v], PT[kb]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) dc[nb] = mfma4(yb[v], ev[s][nb][v], dc[nb]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if ((nb & 3) != wv) continue;  // pair columns nb = wv (mod 4)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int p = 16 * s + 4 * g + v, n = 16 * nb + c;
-          const float e = ev[s][nb][v];
-          const float eo = xor1(e);
-          const float gs = sG[p * LDB + n], go = sG[p * LDB + (n ^ 1)];
-          ge += gs * e;
-          pha[nb >> 2] += go * e - gs * eo;  // even lanes: G1 E0 - G0 E1
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int nb = wv + 4 * i;
-      if (nb >= NB) continue;
-      float v = pha[i];
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      if (g == 0 && !(c & 1)) ss[oPhA + ((16 * nb + c) >> 1)] = v;
-    }
-    ge = lane_group_sum(ge, kWave);
-    if (lane == 0) ss[oGE + wv] = ge;
-    // carried part of dl: e^{l_q} sum_n carry[q][n] Ct[q][n]
-    float dl4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) dl4[v] += dc[nb][v] * sCt[(16 * wv + 4 * g + v) * LDB + 16 * nb + c];
-    rank_sum4(dl4, rs);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (v & (R - 1)) continue;
-      const float r = lane_group_sum(dl4[v], 16);
-      const int tq = (16 * wv + 4 * g + v) >> rs;
-      if (c == 0) ss[oDlc + tq] = tEl[tq] * r;
-    }
-    // mask of the transposed tiles: rows k = 16 kb + 4 g + v, column q = 16 wv + c
-    {
-      const int tq = (16 * wv + c) >> rs;
-      const float lq = tL2[tq];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tk = (16 * kb + 4 * g + v) >> rs, tk1 = min(tk + 1, 63);
-          const bool on = tq < L && tk <= tq;
-          const float e1 = on ? __builtin_amdgcn_exp2f(lq - tL2[tk]) : 0.f;
-          const float e2 = (on && tk < tq) ? __builtin_amdgcn_exp2f(lq - tL2[tk1]) : 0.f;
-          PT[kb][v] *= tGa[tk] * e1 + tBe[tk1] * e2;
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float el = tEl[(16 * wv + 4 * g + v) >> rs];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) dc[nb][v] *= el;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float av = PT[kb][v];
-        const float* br = sBt + (16 * kb + 4 * g + v) * LDB + c;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) dc[nb] = mfma4(av, br[16 * nb], dc[nb]);
-      }
-  }
-  // <dY, X> over the unit (D's gradient)
-  {
-    float yx = 0.f;
-#pragma unroll
-    for (int i = 0; i < kU * P / kBT; ++i) {
-      const int e = threadIdx.x + i * kBT, rho = e / P, p = e % P;
-      yx += sdY[rho * LDX + p] * sX[rho * LDX + p];
-    }
-    yx = lane_group_sum(yx, kWave);
-    if (lane == 0) ss[oRed + wv] = yx;
-  }
-  __syncthreads();  // X, dY and G are dead: their space takes the angle gradients
-
-  // ---- 6. rows back to the lab frame (dB, dC); angle gradient per (token, pair) ----
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float* sDphi = sm + ly.oX;
-  {
-    float* dBg = a.dB + tb * R * N;
-    float* dCg = a.dC + tb * R * N;
-    const bool odd = c & 1;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int n = 16 * nb + c, j = n >> 1;
-      float phs[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 16 * wv + 4 * g + v, t = row >> rs;
-        const float bq = db[nb][v], bo = xor1(bq);
-        const float cq = dc[nb][v], co = xor1(cq);
-        const float d0 = odd ? bo : bq, d1 = odd ? bq : bo;
-        const float e0 = odd ? co : cq, e1 = odd ? cq : co;
-        if (row < nrow) {
-          float sn, cs;
-          trig<IO>(sPhi[t * LDPH + j], sn, cs);
-          const size_t o = (size_t)t * tokBC + (row & (R - 1)) * N + n;
-          dBg[o] = odd ? d0 * sn + d1 * cs : d0 * cs - d1 * sn;  // Rot(+phi)
-          dCg[o] = odd ? e0 * sn + e1 * cs : e0 * cs - e1 * sn;
-        }
-        const float* br = sBt + row * LDB + (n & ~1);
-        const float* cr = sCt + row * LDB + (n & ~1);
-        phs[v] = d0 * br[1] - d1 * br[0] + e0 * cr[1] - e1 * cr[0];
-      }
-      rank_sum4(phs, rs);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (v & (R - 1)) continue;
-        if (!odd) sDphi[((16 * wv + 4 * g + v) >> rs) * LDPH + j] = phs[v];
-      }
-    }
-  }
-  __syncthreads();
 
   // ---- 7. token scalars (wave 0, lane t = token) and angles ----
   const float elE = sMisc[1];
