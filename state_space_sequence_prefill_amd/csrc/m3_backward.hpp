@@ -388,6 +388,188 @@ __global__ __launch_bounds__(kBT) void local_kernel(BackwardArgs a, BwdWs ws, in
   }
 }
 
+// ======================== local, bf16 inputs ========================
+// The same U_u and V_u on the bf16 matrix cores.  bf16 inputs are exact bf16
+// numbers, so x (or dy) enters v_mfma_f32_16x16x32_bf16 as it is, and the fp32
+// factor w B~ (or e^l C~) as three bf16 parts hi + mid + lo whose sum is that
+// fp32 value exactly (each part takes the next 8 bits of the 24-bit
+// significand); products of bf16 numbers are exact in fp32 and the sums run
+// in fp32, so the three products give the fp32 result at a sixth of the
+// matrix-core time of v_mfma_f32_16x16x4_f32.  Both operands sit in LDS
+// transposed (K = the unit's 64 rows contiguous): rows of 64 bf16 (128 B)
+// whose 16-byte chunks are XOR-swizzled by the row index, so the fragment
+// reads (16 rows, one chunk each) spread over the banks.
+typedef __bf16 bf16x2l __attribute__((ext_vector_type(2)));
+
+// byte offset of element k of row r in a transposed tile
+__device__ __forceinline__ int tt_off(int r, int k) { return r * 128 + ((((k >> 3) ^ r) & 7) << 4) + ((k & 7) << 1); }
+
+// RPT consecutive K values of one row (all in one 16-byte chunk)
+template <int RPT>
+__device__ __forceinline__ void tt_store(char* base, int r, int k0, const float (&v)[RPT]) {
+  char* p = base + tt_off(r, k0);
+  if constexpr (RPT == 8) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = o;
+  } else if constexpr (RPT == 4) {
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x4*>(p) = o;
+  } else if constexpr (RPT == 2) {
+    bf16x2l o;
+    o[0] = (bf16)v[0];
+    o[1] = (bf16)v[1];
+    *reinterpret_cast<bf16x2l*>(p) = o;
+  } else {
+    *reinterpret_cast<bf16*>(p) = (bf16)v[0];
+  }
+}
+
+// Columns of a (token, rank)-major bf16 input: thread t holds columns
+// 4 (t % (W/4)) .. + 3 of the W/16 consecutive rows starting at
+// (t / (W/4)) W/16, as raw bf16 pairs (rows past the end re-read row 0).
+template <int W>
+struct ColsIn {
+  static constexpr int CG = W / 4, RPT = kU * CG / kBT;
+  static_assert(RPT >= 1 && RPT <= 8 && (kU * CG) % kBT == 0, "rows per thread");
+  uint32_t lo[RPT], hi[RPT];
+  __device__ __forceinline__ void load(const bf16* g, size_t tok, int rs, int L) {
+    const int cg = threadIdx.x % CG, r0 = (threadIdx.x / CG) * RPT;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int rho = r0 + i, rr = rho < (L << rs) ? rho : 0;
+      const uint2 w = *reinterpret_cast<const uint2*>(g + (size_t)(rr >> rs) * tok + (rr & ((1 << rs) - 1)) * W + 4 * cg);
+      lo[i] = w.x;
+      hi[i] = w.y;
+    }
+  }
+  // element e (0..3) of row i as fp32
+  __device__ __forceinline__ float get(int i, int e) const {
+    const uint32_t w = e < 2 ? lo[i] : hi[i];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+
+template <int PB, int NB>
+__global__ __launch_bounds__(kBT) void local_bf_kernel(BackwardArgs a, BwdWs ws, int H, int rs, int nu) {
+  constexpr int P = 16 * PB, N = 16 * NB, NH = N / 2, LDPH = NH + 1;
+  using XC = ColsIn<P>;
+  using BC = ColsIn<N>;
+  extern __shared__ __align__(16) float sm[];
+  char* const sXT = reinterpret_cast<char*>(sm);  // (P rows, 64 K) bf16
+  char* const sPL = sXT + P * 128;                 // 3 planes of (N rows, 64 K) bf16: lo, mid, hi
+  float* const sPhi = reinterpret_cast<float*>(sPL + 3 * N * 128);
+  const int R = 1 << rs, Qu = kU >> rs;
+  const int which = blockIdx.x & 1, unit = blockIdx.x >> 1;
+  const int chain = unit / nu, u = unit - chain * nu;
+  const int hh = chain % H, b = chain / H;
+  const int T = a.seqlen, t0 = u * Qu, L = min(Qu, T - t0);
+  const bool nxt = t0 + L < T;
+  float* sTk = sPhi + Qu * LDPH + oTk;
+  float* sMisc = sPhi + Qu * LDPH + oMisc;
+  const size_t tokBC = (size_t)H * R * N, tokX = (size_t)H * R * P, tokTh = (size_t)H * NH;
+  const size_t tb = ((size_t)b * T + t0) * H + hh;  // (b, t0, h)
+  CoefIn<NH> ci;
+  ci.load(a.dt + tb, a.lam + tb, a.theta + tb * NH, H, tokTh, L, nxt);
+  XC xin;
+  xin.load(static_cast<const bf16*>(which ? a.dy : a.x) + tb * R * P, tokX, rs, L);
+  BC bin;
+  bin.load(static_cast<const bf16*>(which ? a.C : a.B) + tb * R * N, tokBC, rs, L);
+  unit_coefs<NH>(ci, a.A[hh], a.disc, L, nxt, Qu, sTk, sMisc, sPhi);
+
+  const int nrow = L << rs;
+  {  // x (or dy) transposed, rows past the end as zeros
+    const int cg = threadIdx.x % XC::CG, r0 = (threadIdx.x / XC::CG) * XC::RPT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v[XC::RPT];
+#pragma unroll
+      for (int i = 0; i < XC::RPT; ++i) v[i] = r0 + i < nrow ? xin.get(i, e) : 0.f;
+      tt_store<XC::RPT>(sXT, 4 * cg + e, r0, v);
+    }
+  }
+  {  // w B~ (or e^l C~) rotated back per token, split into three planes
+    const float* tw = sTk + (which ? kEl : kW) * 64;
+    const int cg = threadIdx.x % BC::CG, r0 = (threadIdx.x / BC::CG) * BC::RPT;
+    float pv[3][4][BC::RPT];  // [plane][column][row]
+#pragma unroll
+    for (int i = 0; i < BC::RPT; ++i) {
+      const int rho = r0 + i, t = rho >> rs;
+      const float wt = rho < nrow ? tw[t] : 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float sn, cs;
+        trig<bf16>(sPhi[t * LDPH + 2 * cg + h], sn, cs);
+        const float b0 = bin.get(i, 2 * h), b1 = bin.get(i, 2 * h + 1);
+        const float r2[2] = {wt * (b0 * cs + b1 * sn), wt * (b1 * cs - b0 * sn)};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float vh = (float)(bf16)r2[q];
+          const float rem = r2[q] - vh;
+          const float vm = (float)(bf16)rem;
+          pv[2][2 * h + q][i] = vh;
+          pv[1][2 * h + q][i] = vm;
+          pv[0][2 * h + q][i] = rem - vm;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tt_store<BC::RPT>(sPL + q * N * 128, 4 * cg + e, r0, pv[q][e]);
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  const size_t slot = ((size_t)chain * nu + u) * P * N;
+  float* Og = (which ? ws.ckG : ws.ckE) + slot;
+  const float* phE = sPhi + (L - 1) * LDPH;
+  constexpr int kTiles = PB * NB, kPer = (kTiles + 3) / 4;
+#pragma unroll
+  for (int ti = 0; ti < kPer; ++ti) {
+    const int tile = wv + 4 * ti;
+    if (tile >= kTiles) break;
+    const int pb = tile / NB, nb = tile % NB;
+    const int p = 16 * pb + c, n = 16 * nb + c;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kc = 4 * ks + g;
+      const bf16x8 xa = *reinterpret_cast<const bf16x8*>(sXT + p * 128 + (((kc ^ p) & 7) << 4));
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sPL + (q * N + n) * 128 + (((kc ^ n) & 7) << 4));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bb, acc, 0, 0, 0);
+      }
+    }
+    f32x4 o = acc;
+    if (!which) {  // U: each (p, pair) turned by the unit's end angle
+      const bool odd = c & 1;
+      float sn, cs;
+      trig<bf16>(phE[n >> 1], sn, cs);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float mine = acc[v], other = xor1(mine);
+        const float u0 = odd ? other : mine, u1 = odd ? mine : other;
+        o[v] = odd ? u0 * sn + u1 * cs : u0 * cs - u1 * sn;
+      }
+    }
+    reinterpret_cast<f32x4*>(Og)[(size_t)(pb * NB + nb) * 64 + lane] = o;
+  }
+  if (!which) {
+    const size_t us = (size_t)chain * nu + u;
+    for (int j = threadIdx.x; j < NH; j += kBT) {
+      float sn, cs;
+      trig<bf16>(phE[j], sn, cs);
+      reinterpret_cast<float2*>(ws.ucs)[us * NH + j] = make_float2(cs, sn);
+    }
+    if (threadIdx.x == 0) ws.uel[us] = sMisc[1];
+  }
+}
+
 // ============================ scan ============================
 // One thread per (chain, 4 rows p, rotation pair): E_u forward from the entry
 // value, then G_u backward from dh_final; the slots are read (U_u, V_u) and
@@ -1074,8 +1256,12 @@ hipError_t launch_io_pn(const Dims& d, const BackwardArgs& a, const BwdWs& w, hi
   constexpr int P = 16 * PB, N = 16 * NB;
   static bool attr_set = false;
   if (!attr_set) {
-    for (const void* f : {reinterpret_cast<const void*>(&local_kernel<IO, PB, NB>),
-                          reinterpret_cast<const void*>(&grad_kernel<IO, PB, NB>)}) {
+    const void* local;
+    if constexpr (sizeof(IO) == 2)
+      local = reinterpret_cast<const void*>(&local_bf_kernel<PB, NB>);
+    else
+      local = reinterpret_cast<const void*>(&local_kernel<IO, PB, NB>);
+    for (const void* f : {local, reinterpret_cast<const void*>(&grad_kernel<IO, PB, NB>)}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
     }
@@ -1088,7 +1274,12 @@ hipError_t launch_io_pn(const Dims& d, const BackwardArgs& a, const BwdWs& w, hi
   const size_t lds_local = (size_t)(kU * (P + 4) + kU * (N + 4) + (kU / d.R) * (N / 2 + 1) + kSmall) * 4;
   const size_t lds_grad = (size_t)Lay(P, N, d.R, true).total * 4;
   const dim3 units((unsigned)chains * nu), blk(kBT);
-  hipLaunchKernelGGL((local_kernel<IO, PB, NB>), dim3(2 * units.x), blk, lds_local, s, a, w, d.heads, rs, nu);
+  if constexpr (sizeof(IO) == 2) {
+    const size_t lds_bf = (size_t)(P + 3 * N) * 128 + (size_t)((kU / d.R) * (N / 2 + 1) + kSmall) * 4;
+    hipLaunchKernelGGL((local_bf_kernel<PB, NB>), dim3(2 * units.x), blk, lds_bf, s, a, w, d.heads, rs, nu);
+  } else {
+    hipLaunchKernelGGL((local_kernel<IO, PB, NB>), dim3(2 * units.x), blk, lds_local, s, a, w, d.heads, rs, nu);
+  }
   hipLaunchKernelGGL(scan_kernel<IO>, dim3(chains * bpc), dim3(kScanT), 0, s, a, w, d.heads, P, N, d.R, nu, bpc);
   hipLaunchKernelGGL((grad_kernel<IO, PB, NB>), units, blk, lds_grad, s, a, w, d.heads, rs, nu);
   hipLaunchKernelGGL(finish_kernel<IO>, dim3(chains), dim3(256), 0, s, a, w, d.heads, P, N, d.R, nu);

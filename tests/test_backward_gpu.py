@@ -86,11 +86,11 @@ def test_backward_shapes(io, P, N, R, T):
 TILE_SHAPES = [(P, N) for P in (16, 32, 64, 128) for N in (16, 32, 64, 128) if P * N <= 8192]
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("P,N", TILE_SHAPES)
-def test_backward_every_tile_shape(P, N):
-    """Every (P/16, N/16) the kernels are instantiated for, over two units
-    (one ragged), alternating the I/O dtype."""
-    io = "f32" if (P + N) % 64 else "bf16"
+def test_backward_every_tile_shape(P, N, io):
+    """Every (P/16, N/16) the kernels are instantiated for, in both I/O dtypes
+    (bf16 inputs take their own local kernel), over two units (one ragged)."""
     w = W("tiny_siso_f32", batch=1, heads=2, headdim=P, dstate=N, rank=1, io_dtype=io, seqlen=70)
     check_backward(w, seed=2200 + P + N, st=syn.draw_state(w, 2201))
 
