@@ -1007,15 +1007,16 @@ __device__ __forceinline__ void grad_body(const BackwardArgs& a, const float* Eg
   __syncthreads();  // X, dY and G are dead: their space takes the angle gradients
 
   // ---- 6. rows back to the lab frame (dB, dC); angle gradient per (token, pair) ----
+  // After the barrier above every wave reads only its own 16 rows of Bt and
+  // Ct, so each overwrites them with its dB, dC rows (after reading them for
+  // the angle gradient) and writes those rows out as whole 16-byte runs.
   float* sDphi = sm + ly.oX;
   {
-    float* dBg = a.dB + tb * R * N;
-    float* dCg = a.dC + tb * R * N;
     const bool odd = c & 1;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = 16 * nb + c, j = n >> 1;
-      float phs[4];
+      float phs[4], ob[4], oc[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 16 * KB + 4 * g + v, t = row >> rs;
@@ -1023,22 +1024,40 @@ __device__ __forceinline__ void grad_body(const BackwardArgs& a, const float* Eg
         const float cq = dc[nb][v], co = xor1(cq);
         const float d0 = odd ? bo : bq, d1 = odd ? bq : bo;
         const float e0 = odd ? co : cq, e1 = odd ? cq : co;
-        if (row < nrow) {
-          float sn, cs;
-          trig<IO>(sPhi[t * LDPH + j], sn, cs);
-          const size_t o = (size_t)t * tokBC + (row & (R - 1)) * N + n;
-          dBg[o] = odd ? d0 * sn + d1 * cs : d0 * cs - d1 * sn;  // Rot(+phi)
-          dCg[o] = odd ? e0 * sn + e1 * cs : e0 * cs - e1 * sn;
-        }
+        float sn, cs;
+        trig<IO>(sPhi[t * LDPH + j], sn, cs);
+        ob[v] = odd ? d0 * sn + d1 * cs : d0 * cs - d1 * sn;  // Rot(+phi)
+        oc[v] = odd ? e0 * sn + e1 * cs : e0 * cs - e1 * sn;
         const float* br = sBt + row * LDB + (n & ~1);
         const float* cr = sCt + row * LDB + (n & ~1);
         phs[v] = d0 * br[1] - d1 * br[0] + e0 * cr[1] - e1 * cr[0];
+      }
+      // (the wave's reads above precede these writes in its LDS queue)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * KB + 4 * g + v;
+        sBt[row * LDB + n] = ob[v];
+        sCt[row * LDB + n] = oc[v];
       }
       rank_sum4(phs, rs);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         if (v & (R - 1)) continue;
         if (!odd) sDphi[((16 * KB + 4 * g + v) >> rs) * LDPH + j] = phs[v];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float* dBg = a.dB + tb * R * N;
+    float* dCg = a.dC + tb * R * N;
+    constexpr int Q4 = N / 4, kIt = 16 * Q4 / kWave;  // 16-byte runs of the wave's 16 rows, per lane
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int e = lane + kWave * i, row = 16 * KB + e / Q4, q = e % Q4;
+      if (row < nrow) {
+        const size_t o = (size_t)(row >> rs) * tokBC + (row & (R - 1)) * N + 4 * q;
+        *reinterpret_cast<f32x4*>(dBg + o) = ld4(sBt + row * LDB + 4 * q);
+        *reinterpret_cast<f32x4*>(dCg + o) = ld4(sCt + row * LDB + 4 * q);
       }
     }
   }
