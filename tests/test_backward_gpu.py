@@ -95,9 +95,10 @@ def test_backward_every_tile_shape(P, N, io):
     check_backward(w, seed=2200 + P + N, st=syn.draw_state(w, 2201))
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("disc", [1, 2])
-def test_backward_discretisation_rules(disc):
-    w = W("tiny_siso_f32", batch=2, heads=2, headdim=32, dstate=32, rank=2, io_dtype="f32", seqlen=41)
+def test_backward_discretisation_rules(disc, io):
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=32, dstate=32, rank=2, io_dtype=io, seqlen=41)
     check_backward(w, seed=2100 + disc, disc=disc, st=syn.draw_state(w, 2102))
 
 
@@ -106,8 +107,9 @@ def test_backward_zero_state_without_final_cotangent():
     check_backward(w, seed=2110, with_dh=False)
 
 
-def test_backward_single_token():
-    w = W("tiny_siso_f32", batch=2, heads=2, headdim=16, dstate=16, rank=4, io_dtype="f32", seqlen=1)
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_single_token(io):
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=16, dstate=16, rank=4, io_dtype=io, seqlen=1)
     check_backward(w, seed=2120, st=syn.draw_state(w, 2121))
 
 
