@@ -98,6 +98,25 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// K slots of a bf16 16x16x32 product over two p slabs: p = 16 s + 4 g + v and
+// 16 (s + 1) + 4 g + v (v = 0..3) of an LDS row of exact bf16 values held as
+// fp32 (the conversion is exact); the second run is zero when there is no
+// slab s + 1.  Both operands of a product take the same slots.
+template <bool kTwo>
+__device__ __forceinline__ bf16x8 slab_pair(const float* p) {
+  const f32x4 a = ld4(p), b = kTwo ? ld4(p + 16) : zero4();
+  bf16x8 o;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    o[v] = (bf16)a[v];
+    o[4 + v] = (bf16)b[v];
+  }
+  return o;
+}
+__device__ __forceinline__ f32x4 mfma_bf(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = lane_group_sum(v, kWave);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -724,16 +743,26 @@ __device__ __forceinline__ void grad_body(const BackwardArgs& a, const float* Eg
 #pragma unroll
       for (int qb = KB; qb < 4; ++qb) S[qb] = mfma4(aa[qb][v], bb[v], S[qb]);
   }
+  if constexpr (sizeof(IO) == 2) {  // dY and X are exact bf16: one bf16 product per two p slabs
 #pragma unroll
-  for (int s = 0; s < PB; ++s) {
-    const f32x4 bb = ld4(sX + (16 * KB + c) * LDX + 16 * s + 4 * g);
-    f32x4 aa[4];
+    for (int s = 0; s < PB; s += 2) {
+      const bf16x8 bb = slab_pair<(PB > 1)>(sX + (16 * KB + c) * LDX + 16 * s + 4 * g);
 #pragma unroll
-    for (int qb = KB; qb < 4; ++qb) aa[qb] = ld4(sdY + (16 * qb + c) * LDX + 16 * s + 4 * g);
+      for (int qb = KB; qb < 4; ++qb)
+        Pm[qb] = mfma_bf(slab_pair<(PB > 1)>(sdY + (16 * qb + c) * LDX + 16 * s + 4 * g), bb, Pm[qb]);
+    }
+  } else {
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int s = 0; s < PB; ++s) {
+      const f32x4 bb = ld4(sX + (16 * KB + c) * LDX + 16 * s + 4 * g);
+      f32x4 aa[4];
 #pragma unroll
-      for (int qb = KB; qb < 4; ++qb) Pm[qb] = mfma4(aa[qb][v], bb[v], Pm[qb]);
+      for (int qb = KB; qb < 4; ++qb) aa[qb] = ld4(sdY + (16 * qb + c) * LDX + 16 * s + 4 * g);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int qb = KB; qb < 4; ++qb) Pm[qb] = mfma4(aa[qb][v], bb[v], Pm[qb]);
+    }
   }
 
   // ---- 2. mask: M(q, k) = gamma_k e^{l_q - l_k} + beta_{k+1} e^{l_q - l_{k+1}} [k < q]
@@ -909,16 +938,27 @@ __device__ __forceinline__ void grad_body(const BackwardArgs& a, const float* Eg
 #pragma unroll
     for (int i = 0; i < NB; ++i) dc[i] = zero4();
     float ge = 0.f, pha[2] = {0.f, 0.f};
+    if constexpr (sizeof(IO) == 2) {  // exact bf16 operands, as Pm
+#pragma unroll
+      for (int s = 0; s < PB; s += 2) {
+        const bf16x8 yq = slab_pair<(PB > 1)>(sdY + (16 * KB + c) * LDX + 16 * s + 4 * g);
+#pragma unroll
+        for (int kb = 0; kb <= KB; ++kb)
+          PT[kb] = mfma_bf(slab_pair<(PB > 1)>(sX + (16 * kb + c) * LDX + 16 * s + 4 * g), yq, PT[kb]);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < PB; ++s) {
       const f32x4 yb = ld4(sdY + (16 * KB + c) * LDX + 16 * s + 4 * g);
-      f32x4 xa[4];  // (key blocks kb > KB hold later tokens than every query here: masked, skipped)
+      if constexpr (sizeof(IO) != 2) {
+        f32x4 xa[4];  // (key blocks kb > KB hold later tokens than every query here: masked, skipped)
 #pragma unroll
-      for (int kb = 0; kb <= KB; ++kb) xa[kb] = ld4(sX + (16 * kb + c) * LDX + 16 * s + 4 * g);
+        for (int kb = 0; kb <= KB; ++kb) xa[kb] = ld4(sX + (16 * kb + c) * LDX + 16 * s + 4 * g);
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int kb = 0; kb <= KB; ++kb) PT[kb] = mfma4(xa[kb][v], yb[v], PT[kb]);
+          for (int kb = 0; kb <= KB; ++kb) PT[kb] = mfma4(xa[kb][v], yb[v], PT[kb]);
+      }
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
