@@ -27,9 +27,13 @@
 //           the first token's alpha and beta), the first-token terms each
 //           unit hands to the next, and the sums over units.
 // The contractions run on the matrix cores in fp32 (v_mfma_f32_16x16x4_f32)
-// from LDS tiles; everything else is fp32 VALU.  Gradients are fp32.  The
-// local and grad kernels are instantiated per (P / 16, N / 16), so that every
-// tile loop has a fixed trip count.
+// from LDS tiles; everything else is fp32 VALU.  Gradients are fp32.  With
+// bf16 inputs, x and dy are exact bf16 numbers, so the products whose other
+// operand is exact too (dY X^T, X dY^T) run on v_mfma_f32_16x16x32_bf16, and
+// the local summaries take their fp32 factor as three exact bf16 parts
+// (local_bf_kernel); the results are those of the fp32 products up to the
+// order of the fp32 sums.  The local and grad kernels are instantiated per
+// (P / 16, N / 16), so that every tile loop has a fixed trip count.
 //
 // MFMA fragments (16 x 16 x 4, wave64): lane (g = lane / 16, c = lane % 16)
 // gives A[i = c][k = g] and B[k = g][j = c] and holds D[i = 4 g + v][j = c]
