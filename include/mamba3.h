@@ -91,7 +91,9 @@ typedef enum {
  *                                    Q*R rows do not fit its tiles),
  *   io_dtype in m3_dtype,
  *   disc in m3_disc (0, the default, when the struct is zero-initialised).
- * Anything else returns M3_ERR_UNSUPPORTED (or M3_ERR_SHAPE for values <= 0). */
+ * Anything else returns M3_ERR_UNSUPPORTED (or M3_ERR_SHAPE for values <= 0),
+ * as do prefill sizes whose tiles fit the 160 KiB of LDS at no tile height
+ * down to 16 tokens (fp32 I/O with N = 128 and P = 128, or N = 128 and R = 4). */
 typedef struct {
   int32_t batch, heads, headdim, dstate, rank, chunk;
   int32_t io_dtype;

@@ -60,10 +60,10 @@ int check_dims(const m3_dims* d, bool need_chunk, m3::Dims* out) {
   const bool supported = need_chunk ? m3::prefill_supported(m) : m3::decode_supported(m);
   if (!supported)
     return fail(M3_ERR_UNSUPPORTED,
-                "unsupported sizes headdim=%d dstate=%d rank=%d chunk=%d (supported: headdim in "
+                "unsupported sizes headdim=%d dstate=%d rank=%d chunk=%d %s (supported: headdim in "
                 "{16,32,64,128}, dstate in {16,32,64,128}, rank in {1,2,4}, chunk in {16,32,64}, "
-                "chunk*rank <= 256)",
-                d->headdim, d->dstate, d->rank, d->chunk);
+                "chunk*rank <= 256, and prefill tiles that fit the LDS at some tile height >= 16 tokens)",
+                d->headdim, d->dstate, d->rank, d->chunk, d->io_dtype == M3_BF16 ? "bf16" : "f32");
   *out = m;
   return M3_OK;
 }

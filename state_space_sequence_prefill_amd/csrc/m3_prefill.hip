@@ -829,8 +829,11 @@ bool prefill_supported(const Dims& d) {
   const bool q_ok = d.Q == 16 || d.Q == 32 || d.Q == 64;
   if (!(n_ok && p_ok && r_ok && q_ok)) return false;
   if (d.Q * d.R > 256) return false;
+  // the producer/consumer kernel at the chunk or at a halved tile height (the
+  // chunk length is a tile height; the result does not depend on it)
+  if (prefill_pc_path_supported(d)) return true;
   const int rows_pad = ((d.Q * d.R) + 31) & ~31;
-  return prefill_pc_supported(d) || rows_pad <= (d.bf16 ? max_rows<bf16>(d) : max_rows<float>(d));
+  return rows_pad <= (d.bf16 ? max_rows<bf16>(d) : max_rows<float>(d));
 }
 
 int prefill_tile_chunk(const Dims& d) {

@@ -93,10 +93,17 @@ def test_prefill_rejects_bad_dims(field, value, status):
     assert B.m3_last_error()
 
 
-def test_prefill_lds_limit_is_unsupported():
-    # fp32 I/O with N = 128 and a 64-token chunk does not fit 160 KiB of LDS
-    assert call_prefill(dims(io_dtype="f32", dstate=128, chunk=64)) == B.M3_ERR_UNSUPPORTED
-    assert call_prefill(dims(rank=4, chunk=64, dstate=128)) == B.M3_ERR_UNSUPPORTED
+def test_prefill_tile_height_and_lds_limit():
+    # The chunk length is a tile height (the chunked form gives the same result
+    # for any chunk): where chunk x rank rows do not fit 160 KiB of LDS the
+    # library tiles with half or a quarter of the chunk, so fp32 I/O with N =
+    # 128 at a 64-token chunk (32-token tiles) and rank 4 with N = 128 at a
+    # 64-token chunk (16-token tiles) are accepted (seqlen 0: checks only) ...
+    assert call_prefill(dims(io_dtype="f32", dstate=128, chunk=64), seqlen=0) == B.M3_OK
+    assert call_prefill(dims(rank=4, chunk=64, dstate=128), seqlen=0) == B.M3_OK
+    # ... and shapes whose rows fit no tile height down to 16 tokens are refused
+    assert call_prefill(dims(io_dtype="f32", dstate=128, rank=4, chunk=16)) == B.M3_ERR_UNSUPPORTED
+    assert call_prefill(dims(io_dtype="f32", dstate=128, headdim=128, chunk=64)) == B.M3_ERR_UNSUPPORTED
 
 
 def test_decode_checks_dims():
