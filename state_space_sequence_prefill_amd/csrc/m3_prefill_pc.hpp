@@ -588,6 +588,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       for (int j = pt; j < 2 * N; j += kProdThreads)
         sGw[j] = j < N ? a.nbw[(size_t)hh * N + j] : a.ncw[(size_t)hh * N + j - N];
     }
+    // bf16 I/O keeps two chunks of raw inputs in flight; fp32 I/O, whose raw
+    // chunk takes twice the registers, one (loaded right after the tiles of
+    // the previous one are built, so it arrives during the consumers' phase)
+    constexpr bool kTwoAhead = sizeof(IO) == 2;
     if (ck0 < ck1) {
       // prologue: coefficients of the first chunk, then the first prefetches
       const int n1 = ck0 + 1 < ck1 ? ck0 + 1 : ck0;
@@ -597,18 +601,34 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
       load_chunk(ck0, rsA);
       if (pw == 0) load_dt(n1);
-      load_chunk(n1, rsB);
+      if constexpr (kTwoAhead) load_chunk(n1, rsB);
       norm_partials(rsA);
     }
     __syncthreads();
-    // the pair loop has no conditional loads, so the wait counts the compiler
-    // derives around its back edge stay exact (only the batch consumed waits)
-    int i = ck0;
-    for (; i + 1 < ck1; i += 2) {
-      step(i, rsA, rsB);
-      step(i + 1, rsB, rsA);
+    if constexpr (kTwoAhead) {
+      // the pair loop has no conditional loads, so the wait counts the compiler
+      // derives around its back edge stay exact (only the batch consumed waits)
+      int i = ck0;
+      for (; i + 1 < ck1; i += 2) {
+        step(i, rsA, rsB);
+        step(i + 1, rsB, rsA);
+      }
+      if (i < ck1) step(i, rsA, rsB);
+    } else {
+      for (int i = ck0; i < ck1; ++i) {
+        build_tiles(i, rsA);
+        __syncthreads();
+        const int n1 = i + 1 < ck1 ? i + 1 : i;
+        const int n2 = i + 2 < ck1 ? i + 2 : n1;
+        if (pw == 0) {
+          decay_coefs(n1, n1 != i);
+          load_dt(n2);
+        }
+        load_chunk(n1, rsA);
+        norm_partials(rsA);
+        __syncthreads();
+      }
     }
-    if (i < ck1) step(i, rsA, rsB);
     __syncthreads();
     __syncthreads();
   } else {
