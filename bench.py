@@ -21,7 +21,7 @@ only a few warm-up steps the timed region measures the clock ramp.  The same JSO
                    1000 steps captured in a HIP graph, plus a run with a
                    512 MiB cache flush between steps), MIMO / 16K-token
                    prefill throughput, the headline shape under the other two
-                   discretisation rules, and the gated entry points (pre-gate
+                   discretisation rules and with fp32 I/O, and the gated entry points (pre-gate
                    grouped RMSNorm fused into the store of y) on the headline
                    prefill and both decode shapes, BC normalisation, the MIMO
                    rank down-projection, and the backward pass (all gradients)
@@ -642,6 +642,18 @@ def main():
                                          "hbm_frac": round(nbytes / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
             del p
             torch.cuda.empty_cache()
+        # fp32 I/O on the headline shape (x, B, C, y in fp32; 32-token tiles)
+        wf = w.with_(io_dtype="f32")
+        log(f"bench: prefill {w.name} fp32 I/O")
+        p = Prefill(wf, seed=1005)
+        ms, kms = p.time(max(3, args.steps // 2), 2)
+        nbf = prefill_bytes(wf)
+        extra[f"{w.name}_f32io"] = {"ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                                    "Mtokens_per_s": round(w.batch * w.seqlen / ms / 1e3, 3),
+                                    "algorithmic_bytes": nbf,
+                                    "hbm_frac": round(nbf / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del p
+        torch.cuda.empty_cache()
         # the output epilogue (pre-gate grouped RMSNorm) fused into the store
         # of y: the headline shape and both decode shapes
         log(f"bench: gated prefill {w.name}")
