@@ -146,6 +146,13 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   constexpr int NK = L::NK, LDN = L::LDN, PAD = L::PAD;
   constexpr int NS = NK / 32;
   constexpr int MI = Lim::kMI, MX = Lim::kMX, PBW = Lim::kPBW;
+  // Split producer roles when a chunk holds at most half as many B/C items
+  // (and x items) as there are producer threads: waves 0-1 then take the B
+  // rows of the items (B~, its weighted tile, the end rotations), waves 2-3
+  // the C rows and x, so each thread rotates one matrix instead of two and no
+  // wave works on duplicates only.
+  constexpr bool kSplit = (Lim::kMaxRows / 4) * (N / 8) <= kProdThreads / 2 &&
+                          (Lim::kMaxRows / 4) * (P / 8) <= kProdThreads / 2;
   // Tiles always hold RMAX rows; rows past Q*R stay zero, so every consumer
   // loop has compile-time bounds.
   // (instances whose tiles do not fit at all are never launched; they compile
@@ -244,6 +251,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // would make the compiler wait for all outstanding loads.
     const int pt = tid;
     const int pw = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform producer index
+    const bool crole = kSplit && pw >= 2;                 // split roles: this thread's rows are C's
     const int RG = rows_pad / 4;
     const int npg = N / 8;
     const int GW = npg < 64 / RG ? npg : 64 / RG;  // pair groups per lane group
@@ -270,7 +278,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     uint32_t ox[MX][4], oxs[MX];
 #pragma unroll
     for (int m = 0; m < MI; ++m) {
-      const int it0 = pt + m * kProdThreads;
+      const int it0 = (kSplit ? pt & (kProdThreads / 2 - 1) : pt) + m * kProdThreads;
       ist[m] = it0 < nbitems;
       const int it = ist[m] ? it0 : it0 % nbitems;
       const int rg = (it / GW) % RG, pg = (it / (GW * RG)) * GW + it % GW;
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     }
 #pragma unroll
     for (int m = 0; m < MX; ++m) {
-      const int it0 = pt + m * kProdThreads;
+      const int it0 = (kSplit ? pt ^ (kProdThreads / 2) : pt) + m * kProdThreads;  // split: waves 2-3
       xst[m] = it0 < nxitems;
       const int it = xst[m] ? it0 : it0 % nxitems;
       const int rg = (it / GX) % RG, xg = (it / (GX * RG)) * GX + it % GX;
@@ -315,8 +323,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const uint32_t o = rtok[m][k] < Lc ? ob[m][k] : obs[m];
-          rs.b[m][k].load(Bc + o);
-          rs.c[m][k].load(Cc + o);
+          if constexpr (kSplit) {
+            rs.b[m][k].load((crole ? Cc : Bc) + o);  // this role's matrix
+          } else {
+            rs.b[m][k].load(Bc + o);
+            rs.c[m][k].load(Cc + o);
+          }
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -347,9 +359,14 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           for (int k = 0; k < 4; ++k) {
             pb[k] = lane_group_sum(rs.b[m][k].sumsq(), GW);
             // segment summaries never read C
-            pc[k] = has_y ? lane_group_sum(rs.c[m][k].sumsq(), GW) : 0.f;
+            pc[k] = (has_y && !kSplit) ? lane_group_sum(rs.c[m][k].sumsq(), GW) : 0.f;
           }
-          if (ist[m] && (lane & (GW - 1)) == 0) {
+          if (kSplit && ist[m] && (lane & (GW - 1)) == 0) {  // this role's matrix only
+            const int grp = ipg[m] / GW + (crole ? NG : 0);
+            *reinterpret_cast<float4*>(sPart + (size_t)grp * rows_pad + 4 * irg[m]) =
+                make_float4(pb[0], pb[1], pb[2], pb[3]);
+          }
+          if (!kSplit && ist[m] && (lane & (GW - 1)) == 0) {
             const int grp = ipg[m] / GW;
             *reinterpret_cast<float4*>(sPart + (size_t)grp * rows_pad + 4 * irg[m]) =
                 make_float4(pb[0], pb[1], pb[2], pb[3]);
@@ -458,7 +475,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         float sclB[4] = {1.f, 1.f, 1.f, 1.f}, sclC[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (BCN) {
           float4 tb = make_float4(0.f, 0.f, 0.f, 0.f), tc = tb;
-          for (int grp = 0; grp < NG; ++grp) {
+          for (int grp = crole ? NG : 0; grp < (crole ? 2 * NG : NG); ++grp) {  // split: this role's rows
+            if (kSplit) {
+              const float4 u = *reinterpret_cast<const float4*>(sPart + (size_t)grp * rows_pad + 4 * rg);
+              tb.x += u.x; tb.y += u.y; tb.z += u.z; tb.w += u.w;
+              continue;
+            }
             const float4 u = *reinterpret_cast<const float4*>(sPart + (size_t)grp * rows_pad + 4 * rg);
             const float4 w = *reinterpret_cast<const float4*>(sPart + (size_t)(NG + grp) * rows_pad + 4 * rg);
             tb.x += u.x; tb.y += u.y; tb.z += u.z; tb.w += u.w;
@@ -482,7 +504,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           rs.b[m][k].unpack(bv);
           if constexpr (BCN) {  // column weights read where used (registers are scarce here)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bv[e] *= sGw[8 * pg + e] * sclB[k];
+            for (int e = 0; e < 8; ++e) bv[e] *= sGw[(crole ? N : 0) + 8 * pg + e] * sclB[k];
           }
           float cs4[4], sn4[4];
 #pragma unroll
@@ -498,7 +520,8 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           for (int e = 0; e < 8; ++e) bt[k][e] = bv[e] * wt;
           // the row-major B~ and C~ tiles feed only the outputs; a segment
           // summary needs just the state update's tiles
-          if (ist[m] && has_y) {
+          if (kSplit && ist[m] && has_y) store8((crole ? bf.sC : bf.sB) + rho * LDN + 8 * pg, bv);
+          if (!kSplit && ist[m] && has_y) {
             float cv[8];
             rs.c[m][k].unpack(cv);
             if constexpr (BCN) {
@@ -510,7 +533,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             store8(bf.sB + rho * LDN + 8 * pg, bv);
             store8(bf.sC + rho * LDN + 8 * pg, cv);
           }
-          if (ist[m]) {
+          if (ist[m] && !crole) {
             if (valid && t == te && (rho & (R - 1)) == 0) {
 #pragma unroll
               for (int j = 0; j < 4; ++j)
@@ -518,7 +541,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             }
           }
         }
-        if (ist[m]) {
+        if (ist[m] && !crole) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float col[4] = {bt[0][e], bt[1][e], bt[2][e], bt[3][e]};
