@@ -93,7 +93,11 @@ typedef enum {
  *   disc in m3_disc (0, the default, when the struct is zero-initialised).
  * Anything else returns M3_ERR_UNSUPPORTED (or M3_ERR_SHAPE for values <= 0),
  * as do prefill sizes whose tiles fit the 160 KiB of LDS at no tile height
- * down to 16 tokens (fp32 I/O with N = 128 and P = 128, or N = 128 and R = 4). */
+ * down to 16 tokens: fp32 I/O with N = 128, R = 4 and P >= 64 (16 tokens x 4
+ * ranks = 64 rows of fp32 B~ and C~ at a 132-float pitch, their transposes,
+ * X^T and the score and output tiles, double buffered, exceed 160 KiB).
+ * Support does not depend on the chunk otherwise: a size accepted at chunk
+ * 16 is accepted at 32 and 64. */
 typedef struct {
   int32_t batch, heads, headdim, dstate, rank, chunk;
   int32_t io_dtype;
@@ -157,7 +161,13 @@ int mamba3_prefill_workspace_bytes(const m3_dims* dims, int32_t seqlen, size_t* 
  * seqlen == 0 is a no-op that returns M3_OK.  Results match the sequential
  * definition up to rounding: fp32 state and accumulation; with bf16 I/O the
  * rotated B/C, the masked score tile and the carried state are rounded to
- * bf16 as matrix-core operands. */
+ * bf16 as matrix-core operands.
+ * Domain: any finite inputs with dt * A <= 0 (decay).  A token's log-decay
+ * dt * A below -32 (a state reset) is raised to -32 inside the chunked
+ * kernels: such a token passes e^-32 ~ 1.3e-14 of the state before it
+ * instead of less, a change far below fp32 resolution, and no intermediate
+ * overflows for any finite decay.  Angles of any size are accepted (the bf16
+ * path reduces them to one revolution before the hardware sine). */
 int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const void* B,
                    const void* C, const float* dt, const float* lam, const float* theta,
                    const float* A, const float* D, m3_state* state, void* y,

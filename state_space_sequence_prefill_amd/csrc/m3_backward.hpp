@@ -144,11 +144,16 @@ __device__ __forceinline__ DCoef dcoef(float dt, float lam, float A, int disc) {
 }
 
 // Trig of the unit-local angles: the hardware sin/cos for bf16 I/O (as in the
-// forward kernels), sincosf for fp32 I/O.
+// forward kernels, reduced first so any angle is in its domain), sincosf for
+// fp32 I/O.
 template <typename IO> __device__ __forceinline__ void trig(float a, float& s, float& c) { sincosf(a, &s, &c); }
-template <> __device__ __forceinline__ void trig<bf16>(float a, float& s, float& c) { __sincosf(a, &s, &c); }
+template <> __device__ __forceinline__ void trig<bf16>(float a, float& s, float& c) { sincos_hw(a, s, c); }
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Log-decay below which a token's own decay gradient is taken as zero:
+// e^-24 ~ 3.8e-11 is far under the fp32 rounding of the sums it would be
+// computed from (see the token scalars of the grad kernel).
+constexpr float kDeadLogDecay = -24.0f;
 
 // The value of the neighbouring lane (lane ^ 1), by DPP.
 __device__ __forceinline__ float xor1(float v) {
@@ -195,18 +200,18 @@ __device__ __forceinline__ void unit_coefs(const CoefIn<NH>& in, float Ah, int d
 #pragma unroll
   for (int i = 0; i < CoefIn<NH>::it; ++i) {
     const int e = tid + i * kBT;
-    if (e < Qu * NH) sPhi[(e / NH) * LDPH + e % NH] = in.th[i];
+    if (e < Qu * NH) sPhi[(e / NH) * LDPH + e % NH] = reduce_angle(in.th[i]);  // small unit-local sums
   }
   if (wv == 0) {
     const int t = lane;
     const bool v = t < L;
     const float av = in.dt * Ah;
     const float2 bg = input_weights(in.dt, in.lm, expf(av), disc);
-    const float l = wave_inclusive_scan((v && t > 0) ? av : 0.f);
+    const float l = wave_inclusive_scan((v && t > 0) ? log_decay(in.dt, Ah) : 0.f);
     // the next token's decay and previous-input weight close this unit
     const float an = in.dtn * Ah;
     const float bn = nxt ? input_weights(in.dtn, in.lmn, expf(an), disc).x : 0.f;
-    const float lE = __shfl(l, L - 1, kWave) + an;
+    const float lE = __shfl(l, L - 1, kWave) + log_decay(in.dtn, Ah);
     const float l_up = __shfl_down(l, 1, kWave), be_up = __shfl_down(bg.x, 1, kWave);
     float w = 0.f;
     if (v) w = bg.y * expf(lE - l) + (t + 1 < L ? be_up * expf(lE - l_up) : bn);
@@ -1203,8 +1208,14 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float rc = lane_group_sum(dl, kWave) - pre + dl;  // sum_{s >= t} dl_s
     float dAp = 0.f;
     if (v) {
-      const float da = t > 0 ? rc + dlE : 0.f;
       const float dt = sTk[kDt * 64 + t], lm = sTk[kLm * 64 + t];
+      // Every term of the loss that depends on this token's log-decay a_t
+      // carries the factor e^{a_t}, so |da_t| <= e^{a_t} times the size of
+      // those terms.  Below kDeadLogDecay that is under the rounding noise of
+      // the suffix sum (its +M and -M terms of the pairs after the token
+      // cancel only to fp32 precision), and the noise times a large dt would
+      // swamp dA: such a token's da is zero to fp32 accuracy.
+      const float da = (t > 0 && dt * Ah >= kDeadLogDecay) ? rc + dlE : 0.f;
       const DCoef dcf = dcoef(dt, lm, Ah, a.disc);
       a.ddt[tb + (size_t)t * H] = Ah * da + dcf.bdt * dbe + dcf.gdt * dga;
       a.dlam[tb + (size_t)t * H] = dcf.blam * dbe + dcf.glam * dga;
@@ -1216,9 +1227,10 @@ __global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (sMisc[3] != 0.f) {  // the next token's decay and previous-input weight
         const float dtn = sMisc[4], lmn = sMisc[5];
         const DCoef dcn = dcoef(dtn, lmn, Ah, a.disc);
-        nd = Ah * dlE + dcn.bdt * dbn;
+        const float dan = dtn * Ah >= kDeadLogDecay ? dlE : 0.f;  // as da above
+        nd = Ah * dan + dcn.bdt * dbn;
         nl = dcn.blam * dbn;
-        dAp += dtn * dlE + dcn.bA * dbn;
+        dAp += dtn * dan + dcn.bA * dbn;
       }
       const size_t us = (size_t)chain * nu + u;
       ws.nxt[us * 2] = nd;

@@ -97,6 +97,39 @@ __device__ __forceinline__ float2 input_weights(float dt, float lam, float alpha
   return make_float2(disc == 1 ? alpha * b : b, lam * dt);
 }
 
+// Floor on a token's log-decay dt*A inside the chunked kernels: lower values
+// are raised to it before the in-chunk prefix sums.  Such a token (a state
+// reset) then passes e^-32 ~ 1.3e-14 of what came before it instead of less:
+// the change to any result is below 1.3e-14 times the magnitude of the state
+// it erases, far under fp32 resolution.  What the floor buys is precision:
+// the prefix sums are rounded relative to their size, and a reset with
+// dt*A = -1000 would otherwise leave every later difference of two prefix
+// sums with an absolute error of ~1e-4 (~4e-6 with the floor).  It also
+// keeps every exponent the kernels form finite.
+constexpr float kLogDecayFloor = -32.0f;
+__device__ __forceinline__ float log_decay(float dt, float A) { return fmaxf(dt * A, kLogDecayFloor); }
+
+// Sine and cosine of an angle of any size on the hardware units: the angle
+// is turned into revolutions, reduced to [0, 1) (an exact operation), and
+// passed to v_sin_f32 / v_cos_f32, whose own input domain is +-256
+// revolutions.  Error ~1e-6 plus the rounding of a / 2pi (2^-24 |a| / 2pi
+// revolutions): ample where the rotated operands are rounded to bf16.
+__device__ __forceinline__ void sincos_hw(float a, float& s, float& c) {
+  const float r = __builtin_amdgcn_fractf(a * 0.15915494309189535f);
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
+}
+
+// An angle reduced to about [-pi, pi]: the nearest multiple k of 2 pi is
+// subtracted in two parts, an 8-bit head (k * head is exact for |k| < 2^16)
+// and the tail.  The chunk-local angle sums of the fp32 kernels then stay
+// small enough that their rounding does not show.
+__device__ __forceinline__ float reduce_angle(float a) {
+  const float k = rintf(a * 0.15915494309189535f);
+  const float r = fmaf(-k, 6.28125f, a);
+  return fmaf(-k, 1.9353071795864769e-3f, r);
+}
+
 // Lane-crossing helpers (wave64).
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, kWave);

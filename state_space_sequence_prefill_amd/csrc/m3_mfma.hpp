@@ -84,12 +84,13 @@ __device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
 }
 
 // Trig of the chunk-local angles.  bf16 I/O rounds the rotated operands to
-// bf16 anyway, so the hardware sin/cos is ample; fp32 I/O uses sincosf.
+// bf16 anyway, so the hardware sin/cos is ample (on angles of any size:
+// sincos_hw reduces them first); fp32 I/O uses sincosf.
 template <typename IO> __device__ __forceinline__ void trig(float a, float& s, float& c) {
   sincosf(a, &s, &c);
 }
 template <> __device__ __forceinline__ void trig<bf16>(float a, float& s, float& c) {
-  __sincosf(a, &s, &c);
+  sincos_hw(a, s, c);
 }
 
 // 8 consecutive I/O elements as raw 32-bit words (4 for bf16, 8 for fp32).

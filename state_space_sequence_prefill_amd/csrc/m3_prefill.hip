@@ -322,14 +322,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
       const int t = lane;
       const bool valid = t < Lc;
       const float dtv = valid ? pf_dt : 0.f, lmv = valid ? pf_lm : 0.f;
-      const float av = (valid && t > 0) ? dtv * Ah : 0.f;
+      const float av = (valid && t > 0) ? log_decay(dtv, Ah) : 0.f;
       const float ell = wave_inclusive_scan(av);   // l_t (first token's decay is in E)
       const float2 wt = input_weights(dtv, lmv, expf(dtv * Ah), a.disc);
       const float bet = wt.x, gam = wt.y;
       const float dtn = fold_next ? pf_dtn : 0.f;
       const float lmn = fold_next ? pf_lmn : 0.f;
       const float ell_last = __shfl(ell, Lc - 1, kWave);
-      const float ellE = ell_last + dtn * Ah;
+      const float ellE = ell_last + log_decay(dtn, Ah);
       const float bet_next_tok = input_weights(dtn, lmn, expf(dtn * Ah), a.disc).x;
       const float bet_up = __shfl_down(bet, 1, kWave);
       const float ell_up = __shfl_down(ell, 1, kWave);
@@ -364,10 +364,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bool tv = 4 * tg + k < Lc;
-        ph[k][0] = tv ? pf_th[k].x : 0.f;
-        ph[k][1] = tv ? pf_th[k].y : 0.f;
-        ph[k][2] = tv ? pf_th[k].z : 0.f;
-        ph[k][3] = tv ? pf_th[k].w : 0.f;
+        ph[k][0] = tv ? reduce_angle(pf_th[k].x) : 0.f;
+        ph[k][1] = tv ? reduce_angle(pf_th[k].y) : 0.f;
+        ph[k][2] = tv ? reduce_angle(pf_th[k].z) : 0.f;
+        ph[k][3] = tv ? reduce_angle(pf_th[k].w) : 0.f;
         if (k > 0) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) ph[k][j] += ph[k - 1][j];
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(KParams kp) {
       if (mode == kSummary) {
         // running angle total of the segment (pairs); sPhi[te] is this chunk's total
         for (int j = tid; j < N / 2; j += kThreads) {
-          const float tot = s.sSeg[j] + s.sPhi[te * (N / 2) + j];
+          const float tot = reduce_angle(s.sSeg[j] + s.sPhi[te * (N / 2) + j]);
           s.sSeg[j] = tot;
           if (last_chunk) a.seg_angle[((size_t)seg * kp.batch * H + chain) * (N / 2) + j] = tot;
         }
@@ -822,38 +822,46 @@ int max_rows(const Dims& d) {
 
 }  // namespace
 
+namespace {
+// Whether the single-role kernel's tiles fit at d.Q.
+bool single_role_fits(const Dims& d) {
+  const int rows_pad = ((d.Q * d.R) + 31) & ~31;
+  return rows_pad <= (d.bf16 ? max_rows<bf16>(d) : max_rows<float>(d));
+}
+}  // namespace
+
+int prefill_tile_chunk(const Dims& d) {
+  // The chunk length is a tile height: the chunked form gives the same result
+  // for any chunk length.  The producer/consumer kernel at the largest height
+  // <= Q (halving down to 16 tokens) whose tiles fit, else the single-role
+  // kernel likewise; 0 when neither fits at any height.  Support is thereby
+  // monotone in the chunk: whatever runs at chunk 16 runs at 32 and 64.
+  for (int q = d.Q; q >= 16; q /= 2) {
+    Dims e = d;
+    e.Q = q;
+    if (prefill_pc_supported(e)) return q;
+  }
+  for (int q = d.Q; q >= 16; q /= 2) {
+    Dims e = d;
+    e.Q = q;
+    if (single_role_fits(e)) return q;
+  }
+  return 0;
+}
+
 bool prefill_supported(const Dims& d) {
   const bool n_ok = d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128;
   const bool p_ok = d.P == 16 || d.P == 32 || d.P == 64 || d.P == 128;
   const bool r_ok = d.R == 1 || d.R == 2 || d.R == 4;
   const bool q_ok = d.Q == 16 || d.Q == 32 || d.Q == 64;
   if (!(n_ok && p_ok && r_ok && q_ok)) return false;
-  if (d.Q * d.R > 256) return false;
-  // the producer/consumer kernel at the chunk or at a halved tile height (the
-  // chunk length is a tile height; the result does not depend on it)
-  if (prefill_pc_path_supported(d)) return true;
-  const int rows_pad = ((d.Q * d.R) + 31) & ~31;
-  return rows_pad <= (d.bf16 ? max_rows<bf16>(d) : max_rows<float>(d));
-}
-
-int prefill_tile_chunk(const Dims& d) {
-  // The chunk length is a tile height: the chunked form gives the same result
-  // for any chunk length.  When Q*R rows do not fit the producer/consumer
-  // kernel's tiles, halve the chunk (down to 16 tokens) rather than fall back
-  // to the single-role kernel.
-  if (prefill_pc_supported(d)) return d.Q;
-  for (int q = d.Q / 2; q >= 16; q /= 2) {
-    Dims e = d;
-    e.Q = q;
-    if (prefill_pc_supported(e)) return q;
-  }
-  return d.Q;
+  return prefill_tile_chunk(d) > 0;
 }
 
 bool prefill_pc_path_supported(const Dims& d) {
   Dims e = d;
   e.Q = prefill_tile_chunk(d);
-  return prefill_pc_supported(e);
+  return e.Q > 0 && prefill_pc_supported(e);
 }
 
 hipError_t launch_prefill(const Dims& d, const PrefillArgs& a, hipStream_t s) {

@@ -101,7 +101,7 @@ struct PcBuf {
   float4* sEnd;
 };
 struct PcCoef {
-  float4* sTok;  // [Q] {gamma, l*log2e, beta of the next token, l_next*log2e}
+  float4* sTok;  // [Q] {A_t, B_t, L_t, Kf_t}: mask exponents, log2-decay, key factor
   float* sW;     // [Q] state-update weights
   float* sMisc;  // [0] l_E, [1] l_E*log2e
 };
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     };
     // In-chunk decay scan and per-token coefficients of chunk ck -> coef slot
     // ck % 3 (producer wave 0 only, which alone loads dt and lam).
-    // sTok[t] = {A_t, B_t, L_t, 0} with L_t = l_t log2(e) and the mask weights
+    // sTok[t] = {A_t, B_t, L_t, Kf_t} with L_t = l_t log2(e) and the mask weights
     // gamma_t 2^{L_q - L_t} = 2^{L_q - A_t},  beta_{t+1} 2^{L_q - L_{t+1}} = 2^{L_q - B_t}
     // (a zero weight gives an infinite exponent and an exact zero).
     auto decay_coefs = [&](int ck, bool store) {
@@ -397,13 +397,13 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const int t = lane;
       const bool valid = t < Lc;
       const float dtv = valid ? rdt : 0.f, lmv = valid ? rlm : 0.f;
-      const float av = (valid && t > 0) ? dtv * Ah : 0.f;
+      const float av = (valid && t > 0) ? log_decay(dtv, Ah) : 0.f;
       const float ell = wave_inclusive_scan(av);
       const float2 wt = input_weights(dtv, lmv, expf(dtv * Ah), a.disc);
       const float bet = wt.x, gam = wt.y;
       const float dtn = fold_next ? rdtn : 0.f, lmn = fold_next ? rlmn : 0.f;
       const float ell_last = __shfl(ell, Lc - 1, kWave);
-      const float ellE = ell_last + dtn * Ah;
+      const float ellE = ell_last + log_decay(dtn, Ah);
       const float bet_up = __shfl_down(bet, 1, kWave);
       const float ell_up = __shfl_down(ell, 1, kWave);
       const bool inner = t < Lc - 1, lastv = t == Lc - 1;
@@ -416,12 +416,17 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       const float Ak = (valid && gam > 0.f) ? L2 - __log2f(gam) : inf;
       const float Bk = (valid && betn > 0.f) ? elln * kLog2ePc - __log2f(betn) : inf;
       // key factor for score blocks below the diagonal: with e the last token
-      // of the key's 16-row block, M[q][k] = 2^{L_q - L_e} * Kf_k for every
-      // query q after that block (both factors <= 1 except Kf's beta term at
-      // k = e, which is 1/alpha of the next token)
-      const int te = t | ((16 >> lgR) - 1);
-      const float Le = __shfl(L2, te < Lc ? te : Lc - 1, kWave);
-      const float Kf = valid ? gam * exp2f(Le - L2) + betn * exp2f(Le - elln * kLog2ePc) : 0.f;
+      // of the key's 16-row block, every query q of a later block has q >=
+      // e + 1, and M[q][k] = 2^{L_q - L_{e+1}} * Kf_k with
+      //   Kf_k = gamma_k 2^{L_{e+1} - L_k} + beta_{k+1} 2^{L_{e+1} - L_{k+1}}.
+      // Both exponents of Kf and the row factor's are <= 0 (the log-decays
+      // only fall), so neither factor overflows for any decay: Kf_k <=
+      // gamma_k + beta_{k+1}, and the row factor <= 1.  When e + 1 is past
+      // the chunk no valid query uses Kf, and L_E keeps it bounded.
+      const int te1 = (t | ((16 >> lgR) - 1)) + 1;
+      const float Le1s = __shfl(L2, te1 < Lc ? te1 : Lc - 1, kWave);
+      const float Le1 = te1 < Lc ? Le1s : ellE * kLog2ePc;
+      const float Kf = valid ? gam * exp2f(Le1 - L2) + betn * exp2f(Le1 - elln * kLog2ePc) : 0.f;
       if (store && t < Q) {
         co.sTok[t] = make_float4(Ak, Bk, L2, Kf);
         co.sW[t] = w;
@@ -449,6 +454,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           th[q][1] = tv * rs.th[m][q].y;
           th[q][2] = tv * rs.th[m][q].z;
           th[q][3] = tv * rs.th[m][q].w;
+          if constexpr (sizeof(IO) == 4) {  // fp32: keep the angle sums small (bf16's hardware trig reduces them)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) th[q][j] = reduce_angle(th[q][j]);
+          }
         }
         // exclusive prefix of the row groups' totals within the pair group
         float base[4], tot[4];
@@ -892,8 +901,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             }
             const int tq = (16 * rbq[q] + c) >> lgR;
             lq[q] = co.sTok[tq < Q ? tq : Q - 1].z;
-            const int tkl = (16 * kbq[q] + 15) >> lgR;  // last token of the key block
-            le[q] = co.sTok[tkl < Q ? tkl : Q - 1].z;
+            // first token after the key block (the factored mask's reference)
+            const int tk1 = ((16 * kbq[q] + 15) >> lgR) + 1;
+            le[q] = co.sTok[tk1 < Q ? tk1 : Q - 1].z;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               const int tk = (16 * kbq[q] + 4 * g + i4) >> lgR;
@@ -909,7 +919,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             float v[4];
             if (kbq[q] < rbq[q]) {
               // below the diagonal every key precedes every query: one row
-              // factor 2^{L_q - L_e} times the key factors
+              // factor 2^{L_q - L_{e+1}} times the key factors
               const float rf = __builtin_amdgcn_exp2f(lq[q] - le[q]);
 #pragma unroll
               for (int i4 = 0; i4 < 4; ++i4) v[i4] = St[i4] * (rf * kt[q][i4].w);
@@ -1023,7 +1033,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         if (mode == kPcSummary) {
           const int ct = tid - kProdThreads;
           if (ct < N / 2) {
-            const float tot = sSeg[ct] + bf.sEnd[ct].z;
+            const float tot = reduce_angle(sSeg[ct] + bf.sEnd[ct].z);
             sSeg[ct] = tot;
             if (last_chunk) a.seg_angle[((size_t)seg * kp.batch * H + chain) * (N / 2) + ct] = tot;
           }

@@ -18,6 +18,71 @@ def tol_for(io_dtype):
     return 2e-2 if io_dtype == "bf16" else 1e-5
 
 
+# Regression guard for bf16 I/O, separate from the 2e-2 bar: about twice the
+# largest pooled error the kernels showed on the seeded workloads (3.3e-3),
+# so a change that loses precision fails here long before it reaches the bar.
+BF16_GUARD = 7e-3
+# Per-token bound, as a multiple of the bar: ||e_t|| <= TOKEN_FACTOR * bar *
+# max(||ref_t||, 0.1 * median_t ||ref_t||) for every token t of every chain.  A
+# fault confined to some tokens (say the first of each chunk) fails it even
+# when the pooled norm hides it.
+TOKEN_FACTOR = 4.0
+
+
+# State-reset inputs (a token with dt = 1000 / |A|) give that token's input
+# weights ~1000x the others', and with bf16 I/O the carried state enters the
+# output product rounded to bf16 relative to that size: tokens shortly after a
+# reset whose output is a small difference of two large terms see up to ~0.13
+# relative error, and the pooled error up to 7.3e-3.  For such inputs the
+# regression guard is off and the per-token bound is SPREAD_TOKEN_FACTOR x the
+# bar (the pooled and per-chain bars are unchanged).
+SPREAD_TOKEN_FACTOR = 10.0
+
+
+def assert_parity(got, ref, io_dtype, label, chain_axis, token_axis=None, tol=None, guard=True, token_factor=None,
+                  spread=False):
+    """Compare a GPU result with the oracle's: the pooled relative L2 error,
+    the error of every chain (index along chain_axis) and, with token_axis,
+    every token's relative error (the floor keeps near-zero rows meaningful).
+    Prints all three; returns the pooled error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{label}: non-finite values"
+    bar = tol_for(io_dtype) if tol is None else tol
+    pooled = relerr(got, ref)
+    g = np.moveaxis(got, chain_axis, 0).reshape(got.shape[chain_axis], -1)
+    r = np.moveaxis(ref, chain_axis, 0).reshape(ref.shape[chain_axis], -1)
+    rn = np.linalg.norm(r, axis=1)
+    per_chain = np.linalg.norm(g - r, axis=1) / np.where(rn > 0, rn, 1.0)
+    msg = f"{label}: pooled {pooled:.3e}, worst chain {per_chain.max():.3e}"
+    worst_tok = None
+    if token_axis is not None:
+        ax = [chain_axis, token_axis]
+        gt = np.moveaxis(got, ax, [0, 1])
+        rt = np.moveaxis(ref, ax, [0, 1])
+        gt = gt.reshape(gt.shape[0], gt.shape[1], -1)
+        rt = rt.reshape(rt.shape[0], rt.shape[1], -1)
+        en = np.linalg.norm(gt - rt, axis=2)
+        tn = np.linalg.norm(rt, axis=2)
+        floor = 0.1 * np.median(tn, axis=1, keepdims=True)
+        rel_tok = en / np.maximum(np.maximum(tn, floor), 1e-300)
+        worst_tok = float(rel_tok.max())
+        ci, ti = np.unravel_index(int(rel_tok.argmax()), rel_tok.shape)
+        msg += f", worst token {worst_tok:.3e} (chain {ci}, token {ti})"
+    print(msg, flush=True)
+    assert pooled <= bar, msg
+    assert per_chain.max() <= bar, msg
+    if spread and io_dtype == "bf16":
+        guard = False
+        token_factor = SPREAD_TOKEN_FACTOR if token_factor is None else token_factor
+    if worst_tok is not None:
+        assert worst_tok <= (TOKEN_FACTOR if token_factor is None else token_factor) * bar, msg
+    if guard and io_dtype == "bf16" and tol is None:
+        assert pooled <= BF16_GUARD, msg
+    return pooled
+
+
 def to_gpu(arr, io_dtype, key):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
@@ -26,9 +91,15 @@ def to_gpu(arr, io_dtype, key):
     return t.cuda().contiguous()
 
 
-def inputs_on_gpu(w, seed, long_memory=False, seqlen=None, zero_D=False, dt_scale=1.0, a_scale=1.0):
+def inputs_on_gpu(w, seed, long_memory=False, seqlen=None, zero_D=False, dt_scale=1.0, a_scale=1.0,
+                  resets=(), big_angles=0.0):
     """Returns (exact fp64 dict, torch dict) for workload w.  dt_scale and
-    a_scale stretch dt (and the dt-scaled angles) and A, e.g. for strong decay."""
+    a_scale stretch dt (and the dt-scaled angles) and A, e.g. for strong decay.
+    resets: (token, log_decay) pairs; that token's dt is set so that dt * A
+    equals log_decay in every chain (a state reset; its angle is left as
+    drawn).  big_angles > 0 adds a one-signed angle of big_angles * U(1, 2)
+    radians per (token, pair), so chunk-local angle sums run to thousands of
+    radians."""
     raw = syn.draw(w, seed, long_memory=long_memory, seqlen=seqlen)
     if zero_D:
         raw["D"] = np.zeros_like(raw["D"])
@@ -37,6 +108,11 @@ def inputs_on_gpu(w, seed, long_memory=False, seqlen=None, zero_D=False, dt_scal
         raw["theta"] = raw["theta"] * dt_scale
     if a_scale != 1.0:
         raw["A"] = raw["A"] * a_scale
+    for t, ld in resets:
+        raw["dt"][:, t, :] = ld / raw["A"][None, :]
+    if big_angles:
+        rng = np.random.default_rng(seed + 12345)
+        raw["theta"] = raw["theta"] + big_angles * rng.uniform(1.0, 2.0, size=raw["theta"].shape)
     ex = syn.as_exact(raw, w.io_dtype)
     tt = {k: to_gpu(v, w.io_dtype, k) for k, v in ex.items()}
     return ex, tt

@@ -101,9 +101,32 @@ def test_prefill_tile_height_and_lds_limit():
     # 64-token chunk (16-token tiles) are accepted (seqlen 0: checks only) ...
     assert call_prefill(dims(io_dtype="f32", dstate=128, chunk=64), seqlen=0) == B.M3_OK
     assert call_prefill(dims(rank=4, chunk=64, dstate=128), seqlen=0) == B.M3_OK
+    assert call_prefill(dims(io_dtype="f32", dstate=128, headdim=128, chunk=64), seqlen=0) == B.M3_OK
     # ... and shapes whose rows fit no tile height down to 16 tokens are refused
     assert call_prefill(dims(io_dtype="f32", dstate=128, rank=4, chunk=16)) == B.M3_ERR_UNSUPPORTED
-    assert call_prefill(dims(io_dtype="f32", dstate=128, headdim=128, chunk=64)) == B.M3_ERR_UNSUPPORTED
+
+
+def _prefill_support(io, P, N, R, Q):
+    d = B.make_dims(1, 1, P, N, R, Q, io)
+    nbytes = ctypes.c_size_t()
+    return B.lib().mamba3_prefill_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(nbytes)) == B.M3_OK
+
+
+def test_prefill_support_is_monotone_in_chunk():
+    """The chunk is a tile height: every (dtype, P, N, R) accepted at chunk 16
+    is accepted at 32 and 64, and the only sizes refused at every chunk are
+    the ones the header lists (fp32 I/O, N = 128, R = 4, P >= 64)."""
+    refused = []
+    for io in ("bf16", "f32"):
+        for P in (16, 32, 64, 128):
+            for N in (16, 32, 64, 128):
+                for R in (1, 2, 4):
+                    ok = [_prefill_support(io, P, N, R, Q) for Q in (16, 32, 64)]
+                    if ok[0]:
+                        assert ok[1] and ok[2], (io, P, N, R, ok)
+                    if not any(ok):
+                        refused.append((io, P, N, R))
+    assert refused == [("f32", 64, 128, 4), ("f32", 128, 128, 4)]
 
 
 def test_decode_checks_dims():

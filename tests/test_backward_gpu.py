@@ -31,10 +31,10 @@ def W(name, **kw):
     return syn.WORKLOADS[name].with_(**kw)
 
 
-def run_backward(w, seed, disc=0, st=None, with_dh=True):
+def run_backward(w, seed, disc=0, st=None, with_dh=True, resets=()):
     d = m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype, disc)
     T = w.seqlen
-    ex, tt = inputs_on_gpu(w, seed)
+    ex, tt = inputs_on_gpu(w, seed, resets=resets)
     rng = np.random.default_rng(seed + 31)
     dy = syn.round_io(rng.standard_normal((w.batch, T, w.heads, w.rank, w.headdim)), w.io_dtype)
     dh = syn.round_io(rng.standard_normal((w.batch, w.heads, w.headdim, w.dstate)), "f32") if with_dh else None
@@ -55,18 +55,32 @@ def run_backward(w, seed, disc=0, st=None, with_dh=True):
     return ex, st_ex, dy, dh, {k: to_np(v) for k, v in grads.items()}
 
 
-def check_backward(w, seed, disc=0, st=None, with_dh=True):
-    ex, st_ex, dy, dh, g = run_backward(w, seed, disc, st, with_dh)
+def check_backward(w, seed, disc=0, st=None, with_dh=True, resets=()):
+    ex, st_ex, dy, dh, g = run_backward(w, seed, disc, st, with_dh, resets)
     ref = oracle.prefill_backward(ex["x"], ex["B"], ex["C"], ex["dt"], ex["lam"], ex["theta"], ex["A"], ex["D"],
                                   st_ex, dy, dh_final=dh, disc=disc)
     errs = {k: relerr(g[k], ref[k]) for k in NAMES if np.linalg.norm(ref[k]) > 0}
     print(f"[backward {w.name} T={w.seqlen} R={w.rank} disc={disc}] " +
           " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    for k in NAMES:
+        assert np.all(np.isfinite(g[k])), k
     for k, v in errs.items():
         assert v <= TOL, (k, v)
     for k in NAMES:
         if np.linalg.norm(ref[k]) == 0:
             assert np.all(g[k] == 0), k
+
+
+@pytest.mark.parametrize("ld", [-100.0, -1000.0])
+@pytest.mark.parametrize("io,P,N,R,T", [("f32", 32, 64, 1, 150), ("bf16", 64, 64, 4, 70), ("f32", 32, 32, 2, 90)])
+def test_backward_state_reset(io, P, N, R, T, ld):
+    """Tokens with dt * A = -100 or -1000 (state resets): right after a
+    16-row block, at a unit start (units of 64 / R tokens), and the last
+    token; every gradient finite and at the fp32 bar."""
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=T)
+    qu = 64 // R
+    resets = [(t, ld) for t in sorted({16 // R, qu, qu + 3 * (16 // R), T - 1})]
+    check_backward(w, seed=2300 + R, st=syn.draw_state(w, 2301), resets=resets)
 
 
 @pytest.mark.parametrize("io,P,N,R,T", [
