@@ -30,7 +30,9 @@
  *   - All tensor pointers are DEVICE pointers (HIP device memory of the
  *     current device); every call is asynchronous on `stream` (a hipStream_t
  *     passed as void*; NULL = the default stream).  Nothing synchronises.
- *   - The caller owns every buffer.  The library allocates no device memory.
+ *   - The caller owns every buffer.  The library allocates no device memory;
+ *     the only device memory of its own is the 16 MiB scratch array of
+ *     mamba3_prefill_noalloc, part of its loaded code object on each GPU.
  *   - Tensors are dense, row-major, in the layouts given below, with base
  *     pointers aligned to 16 bytes.
  *   - I/O dtype (x, B, C, y, B_prev, x_prev) is fp32 or bf16 as dims.io_dtype
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define M3_ABI_VERSION 5
+#define M3_ABI_VERSION 6
 
 typedef enum {
   M3_OK = 0,
@@ -172,6 +174,22 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
                    const void* C, const float* dt, const float* lam, const float* theta,
                    const float* A, const float* D, m3_state* state, void* y,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* mamba3_prefill for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace.  Where mamba3_prefill needs a
+ * segment workspace (long prompts of few chains), this call uses the
+ * library's own device scratch instead: a file-scope device array of 16 MiB
+ * per GPU, held until the process ends.  Sizes whose workspace
+ * (mamba3_prefill_workspace_bytes) exceeds 16 MiB return M3_ERR_UNSUPPORTED
+ * before any HIP call.  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  The scratch
+ * needs no clearing between calls (a call writes everything it reads), and
+ * results are identical to mamba3_prefill's.  ABI version 6. */
+int mamba3_prefill_noalloc(const m3_dims* dims, int32_t seqlen, const void* x, const void* B,
+                           const void* C, const float* dt, const float* lam, const float* theta,
+                           const float* A, const float* D, m3_state* state, void* y, void* stream);
 
 /* One recurrent step: one new token for every (batch, head).
  *   x      io    (batch, heads, R, P)

@@ -9,5 +9,5 @@ from .binding import (  # noqa: F401
     m3_abi_version, m3_last_error, m3_state_bytes, m3_state_zero, m3_state_load,
     m3_state_readout, mamba3_prefill_workspace_bytes, mamba3_prefill, mamba3_decode_step,
     mamba3_prefill_gated, mamba3_decode_step_gated, mamba3_prefill_ex, mamba3_decode_step_ex,
-    mamba3_prefill_backward_workspace_bytes, mamba3_prefill_backward,
+    mamba3_prefill_backward_workspace_bytes, mamba3_prefill_backward, mamba3_prefill_noalloc,
 )

@@ -36,7 +36,7 @@ EXPORTED = (
     "m3_abi_version", "m3_last_error", "m3_state_bytes", "m3_state_zero", "m3_state_load",
     "m3_state_readout", "mamba3_prefill_workspace_bytes", "mamba3_prefill", "mamba3_decode_step",
     "mamba3_prefill_gated", "mamba3_decode_step_gated", "mamba3_prefill_ex", "mamba3_decode_step_ex",
-    "mamba3_prefill_backward_workspace_bytes", "mamba3_prefill_backward",
+    "mamba3_prefill_backward_workspace_bytes", "mamba3_prefill_backward", "mamba3_prefill_noalloc",
 )
 
 GRAD_FIELDS = ("dx", "dB", "dC", "ddt", "dlam", "dtheta", "dA", "dD", "dh0", "dB_prev", "dx_prev")
@@ -101,6 +101,8 @@ def lib():
         L.mamba3_prefill_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(sz)]
         L.mamba3_prefill.restype = ctypes.c_int
         L.mamba3_prefill.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp, sz, vp]
+        L.mamba3_prefill_noalloc.restype = ctypes.c_int
+        L.mamba3_prefill_noalloc.argtypes = [D, i32, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp]
         L.mamba3_decode_step.restype = ctypes.c_int
         L.mamba3_decode_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, S, vp, vp]
         L.mamba3_prefill_gated.restype = ctypes.c_int
@@ -272,6 +274,16 @@ def mamba3_prefill(dims, seqlen, x, B, C, dt, lam, theta, A, D, state, y, worksp
     cs = state.c_struct()
     _check(lib().mamba3_prefill(ctypes.byref(dims), int(seqlen), *args, ctypes.byref(cs), py, ws, wsb,
                                 _stream(stream)))
+
+
+def mamba3_prefill_noalloc(dims, seqlen, x, B, C, dt, lam, theta, A, D, state, y, stream=None):
+    """mamba3_prefill without a workspace argument: the library's own device
+    scratch serves as the segment workspace (calls on one GPU must not
+    overlap)."""
+    args, py = _prefill_args(dims, seqlen, x, B, C, dt, lam, theta, A, D, y)
+    cs = state.c_struct()
+    _check(lib().mamba3_prefill_noalloc(ctypes.byref(dims), int(seqlen), *args, ctypes.byref(cs), py,
+                                        _stream(stream)))
 
 
 def mamba3_prefill_gated(dims, seqlen, x, B, C, dt, lam, theta, A, D, z, weight, eps, state, y,

@@ -259,7 +259,8 @@ int check_bcnorm(const m3_bcnorm* bc, const float** nbw, const float** ncw, floa
 int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
                  const float* dt, const float* lam, const float* theta, const float* A, const float* D,
                  const m3_bcnorm* bcnorm, const m3_gate* gate, bool gated, m3_state* state, void* y,
-                 void* workspace, size_t workspace_bytes, void* stream, const char* what) {
+                 void* workspace, size_t workspace_bytes, void* stream, const char* what,
+                 bool noalloc = false) {
   m3::Dims m;
   int st = check_dims(dims, true, &m);
   if (st != M3_OK) return st;
@@ -298,6 +299,16 @@ int prefill_impl(const m3_dims* dims, int32_t seqlen, const void* x, const void*
   int nseg = 1, sc = 0;
   plan_segments(m, seqlen, &nseg, &sc);
   const size_t need = workspace_for(m, nseg);
+  if (noalloc && need > 0) {
+    // the library's own device scratch stands in for the caller's workspace
+    if (need > m3::kNoAllocScratchBytes)
+      return fail(M3_ERR_UNSUPPORTED, "%s: these sizes need a %zu-byte segment workspace, more than the %zu bytes "
+                  "of device scratch; use mamba3_prefill with a caller workspace", what, need,
+                  m3::kNoAllocScratchBytes);
+    const hipError_t e = m3::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return fail(M3_ERR_HIP, "%s: device scratch: %s", what, hipGetErrorString(e));
+    workspace_bytes = m3::kNoAllocScratchBytes;
+  }
   if (need > 0) {
     if (workspace_bytes < need)
       return fail(M3_ERR_WORKSPACE, "workspace of %zu bytes < required %zu", workspace_bytes, need);
@@ -395,6 +406,13 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
                    void* stream) {
   return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, nullptr, nullptr, false, state, y, workspace,
                       workspace_bytes, stream, "mamba3_prefill");
+}
+
+int mamba3_prefill_noalloc(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,
+                           const float* dt, const float* lam, const float* theta, const float* A, const float* D,
+                           m3_state* state, void* y, void* stream) {
+  return prefill_impl(dims, seqlen, x, B, C, dt, lam, theta, A, D, nullptr, nullptr, false, state, y, nullptr, 0,
+                      stream, "mamba3_prefill_noalloc", true);
 }
 
 int mamba3_prefill_gated(const m3_dims* dims, int32_t seqlen, const void* x, const void* B, const void* C,

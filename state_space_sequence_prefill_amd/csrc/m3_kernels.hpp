@@ -143,4 +143,10 @@ hipError_t launch_prefill_pc_bcnorm_down(const Dims& d, const PrefillArgs& a, hi
 // the norm's weights and partial sums on top of the plain tiles).
 bool prefill_pc_bcnorm_supported(const Dims& d);
 
+// Device scratch of mamba3_prefill_noalloc (m3_noalloc.hip): a file-scope
+// device array of kNoAllocScratchBytes per GPU; noalloc_scratch returns its
+// device address on the current device (resolved once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace m3

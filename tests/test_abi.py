@@ -39,8 +39,8 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version():
     # version 2 added m3_dims.disc (the discretisation rule); version 3 the
     # gated entry points and m3_gate; version 4 m3_bcnorm and the _ex calls;
-    # version 5 the backward pass and m3_grads
-    assert B.m3_abi_version() == 5
+    # version 5 the backward pass and m3_grads; version 6 mamba3_prefill_noalloc
+    assert B.m3_abi_version() == 6
 
 
 def test_dims_struct_matches_header():
@@ -414,3 +414,35 @@ def test_backward_size_limit():
     assert call_backward(dims(headdim=24, dstate=64)) == B.M3_ERR_UNSUPPORTED
     assert call_backward(dims(headdim=64, dstate=40)) == B.M3_ERR_UNSUPPORTED
     assert call_backward(dims(headdim=64, dstate=64, rank=8)) == B.M3_ERR_UNSUPPORTED
+
+
+def call_prefill_noalloc(d, seqlen=16, ptrs=None, state=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    st = fake_state() if state is None else state
+    return B.lib().mamba3_prefill_noalloc(ctypes.byref(d), seqlen, *p[:8], ctypes.byref(st), p[8], None)
+
+
+def test_noalloc_checks_like_prefill():
+    """mamba3_prefill_noalloc validates exactly like mamba3_prefill (no
+    workspace argument to check), before any HIP call."""
+    assert call_prefill_noalloc(dims(rank=3)) == B.M3_ERR_UNSUPPORTED
+    assert call_prefill_noalloc(dims(), seqlen=-1) == B.M3_ERR_SHAPE
+    assert call_prefill_noalloc(dims(), seqlen=0) == B.M3_OK
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert call_prefill_noalloc(dims(), ptrs=p) == B.M3_ERR_NULL
+    p = [FAKE] * 9
+    p[3] = FAKE + 4
+    assert call_prefill_noalloc(dims(), ptrs=p) == B.M3_ERR_ALIGN
+
+
+def test_noalloc_rejects_workspace_beyond_scratch():
+    """Few long chains whose segment workspace exceeds the 16 MiB scratch are
+    refused with M3_ERR_UNSUPPORTED before any HIP call; the message says why."""
+    d = dims(batch=1, heads=64, headdim=128, dstate=128, rank=1, chunk=64)
+    nbytes = ctypes.c_size_t()
+    assert B.lib().mamba3_prefill_workspace_bytes(ctypes.byref(d), 1 << 16, ctypes.byref(nbytes)) == B.M3_OK
+    assert nbytes.value > 16 << 20
+    assert call_prefill_noalloc(d, seqlen=1 << 16) == B.M3_ERR_UNSUPPORTED
+    assert "scratch" in B.m3_last_error()
