@@ -83,31 +83,49 @@ typedef enum {
 } m3_disc;
 
 /* Problem sizes.  Supported set:
- *   batch >= 1, heads >= 1 (batch*heads < 2^31 / 1024),
+ *   batch >= 1, heads >= 1 (batch*heads <= 2^21),
  *   headdim P in {16, 32, 64, 128},
- *   dstate  N in {16, 32, 64, 128}  (N/2 complex pairs),
- *   rank    R in {1, 2, 4}          (1 = SISO, >1 = MIMO),
- *   chunk   Q in {16, 32, 64}       (prefill block length; Q*R <= 256; the
- *                                    result does not depend on it, and the
- *                                    library may tile with Q/2 or Q/4 when
- *                                    Q*R rows do not fit its tiles),
+ *   dstate  N in {16, 32, 64, 128, 256}  (N/2 complex pairs),
+ *   rank    R in 1..8                    (1 = SISO, > 1 = MIMO; the prefill
+ *                                         tiles hold R rounded up to a power
+ *                                         of two rows per token, the padded
+ *                                         rows with x = 0),
+ *   chunk   Q in {16, 32, 64}            (prefill block length; the result
+ *                                         does not depend on it: the library
+ *                                         tiles with the largest height <= Q
+ *                                         whose tiles fit, halving down to 16
+ *                                         tokens, or 4 for R >= 3),
  *   io_dtype in m3_dtype,
  *   disc in m3_disc (0, the default, when the struct is zero-initialised).
- * Anything else returns M3_ERR_UNSUPPORTED (or M3_ERR_SHAPE for values <= 0),
- * as do prefill sizes whose tiles fit the 160 KiB of LDS at no tile height
- * down to 16 tokens: fp32 I/O with N = 128, R = 4 and P >= 64 (16 tokens x 4
- * ranks = 64 rows of fp32 B~ and C~ at a 132-float pitch, their transposes,
- * X^T and the score and output tiles, double buffered, exceed 160 KiB).
- * Support does not depend on the chunk otherwise: a size accepted at chunk
- * 16 is accepted at 32 and 64. */
+ * Support does not depend on the chunk: a size accepted at chunk 16 is
+ * accepted at 32 and 64.  Within that set M3_ERR_UNSUPPORTED is returned for
+ *   - prefill with fp32 I/O and N = 256, except P = 16 with R <= 2: the
+ *     producer/consumer kernel holds a chunk's B and C rows in producer
+ *     registers (16 KiB at most; a 32-row tile of 256 fp32 values per row is
+ *     32 KiB), and the single-role kernel's LDS (B~, C~ at a 264-float pitch,
+ *     B~^T, X^T and a copy of the state: 2 x 33.8 + 36.9 + 2.3 + 16.9 KiB plus
+ *     the angles at 32 rows) fits 160 KiB only for P = 16;
+ *   - prefill with fp32 I/O, P = 128, N = 128 and R >= 3: two 32-row tile
+ *     buffers (B~, C~ at a 132-float pitch, B~^T, X^T: 70 KiB each) and the
+ *     score and output tiles need 165 KiB of LDS, and the single-role kernel
+ *     fits this size only for R <= 2;
+ *   - decode with P = 128, N = 256 and R >= 5: the matrix-core kernel's
+ *     state staging rows (128 x 260 x 4 B = 130 KiB) and rank operands exceed
+ *     160 KiB of LDS, and the VALU kernel serves R <= 4.
+ * Values <= 0 return M3_ERR_SHAPE.  The backward pass has its own, smaller
+ * set (mamba3_prefill_backward). */
 typedef struct {
   int32_t batch, heads, headdim, dstate, rank, chunk;
   int32_t io_dtype;
   int32_t disc;
 } m3_dims;
 
-/* Recurrent state of every (batch, head), in the LAB frame (the frame of the
- * definition above; no accumulated rotation is folded in):
+/* Recurrent state of every (batch, head): the fixed-size memory an SSM
+ * carries from token to token instead of a Transformer's growing key/value
+ * cache (lilting.ch Mamba-3 article, section "SSMとは何か、Transformerの推論
+ * コスト問題"; the prefill hands it to the decode steps).  It is kept in the
+ * LAB frame (the frame of the definition above; no accumulated rotation is
+ * folded in):
  *   h       fp32      (batch, heads, P, N)
  *   B_prev  io dtype  (batch, heads, R, N)   last token's B  (pending input)
  *   x_prev  io dtype  (batch, heads, R, P)   last token's x
@@ -130,16 +148,20 @@ const char* m3_last_error(void);
 int m3_state_bytes(const m3_dims* dims, size_t* h_bytes, size_t* bprev_bytes,
                    size_t* xprev_bytes);
 
-/* Zero the whole state (h, B_prev, x_prev): the start of a fresh sequence.
- * Uses a fill kernel (no memset node), so it may be captured in a HIP graph. */
+/* Zero the whole state (h, B_prev, x_prev): the start of a fresh sequence
+ * (the state of the section cited at m3_state, before any token).  Uses a
+ * fill kernel (no memset node), so it may be captured in a HIP graph. */
 int m3_state_zero(const m3_dims* dims, m3_state* state, void* stream);
 
-/* Copy a state from caller buffers (same layouts as m3_state) into `dst`.
+/* Copy a state from caller buffers (same layouts as m3_state) into `dst`:
+ * resuming a sequence from its fixed-size state (section cited at m3_state).
  * Source and destination must not overlap. */
 int m3_state_load(const m3_dims* dims, m3_state* dst, const float* h,
                   const void* B_prev, const void* x_prev, void* stream);
 
-/* Copy `src` out into caller buffers (same layouts).  Must not overlap. */
+/* Copy `src` out into caller buffers (same layouts): the whole memory of a
+ * sequence after its last token (section cited at m3_state).  Must not
+ * overlap. */
 int m3_state_readout(const m3_dims* dims, const m3_state* src, float* h,
                      void* B_prev, void* x_prev, void* stream);
 

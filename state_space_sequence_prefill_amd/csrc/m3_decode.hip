@@ -172,7 +172,8 @@ template <typename IO, int N, int R, int IT, int KG>
 __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, int P) {
   constexpr int LPR = N / 4;           // lanes per state row, 4 columns (2 pairs) each
   constexpr int RPI = kWave / LPR;     // state rows covered by one wave instruction
-  constexpr int K = IT * R;            // readout partial sums per lane
+  constexpr int RP = R == 3 ? 4 : R;   // ranks padded to a power of two for the readout (rank 3: one zero)
+  constexpr int K = IT * RP;           // readout partial sums per lane
   using Ops = DecOps<IO, N, R>;
   extern __shared__ __align__(16) char dsm[];
   const int head = blockIdx.x;         // flattened (b, h)
@@ -225,31 +226,43 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
     gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * (a.gdown ? 1 : R) * P, a.gw + (size_t)hh * P,
                   a.gdown != nullptr, P, wave, nthr / kWave, lane);
   // KG granules per thread (the launch picks KG with KG * threads >= total);
-  // every load is unconditional (clamped duplicates are not stored)
-  u32x4 gv[KG];
-#pragma unroll
-  for (int k = 0; k < KG; ++k) {
-    int e = threadIdx.x + k * nthr;
-    e = e < gAll ? e : gAll - 1;
+  // every load is unconditional (clamped duplicates are not stored).  KG = 0:
+  // more granules than a register array holds, staged by a plain loop first.
+  auto granule_src = [&](int e) {
     const u32x4* src = gsrc[0] + e;  // segment by selects, no branch around the load
 #pragma unroll
     for (int q = 1; q < 6; ++q) src = e >= gstart[q] ? gsrc[q] + (e - gstart[q]) : src;
-    gv[k] = *src;
+    return src;
+  };
+  if constexpr (KG == 0) {
+    for (int e = threadIdx.x; e < gAll; e += nthr) reinterpret_cast<u32x4*>(dsm)[e] = *granule_src(e);
+  }
+  constexpr int KGR = KG > 0 ? KG : 1;
+  u32x4 gv[KGR];
+  if constexpr (KG > 0) {
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      int e = threadIdx.x + k * nthr;
+      e = e < gAll ? e : gAll - 1;
+      gv[k] = *granule_src(e);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the state loads after the operand loads
   float4 hv[IT];
 #pragma unroll
   for (int i = 0; i < IT; ++i) hv[i] = *reinterpret_cast<const float4*>(hrow + (size_t)(row0 + i) * N);
   __builtin_amdgcn_sched_barrier(0);  // ... and all IT of them issued before the wait
+  if constexpr (KG > 0) {
 #pragma unroll
-  for (int k = 0; k < KG; ++k) {
-    const int e = threadIdx.x + k * nthr;
-    if (e < gAll) reinterpret_cast<u32x4*>(dsm)[e] = gv[k];
+    for (int k = 0; k < KG; ++k) {
+      const int e = threadIdx.x + k * nthr;
+      if (e < gAll) reinterpret_cast<u32x4*>(dsm)[e] = gv[k];
+    }
   }
   // The old pending pair has been read once the operand loads retired (at
   // most IT loads, the state's, still outstanding); after the barrier every
   // thread may overwrite it, and the LDS operand block is complete.
-  __builtin_amdgcn_s_waitcnt(0x0F70 | IT);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(IT));
   __syncthreads();
 
   const IO* sBp = reinterpret_cast<const IO*>(dsm);
@@ -322,11 +335,14 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
     }
     *reinterpret_cast<float4*>(hrow + (size_t)row * N) = make_float4(v[0], v[1], v[2], v[3]);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float acc = (n4 == 0) ? Dh * xc[r] : 0.0f;
+    for (int r = 0; r < RP; ++r) {
+      float acc = 0.0f;
+      if (r < R) {
+        acc = (n4 == 0) ? Dh * xc[r] : 0.0f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc += v[k] * Cn[r][k];
-      part[i * R + r] = acc;
+        for (int k = 0; k < 4; ++k) acc += v[k] * Cn[r][k];
+      }
+      part[i * RP + r] = acc;
     }
   }
   // ---- 4. readout: reduce the partial sums over the lanes of each row
@@ -340,12 +356,14 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
 #pragma unroll
     for (int j = 0; j < kOut; ++j) {
       const int idx = base + j;
-      const int i = idx / R;
-      const int r = idx % R;
-      if (gated)
-        sYg[r * P + row0 + i] = part[j];
-      else
-        y[r * P + row0 + i] = from_f32<IO>(part[j]);
+      const int i = idx / RP;
+      const int r = idx % RP;
+      if (r < R) {
+        if (gated)
+          sYg[r * P + row0 + i] = part[j];
+        else
+          y[r * P + row0 + i] = from_f32<IO>(part[j]);
+      }
     }
   }
   // ---- 5. new pending pair (B_prev, x_prev) <- (B, x) from the LDS copies,
@@ -379,11 +397,14 @@ hipError_t launch_t(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   const int waves = d.P * N / (4 * kWave * IT);
   const dim3 grid(d.batch * d.heads), block(waves * kWave);
   const size_t lds = DecOps<IO, N, R>::bytes(d.P) + (a.gz ? (size_t)R * d.P * sizeof(float) : 0);
-  if (DecOps<IO, N, R>::granules(d.P) <= waves * kWave)
+  const int gr = DecOps<IO, N, R>::granules(d.P);
+  if (gr <= waves * kWave)
     hipLaunchKernelGGL((decode_kernel<IO, N, R, IT, 1>), grid, block, lds, s, a, d.heads, d.P);
-  else
+  else if (gr <= kDecMaxGranulesPerThread * waves * kWave)
     hipLaunchKernelGGL((decode_kernel<IO, N, R, IT, kDecMaxGranulesPerThread>), grid, block, lds, s, a, d.heads,
                        d.P);
+  else
+    hipLaunchKernelGGL((decode_kernel<IO, N, R, IT, 0>), grid, block, lds, s, a, d.heads, d.P);
   return hipGetLastError();
 }
 
@@ -402,6 +423,7 @@ hipError_t launch_r(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   switch (d.R) {
     case 1: return launch_it<IO, N, 1>(d, a, s);
     case 2: return launch_it<IO, N, 2>(d, a, s);
+    case 3: return launch_it<IO, N, 3>(d, a, s);
     default: return launch_it<IO, N, 4>(d, a, s);
   }
 }
@@ -412,27 +434,33 @@ hipError_t launch_n(const Dims& d, const DecodeArgs& a, hipStream_t s) {
     case 16: return launch_r<IO, 16>(d, a, s);
     case 32: return launch_r<IO, 32>(d, a, s);
     case 64: return launch_r<IO, 64>(d, a, s);
-    default: return launch_r<IO, 128>(d, a, s);
+    case 128: return launch_r<IO, 128>(d, a, s);
+    default: return launch_r<IO, 256>(d, a, s);
   }
+}
+
+// Sizes the VALU kernel serves: ranks 1 to 4 (its per-lane operands and
+// partial sums grow with the rank; ranks above 4 run on the matrix cores).
+bool decode_valu_supported(const Dims& d) {
+  if (!(d.R >= 1 && d.R <= 4)) return false;
+  const int it = pick_iters(d.P, d.N);
+  const int waves = d.P * d.N / (4 * kWave * it);
+  return waves >= 1 && waves <= 16 && waves * 4 * kWave * it == d.P * d.N;
 }
 
 }  // namespace
 
 bool decode_supported(const Dims& d) {
-  const bool n_ok = d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128;
+  const bool n_ok = d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128 || d.N == 256;
   const bool p_ok = d.P == 16 || d.P == 32 || d.P == 64 || d.P == 128;
-  const bool r_ok = d.R == 1 || d.R == 2 || d.R == 4;
+  const bool r_ok = d.R >= 1 && d.R <= 8;
   if (!(n_ok && p_ok && r_ok)) return false;
-  const int it = pick_iters(d.P, d.N);
-  const int waves = d.P * d.N / (4 * kWave * it);
-  if (!(waves >= 1 && waves <= 16 && waves * 4 * kWave * it == d.P * d.N)) return false;
-  const int esz = d.bf16 ? 2 : 4;
-  const int granules = (3 * d.R * d.N + 2 * d.R * d.P) * esz / 16 + d.N / 8;
-  return granules <= kDecMaxGranulesPerThread * waves * kWave;
+  return decode_mimo_supported(d) || decode_valu_supported(d);
 }
 
 hipError_t launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   if (decode_mimo_supported(d)) return launch_decode_mimo(d, a, s);
+  if (!decode_valu_supported(d)) return hipErrorInvalidValue;  // (the host checks this first)
   return d.bf16 ? launch_n<bf16>(d, a, s) : launch_n<float>(d, a, s);
 }
 

@@ -47,9 +47,11 @@ struct MimoLds {
   // floats) between coalesced HBM runs and the MFMA lane layout
   static constexpr int kLdSt = N + 4;
   __host__ __device__ static constexpr size_t stage_bytes(int P) { return (size_t)P * kLdSt * 4; }
-  // everything: derived operands, 16 floats of BC-norm scales, staging, gated outputs
+  // BC-norm scales of the 3R rows B_prev, B, C, in whole 64-byte blocks
+  static constexpr size_t kSclBytes = ((size_t)3 * R * 4 + 63) / 64 * 64;
+  // everything: derived operands, BC-norm scales, staging, gated outputs
   __host__ __device__ static constexpr size_t total_bytes(int P, bool gated) {
-    return bytes(P) + 64 + stage_bytes(P) + (gated ? (size_t)R * P * 4 : 0);
+    return bytes(P) + kSclBytes + stage_bytes(P) + (gated ? (size_t)R * P * 4 : 0);
   }
 };
 constexpr int kMimoMaxGranulesPerThread = 3;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   // HBM and the LDS staging rows in whole 1 KiB runs (lane l, run j: float4
   // l + 64 j), and between staging and registers in the MFMA layout
   float* const hwave = a.h + (size_t)head * P * N + (size_t)(16 * pb) * N;
-  float* const sSt = reinterpret_cast<float*>(dsm + L::bytes(P) + 64) + (size_t)(16 * pb) * L::kLdSt;
+  float* const sSt = reinterpret_cast<float*>(dsm + L::bytes(P) + L::kSclBytes) + (size_t)(16 * pb) * L::kLdSt;
   auto stage_off = [&](int j) {  // staging offset of float4 lane + 64 j of the wave's rows
     const int f = lane + 64 * j;
     return (f / (N / 4)) * L::kLdSt + 4 * (f % (N / 4));
@@ -101,29 +103,42 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   if (gated)
     gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * (a.gdown ? 1 : R) * P, a.gw + (size_t)hh * P,
                   a.gdown != nullptr, P, wave, nthr / kWave, lane);
-  u32x4m gv[KG];
-#pragma unroll
-  for (int k = 0; k < KG; ++k) {
-    int e = tid + k * nthr;
-    e = e < gAll ? e : gAll - 1;  // clamped duplicate, not stored
+  // KG granules per thread in registers; KG = 0: more granules than a
+  // register array holds, staged by a plain loop first
+  auto granule_src = [&](int e) {
     const u32x4m* src = gsrc[0] + e;
 #pragma unroll
     for (int q = 1; q < 6; ++q) src = e >= gstart[q] ? gsrc[q] + (e - gstart[q]) : src;
-    gv[k] = *src;
+    return src;
+  };
+  if constexpr (KG == 0) {
+    for (int e = tid; e < gAll; e += nthr) reinterpret_cast<u32x4m*>(dsm)[e] = *granule_src(e);
+  }
+  constexpr int KGR = KG > 0 ? KG : 1;
+  u32x4m gv[KGR];
+  if constexpr (KG > 0) {
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      int e = tid + k * nthr;
+      e = e < gAll ? e : gAll - 1;  // clamped duplicate, not stored
+      gv[k] = *granule_src(e);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   float4 hv[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) hv[j] = *reinterpret_cast<const float4*>(hwave + 4 * (lane + 64 * j));
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (KG > 0) {
 #pragma unroll
-  for (int k = 0; k < KG; ++k) {
-    const int e = tid + k * nthr;
-    if (e < gAll) reinterpret_cast<u32x4m*>(dsm)[e] = gv[k];
+    for (int k = 0; k < KG; ++k) {
+      const int e = tid + k * nthr;
+      if (e < gAll) reinterpret_cast<u32x4m*>(dsm)[e] = gv[k];
+    }
   }
   // the old pending pair is read once the operand loads retired (at most NB
   // loads, the state's, outstanding); after the barrier it may be overwritten
-  __builtin_amdgcn_s_waitcnt(0x0F70 | NB);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(NB));
   __syncthreads();
 
   const IO* sBp = reinterpret_cast<const IO*>(dsm);
@@ -140,7 +155,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   // ---- 1b. BC normalisation: RMS scales of the 3R rows B_prev, B, C (wave w
   //          takes rows w, w + waves, ...; lane l columns l and l + 64)
   const bool bcn = a.nbw != nullptr;
-  float* const sScl = reinterpret_cast<float*>(dsm + L::bytes(P));  // [3R], padded to 16 floats
+  float* const sScl = reinterpret_cast<float*>(dsm + L::bytes(P));  // [3R], in kSclBytes
   if (bcn) {
     const int nw = nthr / kWave;
     for (int j = wave; j < 3 * R; j += nw) {
@@ -232,18 +247,21 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
 #pragma unroll
   for (int j = 0; j < NB; ++j)
     *reinterpret_cast<float4*>(hwave + 4 * (lane + 64 * j)) = *reinterpret_cast<const float4*>(sSt + stage_off(j));
-  // ---- 4. y: lanes g = 0 hold Y^T[r = i][p = 16pb + c] for r < R
+  // ---- 4. y: lane (g, c) holds Y^T[r = 4g + i][p = 16pb + c], i < 4, for r < R
   //         (gated: the fp32 outputs go to LDS behind the staging rows)
-  float* const sYg = reinterpret_cast<float*>(dsm + L::bytes(P) + 64 + L::stage_bytes(P));
-  if (g == 0) {
+  float* const sYg = reinterpret_cast<float*>(dsm + L::bytes(P) + L::kSclBytes + L::stage_bytes(P));
+  if (4 * g < R) {
     IO* y = static_cast<IO*>(a.y) + (size_t)head * R * P + 16 * pb + c;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float xr = sXk[(R + r) * P + 16 * pb + c];
-      if (gated)
-        sYg[r * P + 16 * pb + c] = yacc[r] + Dh * xr;
-      else
-        y[r * P] = from_f32<IO>(yacc[r] + Dh * xr);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      if (r < R) {
+        const float xr = sXk[(R + r) * P + 16 * pb + c];
+        if (gated)
+          sYg[r * P + 16 * pb + c] = yacc[i] + Dh * xr;
+        else
+          y[r * P] = from_f32<IO>(yacc[i] + Dh * xr);
+      }
     }
   }
   // ---- 5. new pending pair from the raw LDS copies, issued last
@@ -269,23 +287,35 @@ hipError_t launch_mimo_t(const Dims& d, const DecodeArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     for (const void* f : {reinterpret_cast<const void*>(&decode_mimo_kernel<IO, N, R, 1>),
-                          reinterpret_cast<const void*>(&decode_mimo_kernel<IO, N, R, kMimoMaxGranulesPerThread>)}) {
+                          reinterpret_cast<const void*>(&decode_mimo_kernel<IO, N, R, kMimoMaxGranulesPerThread>),
+                          reinterpret_cast<const void*>(&decode_mimo_kernel<IO, N, R, 0>)}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
     }
     attr_set = true;
   }
-  if (MimoLds<IO, N, R>::granules(d.P) <= waves * kWave)
+  const int gr = MimoLds<IO, N, R>::granules(d.P);
+  if (gr <= waves * kWave)
     hipLaunchKernelGGL((decode_mimo_kernel<IO, N, R, 1>), grid, block, lds, s, a, d.heads, d.P);
-  else
+  else if (gr <= kMimoMaxGranulesPerThread * waves * kWave)
     hipLaunchKernelGGL((decode_mimo_kernel<IO, N, R, kMimoMaxGranulesPerThread>), grid, block, lds, s, a,
                        d.heads, d.P);
+  else
+    hipLaunchKernelGGL((decode_mimo_kernel<IO, N, R, 0>), grid, block, lds, s, a, d.heads, d.P);
   return hipGetLastError();
 }
 
 template <typename IO, int N>
 hipError_t launch_mimo_r(const Dims& d, const DecodeArgs& a, hipStream_t s) {
-  return d.R == 2 ? launch_mimo_t<IO, N, 2>(d, a, s) : launch_mimo_t<IO, N, 4>(d, a, s);
+  switch (d.R) {
+    case 2: return launch_mimo_t<IO, N, 2>(d, a, s);
+    case 3: return launch_mimo_t<IO, N, 3>(d, a, s);
+    case 4: return launch_mimo_t<IO, N, 4>(d, a, s);
+    case 5: return launch_mimo_t<IO, N, 5>(d, a, s);
+    case 6: return launch_mimo_t<IO, N, 6>(d, a, s);
+    case 7: return launch_mimo_t<IO, N, 7>(d, a, s);
+    default: return launch_mimo_t<IO, N, 8>(d, a, s);
+  }
 }
 
 template <typename IO>
@@ -294,7 +324,22 @@ hipError_t launch_mimo_n(const Dims& d, const DecodeArgs& a, hipStream_t s) {
     case 16: return launch_mimo_r<IO, 16>(d, a, s);
     case 32: return launch_mimo_r<IO, 32>(d, a, s);
     case 64: return launch_mimo_r<IO, 64>(d, a, s);
-    default: return launch_mimo_r<IO, 128>(d, a, s);
+    case 128: return launch_mimo_r<IO, 128>(d, a, s);
+    default: return launch_mimo_r<IO, 256>(d, a, s);
+  }
+}
+
+template <typename IO>
+size_t mimo_lds_bytes(int P, int N, int R) {
+  switch (N * 16 + R) {
+#define M3_CASE(NN, RR) \
+  case NN * 16 + RR: return MimoLds<IO, NN, RR>::total_bytes(P, true);
+#define M3_CASE_N(NN) M3_CASE(NN, 2) M3_CASE(NN, 3) M3_CASE(NN, 4) M3_CASE(NN, 5) M3_CASE(NN, 6) \
+  M3_CASE(NN, 7) M3_CASE(NN, 8)
+    M3_CASE_N(16) M3_CASE_N(32) M3_CASE_N(64) M3_CASE_N(128) M3_CASE_N(256)
+#undef M3_CASE_N
+#undef M3_CASE
+    default: return (size_t)-1;
   }
 }
 
@@ -302,13 +347,13 @@ hipError_t launch_mimo_n(const Dims& d, const DecodeArgs& a, hipStream_t s) {
 
 bool decode_mimo_supported(const Dims& d) {
   // rank 1 stays on the VALU kernel (measured faster: its readout would use
-  // one row of sixteen in the matrix product)
-  if (!(d.R == 2 || d.R == 4)) return false;
-  if (!(d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128)) return false;
+  // one row of sixteen in the matrix product); ranks 2 to 8 (the update's
+  // 2R slots in up to four K groups, the readout's R rows of a 16-row tile)
+  if (!(d.R >= 2 && d.R <= 8)) return false;
+  if (!(d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128 || d.N == 256)) return false;
   if (!(d.P == 16 || d.P == 32 || d.P == 64 || d.P == 128)) return false;
-  const int esz = d.bf16 ? 2 : 4;
-  const int granules = (3 * d.R * d.N + 2 * d.R * d.P) * esz / 16 + d.N / 8;
-  return granules <= kMimoMaxGranulesPerThread * (d.P / 16) * kWave;
+  // the staging rows, operands and (gated) outputs in 160 KiB of LDS
+  return (d.bf16 ? mimo_lds_bytes<bf16>(d.P, d.N, d.R) : mimo_lds_bytes<float>(d.P, d.N, d.R)) <= 160 * 1024;
 }
 
 hipError_t launch_decode_mimo(const Dims& d, const DecodeArgs& a, hipStream_t s) {

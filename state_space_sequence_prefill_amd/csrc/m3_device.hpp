@@ -130,6 +130,11 @@ __device__ __forceinline__ float reduce_angle(float a) {
   return fmaf(-k, 1.9353071795864769e-3f, r);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// (0 <= n < 64) are outstanding and leaves the other counters alone: vmcnt
+// is split over bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) at max.
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // Lane-crossing helpers (wave64).
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, kWave);

@@ -14,6 +14,10 @@ struct Dims {
   int disc;  // m3_disc
 };
 
+// log2 of the rank padded to a power of two (the prefill tiles hold that
+// many rows per token): 1 -> 0, 2 -> 1, 3..4 -> 2, 5..8 -> 3.
+inline int pad_rank_log2(int R) { return R <= 1 ? 0 : R <= 2 ? 1 : R <= 4 ? 2 : 3; }
+
 // Arguments of one decode step (see mamba3_decode_step in include/mamba3.h).
 struct DecodeArgs {
   const void* x;

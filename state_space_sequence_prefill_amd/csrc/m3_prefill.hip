@@ -647,11 +647,11 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a, int ba
   // BC normalisation of the pending B_prev rows: a wave's elements all belong
   // to one chain (P * N/2 is a multiple of the elements per wave), so the
   // wave sums each row's squares together (lane l: columns l, l + 64).
-  float bscale[4] = {1.f, 1.f, 1.f, 1.f};
+  float bscale[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
   if (a.nbw) {
     const IO* Bp = static_cast<const IO*>(a.B_prev) + (size_t)chain * R * N;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {  // R <= 4
+    for (int r = 0; r < 8; ++r) {  // R <= 8
       if (r < R) {
         float ss = 0.f;
         for (int n = lane; n < N; n += 64) {
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a, int ba
     const float g0 = a.nbw ? a.nbw[(size_t)hh * N + 2 * j] : 1.f;
     const float g1 = a.nbw ? a.nbw[(size_t)hh * N + 2 * j + 1] : 1.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 8; ++r) {  // R <= 8
       if (r < R) {
         const float xp = beta0 * to_f32(Xp[r * P + p]) * bscale[r];
         e0r += xp * g0 * to_f32(Bp[r * N + 2 * j]);
@@ -744,11 +744,13 @@ hipError_t launch_fused_t(const Dims& d, const PrefillArgs& a, hipStream_t st) {
   const int rows_pad = (rows + 31) & ~31;
   const size_t lds = Lds<IO, N, P>::bytes(rows_pad, d.Q);
   static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<IO, N, P>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  if constexpr (Limits<IO, N, P>::kMaxRows > 0) {
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<IO, N, P>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
   }
   KParams kp;
   kp.a = a;
@@ -759,14 +761,20 @@ hipError_t launch_fused_t(const Dims& d, const PrefillArgs& a, hipStream_t st) {
   kp.Q = d.Q;
   const int chains = d.batch * d.heads;
   const bool pc = prefill_pc_supported(d);
-  // the epilogue and the BC normalisation live in the producer/consumer kernel
+  // the epilogue and the BC normalisation live in the producer/consumer
+  // kernel, and so do padded ranks (the host checks all this first)
   if ((a.gz || a.nbw) && !pc) return hipErrorInvalidValue;
+  if (!pc && !(d.R == 1 || d.R == 2 || d.R == 4)) return hipErrorInvalidValue;
   auto pass = [&](int mode, int nblocks) -> hipError_t {
     if (pc) return launch_prefill_pc(d, a, st, mode, nblocks);
-    kp.mode = mode;
-    kp.nblocks = nblocks;
-    hipLaunchKernelGGL((prefill_kernel<IO, N, P>), dim3(nblocks), dim3(kThreads), lds, st, kp);
-    return hipGetLastError();
+    if constexpr (Limits<IO, N, P>::kMaxRows == 0) {
+      return hipErrorInvalidValue;  // (never: such tiles fit at no height, which the host checks first)
+    } else {
+      kp.mode = mode;
+      kp.nblocks = nblocks;
+      hipLaunchKernelGGL((prefill_kernel<IO, N, P>), dim3(nblocks), dim3(kThreads), lds, st, kp);
+      return hipGetLastError();
+    }
   };
   if (a.nseg <= 1) return pass(kFused, chains);
   // pass 1: summaries of segments 0 .. nseg-2 from a zero entry value
@@ -802,7 +810,8 @@ hipError_t launch_n(const Dims& d, const PrefillArgs& a, hipStream_t s) {
     case 16: return launch_p<IO, 16>(d, a, s);
     case 32: return launch_p<IO, 32>(d, a, s);
     case 64: return launch_p<IO, 64>(d, a, s);
-    default: return launch_p<IO, 128>(d, a, s);
+    case 128: return launch_p<IO, 128>(d, a, s);
+    default: return launch_p<IO, 256>(d, a, s);
   }
 }
 
@@ -815,6 +824,7 @@ int max_rows(const Dims& d) {
     M3_CASE(32, 16) M3_CASE(32, 32) M3_CASE(32, 64) M3_CASE(32, 128)
     M3_CASE(64, 16) M3_CASE(64, 32) M3_CASE(64, 64) M3_CASE(64, 128)
     M3_CASE(128, 16) M3_CASE(128, 32) M3_CASE(128, 64) M3_CASE(128, 128)
+    M3_CASE(256, 16) M3_CASE(256, 32) M3_CASE(256, 64) M3_CASE(256, 128)
 #undef M3_CASE
     default: return 0;
   }
@@ -823,8 +833,11 @@ int max_rows(const Dims& d) {
 }  // namespace
 
 namespace {
-// Whether the single-role kernel's tiles fit at d.Q.
+// Whether the single-role kernel's tiles fit at d.Q (it takes ranks 1, 2
+// and 4 only: its rows are (token, rank) pairs with no padded ranks).
 bool single_role_fits(const Dims& d) {
+  if (!(d.R == 1 || d.R == 2 || d.R == 4)) return false;
+  if ((d.Q / 4) * (d.N / 8) > kThreads) return false;  // one angle item (4 tokens x 4 pairs) per thread
   const int rows_pad = ((d.Q * d.R) + 31) & ~31;
   return rows_pad <= (d.bf16 ? max_rows<bf16>(d) : max_rows<float>(d));
 }
@@ -833,10 +846,12 @@ bool single_role_fits(const Dims& d) {
 int prefill_tile_chunk(const Dims& d) {
   // The chunk length is a tile height: the chunked form gives the same result
   // for any chunk length.  The producer/consumer kernel at the largest height
-  // <= Q (halving down to 16 tokens) whose tiles fit, else the single-role
-  // kernel likewise; 0 when neither fits at any height.  Support is thereby
-  // monotone in the chunk: whatever runs at chunk 16 runs at 32 and 64.
-  for (int q = d.Q; q >= 16; q /= 2) {
+  // <= Q whose tiles fit (halving down to 16 tokens, or to 4 when a token
+  // brings 4 or 8 tile rows), else the single-role kernel likewise (down to
+  // 16); 0 when neither fits at any height.  Support is thereby monotone in
+  // the chunk: whatever runs at chunk 16 runs at 32 and 64.
+  const int qmin = d.R > 2 ? 4 : 16;
+  for (int q = d.Q; q >= qmin; q /= 2) {
     Dims e = d;
     e.Q = q;
     if (prefill_pc_supported(e)) return q;
@@ -850,9 +865,9 @@ int prefill_tile_chunk(const Dims& d) {
 }
 
 bool prefill_supported(const Dims& d) {
-  const bool n_ok = d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128;
+  const bool n_ok = d.N == 16 || d.N == 32 || d.N == 64 || d.N == 128 || d.N == 256;
   const bool p_ok = d.P == 16 || d.P == 32 || d.P == 64 || d.P == 128;
-  const bool r_ok = d.R == 1 || d.R == 2 || d.R == 4;
+  const bool r_ok = d.R >= 1 && d.R <= 8;
   const bool q_ok = d.Q == 16 || d.Q == 32 || d.Q == 64;
   if (!(n_ok && p_ok && r_ok && q_ok)) return false;
   return prefill_tile_chunk(d) > 0;

@@ -6,7 +6,7 @@
 namespace m3 {
 
 bool prefill_pc_supported(const Dims& d) {
-  const int rows_pad = ((d.Q * d.R) + 31) & ~31;
+  const int rows_pad = ((d.Q << pad_rank_log2(d.R)) + 31) & ~31;
   return rows_pad <= (d.bf16 ? pc_max_rows<bf16>(d) : pc_max_rows<float>(d));
 }
 

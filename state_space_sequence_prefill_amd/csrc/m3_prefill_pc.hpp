@@ -48,6 +48,9 @@ constexpr float kLog2ePc = 1.4426950408889634f;
 
 enum PcMode : int { kPcFused = 0, kPcSummary = 1, kPcSegment = 2 };
 
+// R is the rank of the data; the tiles hold 2^lgR >= R rows per token (the
+// rank padded to a power of two: rows of the padded ranks carry x = 0, so
+// they add nothing, and their outputs are not stored).
 struct PcParams {
   PrefillArgs a;
   int batch, heads, R, lgR, Q;
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 
   const PrefillArgs& a = kp.a;
   const int Q = kp.Q, R = kp.R, lgR = kp.lgR, H = kp.heads;
+  const int RP = 1 << lgR;  // tile rows per token (R padded to a power of two)
   const int T = a.seqlen;
   const int mode = kp.mode;
   const int nseg_grid = (mode == kPcFused) ? 1 : (mode == kPcSummary ? a.nseg - 1 : a.nseg);
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const bool producer = wave < 4;
-  const int rows = Q * R;
+  const int rows = Q * RP;
   const int rows_pad = (rows + 31) & ~31;
 
   // ---- LDS: [tile buffer 0 | tile buffer 1 | sSM | sY | coefs x3 | sSeg] ----
@@ -259,7 +263,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     const int GX = npx < 64 / RG ? npx : 64 / RG;  // x column groups per lane group
     const int nbitems = RG * npg;
     const int nxitems = RG * npx;
-    const int ntok = 4 >> lgR;  // tokens per row group (R <= 4)
+    // tokens per row group: 4 / RP, or with RP = 8 half a token (the even
+    // row group of a token carries its angle, the odd one none)
+    const int ntok = lgR <= 2 ? 4 >> lgR : 1;
     const IO* const Csrc = has_y ? Cg : Bg;  // segment summaries never read C
     // Two register sets: chunk i is built from one while chunk i+1's loads
     // land in the other, and chunk i+2's loads are issued into the first
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     bool ist[MI];
     uint32_t ob[MI][4], oth[MI][4], obs[MI], oths[MI];
     int xrg[MX], xxg[MX], xtok[MX][4];
-    bool xst[MX];
+    bool xst[MX], xpad[MX][4];  // xpad: a padded rank's row (its x is zero)
     uint32_t ox[MX][4], oxs[MX];
 #pragma unroll
     for (int m = 0; m < MI; ++m) {
@@ -291,7 +297,8 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       for (int k = 0; k < 4; ++k) {
         const int rho = 4 * rg + k;
         rtok[m][k] = rho < rows ? (rho >> lgR) : Q;
-        ob[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokBC + (uint32_t)(rho & (R - 1)) * N + 8 * pg;
+        const int rk = (rho & (RP - 1)) < R ? (rho & (RP - 1)) : R - 1;  // padded ranks read a real row
+        ob[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokBC + (uint32_t)rk * N + 8 * pg;
         oth[m][k] = (uint32_t)(t0 + (k < ntok ? k : ntok - 1)) * (uint32_t)tokTh + 4 * pg;
       }
     }
@@ -308,7 +315,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       for (int k = 0; k < 4; ++k) {
         const int rho = 4 * rg + k;
         xtok[m][k] = rho < rows ? (rho >> lgR) : Q;
-        ox[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokX + (uint32_t)(rho & (R - 1)) * P + 8 * xg;
+        xpad[m][k] = (rho & (RP - 1)) >= R;
+        const int rk = xpad[m][k] ? R - 1 : (rho & (RP - 1));
+        ox[m][k] = (uint32_t)(rho >> lgR) * (uint32_t)tokX + (uint32_t)rk * P + 8 * xg;
       }
     }
 
@@ -447,9 +456,10 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         const int rg = irg[m], pg = ipg[m];
         const int t0 = rtok[m][0];
         float th[4][4];
+        const int ntk = (lgR == 3 && (rg & 1)) ? 0 : ntok;  // RP = 8: odd row groups add no angle
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float tv = (q < ntok && t0 + q < Lc) ? 1.f : 0.f;
+          const float tv = (q < ntk && t0 + q < Lc) ? 1.f : 0.f;
           th[q][0] = tv * rs.th[m][q].x;
           th[q][1] = tv * rs.th[m][q].y;
           th[q][2] = tv * rs.th[m][q].z;
@@ -473,7 +483,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         float ph[4][4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int kq = R == 1 ? k : (k >> lgR);
+          const int kq = k >> lgR;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             ph[k][j] = base[j] + th[0][j] + (kq >= 1 ? th[1][j] : 0.f) + (kq >= 2 ? th[2][j] : 0.f) +
@@ -543,7 +553,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             store8(bf.sC + rho * LDN + 8 * pg, cv);
           }
           if (ist[m] && !crole) {
-            if (valid && t == te && (rho & (R - 1)) == 0) {
+            if (valid && t == te && (rho & (RP - 1)) == 0) {
 #pragma unroll
               for (int j = 0; j < 4; ++j)
                 bf.sEnd[4 * pg + j] = make_float4(cs4[j], sn4[j], ph[k][j], 0.f);
@@ -568,6 +578,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           for (int k = 0; k < 4; ++k)
 #pragma unroll
             for (int q = 0; q < 4; ++q) w[k][q] = rs.x[m][k].w[q];
+          if (R != RP) {  // padded ranks: their rows of X^T are zero
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) w[k][q] = xpad[m][k] ? 0u : w[k][q];
+          }
           uint2 v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -583,6 +599,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           float xv[4][8];
 #pragma unroll
           for (int k = 0; k < 4; ++k) rs.x[m][k].unpack(xv[k]);
+          if (R != RP) {  // padded ranks: their rows of X^T are zero
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) xv[k][e] = xpad[m][k] ? 0.f : xv[k][e];
+          }
           if (xst[m]) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -682,12 +704,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
       // BCN: RMS scales of the pending B_prev rows (lane (g, c) sums its
       // columns 16 nb + 4 g + i; the four g lanes complete the row)
-      float bsc[4] = {1.f, 1.f, 1.f, 1.f};
+      float bsc[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
       if constexpr (BCN) {
         if (mode == kPcFused) {
           const IO* Bp = static_cast<const IO*>(a.B_prev) + (size_t)chain * R * N;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {  // R <= 4
+          for (int r = 0; r < 8; ++r) {  // R <= 8
             if (r < R) {
               float ss = 0.f;
 #pragma unroll
@@ -720,7 +742,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 #pragma unroll
               for (int i4 = 0; i4 < 4; ++i4) v[i4] = alpha0 * h0[i4];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {  // R <= 4
+              for (int r = 0; r < 8; ++r) {  // R <= 8
                 if (r < R) {
                   float bp[4];
                   load4(Bp + r * N + n0, bp);
@@ -751,9 +773,13 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     constexpr int kCT = kConsWaves * kWave;          // consumer threads
     constexpr int KZ = (RMAX * G16 + kCT - 1) / kCT;  // granules per consumer thread
     const int ct = tid - kProdThreads;
+    // output-tile row -> (token, rank); rows of padded ranks map to rank R-1
+    // (read as clamped duplicates, never stored)
+    auto rank_of = [&](int row) { return (row & (RP - 1)) < R ? (row & (RP - 1)) : R - 1; };
+    auto real_row = [&](int row) { return (row & (RP - 1)) < R; };
     auto gran_off = [&](int c0, int e) -> size_t {
       const int row = e / G16, gq = e % G16;
-      return (size_t)(c0 + (row >> lgR)) * tokX + (row & (R - 1)) * P + gq * EG;
+      return (size_t)(c0 + (row >> lgR)) * tokX + rank_of(row) * P + gq * EG;
     };
     // Output epilogue (pre-gate grouped RMSNorm): a consumer thread always
     // handles granule column ct % G16 of its rows (kCT is a multiple of G16),
@@ -764,14 +790,15 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // output-tile rows t*R + r, which phase 2 already scaled by the weights.
     constexpr bool kDown = EPI == kEpiDown;
     const bool gated = EPI != kEpiPlain && has_y;
-    const int RO = kDown ? 1 : R;                    // output rows per token
+    const int RO = kDown ? 1 : R;                    // output rows per token in HBM
+    const int RT = kDown ? 1 : RP;                   // output rows per token in the tile loops
     const size_t tokO = (size_t)H * RO * P;          // output row stride per token
     const IO* Zg = gated ? static_cast<const IO*>(a.gz) + ((size_t)b * T * H + hh) * RO * P : nullptr;
     IO* const Og = static_cast<IO*>(a.y) + ((size_t)b * T * H + hh) * RO * P;
     auto out_off = [&](int c0, int e) -> size_t {
       const int row = e / G16, gq = e % G16;
       if constexpr (kDown) return (size_t)(c0 + row) * tokO + gq * EG;
-      return (size_t)(c0 + (row >> lgR)) * tokO + (row & (R - 1)) * P + gq * EG;
+      return (size_t)(c0 + (row >> lgR)) * tokO + rank_of(row) * P + gq * EG;
     };
     float gwr[EG];
     uint4 zr[KZ];
@@ -788,11 +815,13 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         const int pb = cw + kConsWaves * u;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          dwr[u][i4] = pb < PB ? a.gdown[((size_t)hh * R + (c & (R - 1))) * P + 16 * pb + 4 * g + i4] : 0.f;
+          dwr[u][i4] = (pb < PB && (c & (RP - 1)) < R)
+                           ? a.gdown[((size_t)hh * R + (c & (RP - 1))) * P + 16 * pb + 4 * g + i4]
+                           : 0.f;
       }
     }
     auto load_z = [&](int jz) {
-      const int ng = chunk_len(jz) * RO * G16;
+      const int ng = chunk_len(jz) * RT * G16;
 #pragma unroll
       for (int k = 0; k < KZ; ++k) {
         const int e = ct + k * kCT;  // clamped duplicate past the tail, never used
@@ -800,15 +829,16 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
     };
     auto store_y = [&](int jy) {
-      const int c0 = jy * Q, ng = chunk_len(jy) * R * G16;
+      const int c0 = jy * Q, ng = chunk_len(jy) * RP * G16;
       for (int e = ct; e < ng; e += kCT) {
         const int row = e / G16, gq = e % G16;
-        *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG);
+        if (real_row(row))
+          *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG);
       }
     };
     uint4 gres[KZ];
     auto gate_y = [&](int jy) {
-      const int ng = chunk_len(jy) * RO * G16;
+      const int ng = chunk_len(jy) * RT * G16;
 #pragma unroll
       for (int k = 0; k < KZ; ++k) {
         const int e = ct + k * kCT;
@@ -816,12 +846,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           const int row = e / G16, gq = e % G16;
           float v[EG], z[EG];
           if constexpr (kDown) {
-            Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + row * R * ldy + gq * EG), v);
+            Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + row * RP * ldy + gq * EG), v);
 #pragma unroll
-            for (int r = 1; r < 4; ++r) {
+            for (int r = 1; r < 8; ++r) {
               if (r < R) {
                 float w[EG];
-                Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + (row * R + r) * ldy + gq * EG), w);
+                Gran<IO>::unpack(*reinterpret_cast<const uint4*>(sY + (row * RP + r) * ldy + gq * EG), w);
 #pragma unroll
                 for (int q = 0; q < EG; ++q) v[q] += w[q];
               }
@@ -842,11 +872,11 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
     };
     auto store_gated = [&](int jy) {
-      const int c0 = jy * Q, ng = chunk_len(jy) * RO * G16;
+      const int c0 = jy * Q, ng = chunk_len(jy) * RT * G16;
 #pragma unroll
       for (int k = 0; k < KZ; ++k) {
         const int e = ct + k * kCT;
-        if (e < ng) *reinterpret_cast<uint4*>(Og + out_off(c0, e)) = gres[k];
+        if (e < ng && (kDown || real_row(e / G16))) *reinterpret_cast<uint4*>(Og + out_off(c0, e)) = gres[k];
       }
     };
     for (int i = ck0; i <= ck1; ++i) {
@@ -1065,26 +1095,32 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 
 template <typename IO, int N, int P, int EPI, bool BCN>
 hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int mode, int nblocks) {
-  const size_t lds = PcLds<IO, N, P, BCN>::bytes(PcLimits<IO, N, P>::kMaxRows);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;  // (the host checks this first)
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI, BCN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  // instances whose tiles fit at no height are never launched (the host
+  // checks this first), so their kernels are not compiled
+  if constexpr (PcLimits<IO, N, P>::kMaxRows == 0) {
+    return hipErrorInvalidValue;
+  } else {
+    const size_t lds = PcLds<IO, N, P, BCN>::bytes(PcLimits<IO, N, P>::kMaxRows);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;  // (the host checks this first)
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI, BCN>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    PcParams kp;
+    kp.a = a;
+    kp.batch = d.batch;
+    kp.heads = d.heads;
+    kp.R = d.R;
+    kp.lgR = pad_rank_log2(d.R);
+    kp.Q = d.Q;
+    kp.mode = mode;
+    kp.nblocks = nblocks;
+    hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI, BCN>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
+    return hipGetLastError();
   }
-  PcParams kp;
-  kp.a = a;
-  kp.batch = d.batch;
-  kp.heads = d.heads;
-  kp.R = d.R;
-  kp.lgR = d.R == 1 ? 0 : (d.R == 2 ? 1 : 2);
-  kp.Q = d.Q;
-  kp.mode = mode;
-  kp.nblocks = nblocks;
-  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI, BCN>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
-  return hipGetLastError();
 }
 
 template <typename IO, int N, int EPI, bool BCN>
@@ -1103,7 +1139,8 @@ hipError_t pc_n(const Dims& d, const PrefillArgs& a, hipStream_t s, int mode, in
     case 16: return pc_p<IO, 16, EPI, BCN>(d, a, s, mode, nb);
     case 32: return pc_p<IO, 32, EPI, BCN>(d, a, s, mode, nb);
     case 64: return pc_p<IO, 64, EPI, BCN>(d, a, s, mode, nb);
-    default: return pc_p<IO, 128, EPI, BCN>(d, a, s, mode, nb);
+    case 128: return pc_p<IO, 128, EPI, BCN>(d, a, s, mode, nb);
+    default: return pc_p<IO, 256, EPI, BCN>(d, a, s, mode, nb);
   }
 }
 
@@ -1121,6 +1158,7 @@ int pc_max_rows(const Dims& d) {
     M3_CASE(32, 16) M3_CASE(32, 32) M3_CASE(32, 64) M3_CASE(32, 128)
     M3_CASE(64, 16) M3_CASE(64, 32) M3_CASE(64, 64) M3_CASE(64, 128)
     M3_CASE(128, 16) M3_CASE(128, 32) M3_CASE(128, 64) M3_CASE(128, 128)
+    M3_CASE(256, 16) M3_CASE(256, 32) M3_CASE(256, 64) M3_CASE(256, 128)
 #undef M3_CASE
     default: return 0;
   }
@@ -1137,6 +1175,7 @@ bool pc_bcn_fits(const Dims& d) {
     M3_CASE(32, 16) M3_CASE(32, 32) M3_CASE(32, 64) M3_CASE(32, 128)
     M3_CASE(64, 16) M3_CASE(64, 32) M3_CASE(64, 64) M3_CASE(64, 128)
     M3_CASE(128, 16) M3_CASE(128, 32) M3_CASE(128, 64) M3_CASE(128, 128)
+    M3_CASE(256, 16) M3_CASE(256, 32) M3_CASE(256, 64) M3_CASE(256, 128)
 #undef M3_CASE
     default: return false;
   }

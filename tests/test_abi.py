@@ -82,8 +82,9 @@ def call_decode(d, ptrs=None, state=None):
     ("batch", 0, B.M3_ERR_SHAPE), ("heads", -1, B.M3_ERR_SHAPE), ("headdim", 0, B.M3_ERR_SHAPE),
     ("dstate", 0, B.M3_ERR_SHAPE), ("rank", 0, B.M3_ERR_SHAPE), ("chunk", 0, B.M3_ERR_SHAPE),
     ("io_dtype", 7, B.M3_ERR_DTYPE), ("dstate", 15, B.M3_ERR_UNSUPPORTED),
-    ("dstate", 256, B.M3_ERR_UNSUPPORTED), ("headdim", 48, B.M3_ERR_UNSUPPORTED),
-    ("rank", 3, B.M3_ERR_UNSUPPORTED), ("rank", 8, B.M3_ERR_UNSUPPORTED),
+    ("dstate", 512, B.M3_ERR_UNSUPPORTED), ("dstate", 48, B.M3_ERR_UNSUPPORTED),
+    ("headdim", 48, B.M3_ERR_UNSUPPORTED), ("headdim", 256, B.M3_ERR_UNSUPPORTED),
+    ("rank", 9, B.M3_ERR_UNSUPPORTED),
     ("chunk", 128, B.M3_ERR_UNSUPPORTED), ("chunk", 24, B.M3_ERR_UNSUPPORTED),
     ("disc", 3, B.M3_ERR_UNSUPPORTED), ("disc", -1, B.M3_ERR_UNSUPPORTED),
 ])
@@ -102,8 +103,9 @@ def test_prefill_tile_height_and_lds_limit():
     assert call_prefill(dims(io_dtype="f32", dstate=128, chunk=64), seqlen=0) == B.M3_OK
     assert call_prefill(dims(rank=4, chunk=64, dstate=128), seqlen=0) == B.M3_OK
     assert call_prefill(dims(io_dtype="f32", dstate=128, headdim=128, chunk=64), seqlen=0) == B.M3_OK
-    # ... and shapes whose rows fit no tile height down to 16 tokens are refused
-    assert call_prefill(dims(io_dtype="f32", dstate=128, rank=4, chunk=16)) == B.M3_ERR_UNSUPPORTED
+    # ... and shapes whose rows fit no tile height are refused
+    assert call_prefill(dims(io_dtype="f32", dstate=128, headdim=128, rank=4, chunk=16)) == B.M3_ERR_UNSUPPORTED
+    assert call_prefill(dims(io_dtype="f32", dstate=256, headdim=64, chunk=16)) == B.M3_ERR_UNSUPPORTED
 
 
 def _prefill_support(io, P, N, R, Q):
@@ -112,27 +114,54 @@ def _prefill_support(io, P, N, R, Q):
     return B.lib().mamba3_prefill_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(nbytes)) == B.M3_OK
 
 
+# fp32 sizes the prefill refuses at every chunk (mamba3.h lists them with
+# their LDS / register arithmetic): N = 256 except P = 16 with ranks 1, 2,
+# and P = 128 with N = 128 at ranks 3 to 8
+F32_REFUSED = sorted([(P, 256, R) for P in (16, 32, 64, 128) for R in range(1, 9) if not (P == 16 and R <= 2)]
+                     + [(128, 128, R) for R in range(3, 9)])
+
+
 def test_prefill_support_is_monotone_in_chunk():
     """The chunk is a tile height: every (dtype, P, N, R) accepted at chunk 16
-    is accepted at 32 and 64, and the only sizes refused at every chunk are
-    the ones the header lists (fp32 I/O, N = 128, R = 4, P >= 64)."""
-    refused = []
+    is accepted at 32 and 64; bf16 accepts every P in {16, 32, 64, 128}, N in
+    {16, ..., 256} and R in 1..8, and fp32 all but the listed sizes."""
     for io in ("bf16", "f32"):
+        refused = []
         for P in (16, 32, 64, 128):
-            for N in (16, 32, 64, 128):
-                for R in (1, 2, 4):
+            for N in (16, 32, 64, 128, 256):
+                for R in range(1, 9):
                     ok = [_prefill_support(io, P, N, R, Q) for Q in (16, 32, 64)]
                     if ok[0]:
                         assert ok[1] and ok[2], (io, P, N, R, ok)
                     if not any(ok):
-                        refused.append((io, P, N, R))
-    assert refused == [("f32", 64, 128, 4), ("f32", 128, 128, 4)]
+                        refused.append((P, N, R))
+        assert sorted(refused) == ([] if io == "bf16" else F32_REFUSED), (io, refused)
 
 
 def test_decode_checks_dims():
     assert call_decode(dims(dstate=15)) == B.M3_ERR_UNSUPPORTED
-    assert call_decode(dims(rank=3)) == B.M3_ERR_UNSUPPORTED
+    assert call_decode(dims(dstate=48)) == B.M3_ERR_UNSUPPORTED
+    assert call_decode(dims(dstate=512)) == B.M3_ERR_UNSUPPORTED
+    assert call_decode(dims(rank=9)) == B.M3_ERR_UNSUPPORTED
+    assert call_decode(dims(headdim=256)) == B.M3_ERR_UNSUPPORTED
     assert call_decode(dims(io_dtype=5)) == B.M3_ERR_DTYPE
+
+
+def _decode_support(io, P, N, R):
+    d = B.make_dims(1, 1, P, N, R, 64, io)
+    hb = ctypes.c_size_t()
+    return B.lib().m3_state_bytes(ctypes.byref(d), ctypes.byref(hb), None, None) == B.M3_OK
+
+
+def test_decode_support_set():
+    """Decode serves every headdim in {16, 32, 64, 128}, dstate in {16, ...,
+    256} and rank 1 to 8, except headdim 128 with dstate 256 at ranks above 4
+    (the matrix-core kernel's 133 KiB of state staging rows plus the rank
+    operands exceed 160 KiB of LDS, and the VALU kernel serves ranks <= 4)."""
+    for io in ("bf16", "f32"):
+        refused = [(P, N, R) for P in (16, 32, 64, 128) for N in (16, 32, 64, 128, 256) for R in range(1, 9)
+                   if not _decode_support(io, P, N, R)]
+        assert refused == [(128, 256, R) for R in (5, 6, 7, 8)], (io, refused)
 
 
 @pytest.mark.parametrize("i", range(9))
@@ -425,7 +454,7 @@ def call_prefill_noalloc(d, seqlen=16, ptrs=None, state=None):
 def test_noalloc_checks_like_prefill():
     """mamba3_prefill_noalloc validates exactly like mamba3_prefill (no
     workspace argument to check), before any HIP call."""
-    assert call_prefill_noalloc(dims(rank=3)) == B.M3_ERR_UNSUPPORTED
+    assert call_prefill_noalloc(dims(rank=9)) == B.M3_ERR_UNSUPPORTED
     assert call_prefill_noalloc(dims(), seqlen=-1) == B.M3_ERR_SHAPE
     assert call_prefill_noalloc(dims(), seqlen=0) == B.M3_OK
     for i in range(9):
