@@ -44,7 +44,6 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "state_space_sequence_prefill_amd", "csrc")
 # sources whose code the fused prefill launch runs (kernel, device helpers)
-PREFILL_SRCS = ("m3_prefill_pc.hpp", "m3_prefill_pc.hip", "m3_mfma.hpp", "m3_device.hpp")
 HEADLINE = "siso_1p5b_t4096"
 METRIC = "Mamba-3 scan prefill Mtokens/s + decode \u00b5s/step; % of MFMA / HBM peak"
 
@@ -122,26 +121,54 @@ def decode_bytes(w):
     return 2 * h + 2 * pend + tok + y
 
 
-def source_sha():
+# sources whose code each profiled workload runs (kernels, device helpers)
+SRCS = {
+    "prefill": ("m3_prefill_pc.hpp", "m3_prefill_pc.hip", "m3_mfma.hpp", "m3_device.hpp"),
+    "segments": ("m3_prefill_pc.hpp", "m3_prefill_pc.hip", "m3_prefill.hip", "m3_mfma.hpp", "m3_device.hpp"),
+    "decode": ("m3_decode.hip", "m3_decode_mimo.hip", "m3_device.hpp"),
+}
+# kernels whose dispatches make up one step of each kind
+KERNELS = {
+    "prefill": ("prefill_pc_kernel", "prefill_kernel<"),
+    "segments": ("prefill_pc_kernel", "prefill_kernel<", "segment_scan_kernel"),
+    "decode": ("decode_kernel", "decode_mimo_kernel"),
+}
+
+
+def workload_kind(name):
+    if name.startswith("decode"):
+        return "decode"
+    return "segments" if name == "long_siso_t16384" else "prefill"
+
+
+def source_sha(kind="prefill"):
     h = hashlib.sha256()
-    for name in PREFILL_SRCS:
+    for name in SRCS[kind]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload_name):
+    return os.path.join(PROFILES, f"traffic_{workload_name}.json")
+
+
 def committed_traffic(workload_name):
-    """Per-launch HBM bytes measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    """Per-step HBM bytes measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
     counters (scaled by the copy-kernel calibration), if they were recorded
-    for the current kernel sources (profiles/prefill_pc_<workload>_traffic.json)."""
-    p = os.path.join(PROFILES, f"prefill_pc_{workload_name}_traffic.json")
+    for the current kernel sources (profiles/traffic_<workload>.json)."""
+    p = traffic_path(workload_name)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != source_sha():
+    if rec.get("kernel_source_sha") != source_sha(workload_kind(workload_name)):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_step")
+
+
+RAMP_MIN_LAUNCHES = 200
+RAMP_MIN_MS = 100.0
 
 
 class Prefill:
@@ -187,6 +214,20 @@ class Prefill:
                                          down=dw)
         if ev is not None:
             ev[1].record()
+
+    def ramp(self, min_launches, min_ms):
+        """Untimed steps until at least min_launches launches and min_ms of
+        wall time have passed (the GPU's clocks settle meanwhile)."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 0
+        while n < min_launches or (time.perf_counter() - t0) * 1e3 < min_ms:
+            for _ in range(20):
+                self.step()
+            n += 20
+            torch.cuda.synchronize()
+        return {"launches": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
 
     def time(self, steps, warmup):
         torch = self.torch
@@ -442,15 +483,40 @@ def _cpu_model():
     return "unknown"
 
 
-def profile_prefill(steps):
-    """A few untimed prefill launches of the headline workload (for rocprofv3)."""
+def profile_prefill(steps, name):
+    """A few untimed prefill steps of one workload (for rocprofv3)."""
     import torch
     from state_space_sequence_prefill_amd import synthetic as syn
-    pf = Prefill(syn.WORKLOADS[HEADLINE], seed=1001)
+    pf = Prefill(syn.WORKLOADS[name], seed=1001)
     for _ in range(steps):
         pf.step()
     torch.cuda.synchronize()
-    log(f"bench: {steps} prefill launches of {HEADLINE} done")
+    log(f"bench: {steps} prefill steps of {name} done")
+
+
+def profile_decode(steps, name):
+    """A few untimed decode steps of one workload, each after a 512 MiB write
+    that evicts the state from the Infinity Cache (for rocprofv3: the decode
+    kernel then streams its state from HBM)."""
+    import torch
+    import state_space_sequence_prefill_amd as m3
+    from state_space_sequence_prefill_amd import synthetic as syn
+    w = syn.WORKLOADS[name]
+    d = m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype)
+    tok = syn.draw_torch(w, 7, seqlen=1)
+    tok = {k: (v[:, 0].contiguous() if v.dim() >= 3 else v) for k, v in tok.items()}
+    st = m3.State.empty(d)
+    st.h.normal_()
+    st.B_prev.zero_()
+    st.x_prev.zero_()
+    y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=tok["x"].dtype, device="cuda")
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    for _ in range(steps):
+        flush.zero_()
+        m3.mamba3_decode_step(d, tok["x"], tok["B"], tok["C"], tok["dt"], tok["lam"], tok["theta"], tok["A"],
+                              tok["D"], st, y)
+    torch.cuda.synchronize()
+    log(f"bench: {steps} flushed decode steps of {name} done")
 
 
 def profile_copy(steps):
@@ -499,6 +565,54 @@ def measured_copy_gbs(steps=20):
     return round(moved / (ms / 1e3) / 1e9, 1)
 
 
+PROBE_LIB = os.path.join(ROOT, "state_space_sequence_prefill_amd", "libm3probe.so")
+
+
+def probe_bandwidth(mib=1024, steps=10, blocks=(256, 512, 1024, 2048, 4096)):
+    """Streaming ceilings of this GPU from the probe kernels (libm3probe.so,
+    built beside the scan library): read-only, write-only and copy over a
+    `mib` MiB buffer (twice the 256 MB Infinity Cache), each at several
+    workgroup counts; GB/s of bytes moved over the average launch time (HIP
+    events), best workgroup count reported."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(PROBE_LIB)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.m3probe_read.argtypes = [vp, sz, vp, ctypes.c_int, vp]
+    L.m3probe_write.argtypes = [vp, sz, ctypes.c_int, vp]
+    L.m3probe_copy.argtypes = [vp, vp, sz, ctypes.c_int, vp]
+    nbytes = mib * 1024 * 1024
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    out = torch.empty(max(blocks), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    runs = {
+        "read": (lambda nb: L.m3probe_read(a.data_ptr(), nbytes, out.data_ptr(), nb, st), nbytes),
+        "write": (lambda nb: L.m3probe_write(b.data_ptr(), nbytes, nb, st), nbytes),
+        "copy": (lambda nb: L.m3probe_copy(b.data_ptr(), a.data_ptr(), nbytes, nb, st), 2 * nbytes),
+    }
+    res = {}
+    for name, (fn, moved) in runs.items():
+        best = (0.0, 0)
+        for nb in blocks:
+            for _ in range(3):
+                assert fn(nb) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn(nb)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = moved / (e0.elapsed_time(e1) / steps / 1e3) / 1e9
+            best = max(best, (round(gbs, 1), nb))
+        res[f"{name}_GBs"] = best[0]
+        res[f"{name}_workgroups"] = best[1]
+    res["buffer_MiB"] = mib
+    del a, b, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def _counter_per_dispatch(run_dir, counter, kernel_substr, largest=False):
     """Mean (or, with largest, the maximum) value per dispatch of a counter
     from a rocprofv3 counter_collection.csv under run_dir."""
@@ -517,28 +631,104 @@ def _counter_per_dispatch(run_dir, counter, kernel_substr, largest=False):
     return max(vals) if largest else sum(vals) / len(vals)
 
 
-def record_traffic(base):
-    """Write profiles/prefill_pc_<workload>_traffic.json from four rocprofv3
-    counter runs under `base`: prefill_fetch, prefill_write (FETCH_SIZE /
-    WRITE_SIZE of the prefill launches) and copy_fetch, copy_write (the same
-    counters for the 256 MiB copy).  Counters are KiB per dispatch; each is
-    scaled by known copy bytes / counter reading of the copy."""
+def _counter_by_dispatch(run_dir, counter, kernel_substrs):
+    """{(file, dispatch id): (kernel name, summed value)} of a counter from
+    the rocprofv3 counter_collection.csv files under run_dir, for the
+    dispatches whose kernel name contains one of kernel_substrs."""
+    import csv
+    import glob
+    tot = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and any(k in r["Kernel_Name"] for k in kernel_substrs):
+                    key = (f, r["Dispatch_Id"])
+                    name, v = tot.get(key, (r["Kernel_Name"], 0.0))
+                    tot[key] = (name, v + float(r["Counter_Value"]))
+    if not tot:
+        raise SystemExit(f"no {counter} rows for {kernel_substrs} under {run_dir}")
+    return tot
+
+
+def record_traffic(base, name, steps):
+    """Write profiles/traffic_<workload>.json from four rocprofv3 counter
+    runs under `base`: <workload>_fetch, <workload>_write (FETCH_SIZE /
+    WRITE_SIZE over `steps` profiled steps of the workload) and copy_fetch,
+    copy_write (the same counters for the 256 MiB copy).  Counters are KiB
+    per dispatch; each is scaled by known copy bytes / the copy's reading.
+    Per step: the sum over every dispatch of the step's kernels / steps."""
     copy_bytes = 256 * 32 * 64 * 128 * 4
     cf = _counter_per_dispatch(os.path.join(base, "copy_fetch"), "FETCH_SIZE", "copy_kernel", largest=True) * 1024
     cw = _counter_per_dispatch(os.path.join(base, "copy_write"), "WRITE_SIZE", "copy_kernel", largest=True) * 1024
-    pf = _counter_per_dispatch(os.path.join(base, "prefill_fetch"), "FETCH_SIZE", "prefill_pc_kernel") * 1024
-    pw = _counter_per_dispatch(os.path.join(base, "prefill_write"), "WRITE_SIZE", "prefill_pc_kernel") * 1024
+    kind = workload_kind(name)
+    fetch = _counter_by_dispatch(os.path.join(base, f"{name}_fetch"), "FETCH_SIZE", KERNELS[kind])
+    write = _counter_by_dispatch(os.path.join(base, f"{name}_write"), "WRITE_SIZE", KERNELS[kind])
     kf, kw = copy_bytes / cf, copy_bytes / cw
+    per_kernel = {}
+    for recs, field, k in ((fetch, "fetch_bytes", kf), (write, "write_bytes", kw)):
+        for kname, v in recs.values():
+            short = next(x for x in KERNELS[kind] if x in kname).rstrip("<")
+            e = per_kernel.setdefault(short, {"dispatches": 0, "fetch_bytes": 0.0, "write_bytes": 0.0})
+            e[field] += v * 1024 * k
+            if field == "fetch_bytes":
+                e["dispatches"] += 1
+    for e in per_kernel.values():
+        e["fetch_bytes_per_dispatch"] = round(e.pop("fetch_bytes") / e["dispatches"])
+        e["write_bytes_per_dispatch"] = round(e.pop("write_bytes") / e["dispatches"])
+        e["dispatches_per_step"] = e.pop("dispatches") / steps
+    total = sum(e["dispatches_per_step"] * (e["fetch_bytes_per_dispatch"] + e["write_bytes_per_dispatch"])
+                for e in per_kernel.values())
     from state_space_sequence_prefill_amd import synthetic as syn
-    w = syn.WORKLOADS[HEADLINE]
-    rec = {"workload": HEADLINE, "kernel": "prefill_pc_kernel", "kernel_source_sha": source_sha(),
-           "fetch_bytes_raw": pf, "write_bytes_raw": pw, "copy_fetch_scale": kf, "copy_write_scale": kw,
-           "bytes_per_launch": round(pf * kf + pw * kw), "algorithmic_bytes_per_launch": prefill_bytes(w)}
+    w = syn.WORKLOADS[name]
+    alg = decode_bytes(w) if kind == "decode" else prefill_bytes(w)
+    rec = {"workload": name, "kernels": per_kernel, "kernel_source_sha": source_sha(kind),
+           "copy_fetch_scale": kf, "copy_write_scale": kw, "profiled_steps": steps,
+           "bytes_per_step": round(total), "algorithmic_bytes_per_step": alg, "ratio": round(total / alg, 4)}
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, f"prefill_pc_{HEADLINE}_traffic.json")
-    with open(out, "w") as f:
+    with open(traffic_path(name), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def summarize_counters(run_dir, name):
+    """SQ / GRBM counters of one rocprofv3 --pmc run over profiled steps of a
+    prefill workload: per dispatch of the main kernel, plus the derived MFMA
+    utilisation (busy cycles of the matrix units over the kernel's cycles x
+    1024 SIMDs), the bf16 MFMA FLOPs, the share of a CU's cycles its LDS
+    stalls on bank conflicts and the share of a SIMD's cycles spent issuing
+    VALU instructions (4 cycles per wave64 instruction)."""
+    import csv
+    import glob
+    kind = workload_kind(name)
+    acc = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if not any(k in r["Kernel_Name"] for k in KERNELS[kind]):
+                    continue
+                key = (f, r["Dispatch_Id"])
+                d = acc.setdefault(key, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not acc:
+        raise SystemExit(f"no counter rows under {run_dir}")
+    names = sorted({c for d in acc.values() for c in d})
+    mean = {c: sum(d.get(c, 0.0) for d in acc.values()) / len(acc) for c in names}
+    out = {"workload": name, "dispatches": len(acc), "per_dispatch": {c: round(v, 1) for c, v in mean.items()}}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+        # GRBM_GUI_ACTIVE comes summed over the 8 XCDs (each counts the
+        # kernel's cycles); the matrix units' busy cycles over all 1024 SIMDs
+        cycles = mean["GRBM_GUI_ACTIVE"] / 8
+        out["gpu_cycles"] = round(cycles)
+        out["mfma_busy_frac"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * 1024), 4)
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
+        out["mfma_bf16_flops"] = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    if "gpu_cycles" in out:
+        cyc = out["gpu_cycles"]
+        if "SQ_LDS_BANK_CONFLICT" in mean:  # cycles the LDS of a CU stalls on bank conflicts, over the kernel's
+            out["lds_bank_conflict_frac_per_cu"] = round(mean["SQ_LDS_BANK_CONFLICT"] / (256 * cyc), 4)
+        if "SQ_INSTS_VALU" in mean:  # wave64 VALU issue (4 cycles each) per SIMD, over the kernel's cycles
+            out["valu_issue_frac_per_simd"] = round(4 * mean["SQ_INSTS_VALU"] / (1024 * cyc), 4)
+    print(json.dumps(out))
 
 
 def main():
@@ -549,14 +739,24 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--profile-prefill", type=int, default=0, metavar="K",
-                    help="only run K untimed prefill launches (for rocprofv3)")
+                    help="only run K untimed prefill steps of --workload (for rocprofv3)")
+    ap.add_argument("--profile-decode", type=int, default=0, metavar="K",
+                    help="only run K untimed cache-flushed decode steps of --workload (for rocprofv3)")
     ap.add_argument("--profile-copy", type=int, default=0, metavar="K",
                     help="only run K 256 MiB copies (counter calibration)")
+    ap.add_argument("--probe-bandwidth", action="store_true",
+                    help="only print the streaming read / write / copy ceilings (probe kernels)")
+    ap.add_argument("--workload", default=None, help="workload of the profile and record modes")
     ap.add_argument("--record-traffic", metavar="DIR",
-                    help="write the traffic record from rocprofv3 counter runs under DIR (no GPU)")
+                    help="write profiles/traffic_<workload>.json from rocprofv3 counter runs under DIR (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the SQ/GRBM counters of a rocprofv3 --pmc run under DIR (no GPU)")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic(args.record_traffic)
+        record_traffic(args.record_traffic, args.workload or HEADLINE, args.profile_prefill or args.profile_decode)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload or HEADLINE)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every (batch, head) chain of the scan is independent, so "
@@ -569,16 +769,26 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
-    if args.profile_prefill or args.profile_copy:
+    if args.profile_prefill or args.profile_decode or args.profile_copy or args.probe_bandwidth:
         if args.profile_prefill:
-            profile_prefill(args.profile_prefill)
+            profile_prefill(args.profile_prefill, args.workload or HEADLINE)
+        if args.profile_decode:
+            profile_decode(args.profile_decode, args.workload or "decode_siso_n128")
         if args.profile_copy:
             profile_copy(args.profile_copy)
+        if args.probe_bandwidth:
+            print(json.dumps(probe_bandwidth()))
         return
 
     w = syn.WORKLOADS[HEADLINE]
-    log(f"bench: prefill {w.name} warmup={args.warmup} steps={args.steps}")
     pf = Prefill(w, seed=1001)
+    # Declared clock ramp (untimed, before the warm-up and the timed steps):
+    # from idle the GPU's clocks take ~100 prefill launches to settle, so
+    # whatever --warmup asks for, the headline first runs prefill steps until
+    # both RAMP_MIN_LAUNCHES launches and RAMP_MIN_MS of wall time have passed.
+    ramp = pf.ramp(RAMP_MIN_LAUNCHES, RAMP_MIN_MS)
+    log(f"bench: clock ramp {ramp['launches']} launches / {ramp['ms']} ms; prefill {w.name} "
+        f"warmup={args.warmup} steps={args.steps}")
     ms_step, kern_ms = pf.time(args.steps, args.warmup)
     tokens = w.batch * w.seqlen
     value = tokens / (ms_step / 1e3) / 1e6
@@ -598,6 +808,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "clock_ramp": ramp,
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "headdim": w.headdim,
                    "dstate": w.dstate, "rank": w.rank, "seqlen": w.seqlen, "chunk": w.chunk,
                    "io_dtype": w.io_dtype, "state_dtype": "f32", "parallelism": "single GPU"},
@@ -613,12 +824,18 @@ def main():
     cg = measured_copy_gbs()
     line["roofline"]["measured_copy_GBs"] = cg
     line["roofline"]["frac_of_measured_copy"] = round(achieved / cg, 4)
+    if os.path.exists(PROBE_LIB):
+        log("bench: streaming probes")
+        pb = probe_bandwidth()
+        line["roofline"]["measured_stream"] = pb
+        line["roofline"]["frac_of_measured_read"] = round(achieved / pb["read_GBs"], 4)
 
     if not args.no_extra:
         extra = {}
         for name in ("decode_mimo_r4_n64", "decode_siso_n128"):
             log(f"bench: decode {name}")
             extra[name] = time_decode(syn.WORKLOADS[name], seed=7)
+            extra[name]["traffic_flushed"] = committed_traffic(name)
             torch.cuda.empty_cache()
         for name in ("mimo_r4_t4096", "long_siso_t16384"):
             wx = syn.WORKLOADS[name]
@@ -626,9 +843,11 @@ def main():
             p = Prefill(wx, seed=1002)
             ms, kms = p.time(max(3, args.steps // 2), 2)
             nb = prefill_bytes(wx)
-            extra[name] = {"ms_per_step": round(ms, 4), "Mtokens_per_s": round(wx.batch * wx.seqlen / ms / 1e3, 3),
+            extra[name] = {"ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+                           "Mtokens_per_s": round(wx.batch * wx.seqlen / ms / 1e3, 3),
                            "launches": p.nlaunch, "algorithmic_bytes": nb,
-                           "hbm_frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                           "hbm_frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "traffic": committed_traffic(name)}
             del p
             torch.cuda.empty_cache()
         # the other discretisation rules on the headline shape (same kernel;

@@ -2,9 +2,11 @@
 
     python -m state_space_sequence_prefill_amd.build
 
-Compiles every source under csrc/ with hipcc into objects under _build/ (in
-parallel) and links them into state_space_sequence_prefill_amd/libmamba3.so.
-Always recompiles.  No GPU is needed: hipcc cross-compiles for gfx950.
+Compiles every source of the library with hipcc into objects under _build/
+(in parallel) and links them into state_space_sequence_prefill_amd/libmamba3.so,
+and the bandwidth probes of the measurement harness (csrc/m3_probe.hip) into
+libm3probe.so beside it.  Always recompiles.  No GPU is needed: hipcc
+cross-compiles for gfx950.
 """
 
 import concurrent.futures as cf
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmamba3.so")
+PROBE_LIB = os.path.join(PKG, "libm3probe.so")
+PROBE_SOURCES = ["m3_probe.hip"]
 SOURCES = ["m3_api.cpp", "m3_state.hip", "m3_decode.hip", "m3_decode_mimo.hip", "m3_prefill.hip", "m3_prefill_pc.hip",
            "m3_prefill_pc_gated.hip", "m3_prefill_pc_down.hip", "m3_prefill_pc_bcnorm.hip",
            "m3_prefill_pc_bcnorm_gated.hip", "m3_prefill_pc_bcnorm_down.hip", "m3_backward.hip",
@@ -61,18 +65,24 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 
