@@ -512,6 +512,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           sclC[2] = rsqrtf(tc.z * inN + a.neps); sclC[3] = rsqrtf(tc.w * inN + a.neps);
         }
         float bt[4][8];
+        float cs4[4], sn4[4];  // sines and cosines of the current row's token
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int rho = 4 * rg + k;
@@ -525,15 +526,14 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 #pragma unroll
             for (int e = 0; e < 8; ++e) bv[e] *= sGw[(crole ? N : 0) + 8 * pg + e] * sclB[k];
           }
-          float cs4[4], sn4[4];
+          // rows of one token share its angles: with RP rows per token only
+          // the first row of each token evaluates them (a uniform branch)
+          if ((k & (RP - 1)) == 0) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float sn, cs;
-            trig<IO>(ph[k][j], sn, cs);
-            cs4[j] = cs;
-            sn4[j] = sn;
-            rot2(bv[2 * j], bv[2 * j + 1], cs4[j], -sn4[j]);
+            for (int j = 0; j < 4; ++j) trig<IO>(ph[k][j], sn4[j], cs4[j]);
           }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rot2(bv[2 * j], bv[2 * j + 1], cs4[j], -sn4[j]);
           const float wt = valid ? sW[t < Q ? t : 0] : 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) bt[k][e] = bv[e] * wt;
@@ -795,10 +795,11 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     const size_t tokO = (size_t)H * RO * P;          // output row stride per token
     const IO* Zg = gated ? static_cast<const IO*>(a.gz) + ((size_t)b * T * H + hh) * RO * P : nullptr;
     IO* const Og = static_cast<IO*>(a.y) + ((size_t)b * T * H + hh) * RO * P;
+    const bool padr = R != RP;  // padded ranks present (uniform)
     auto out_off = [&](int c0, int e) -> size_t {
       const int row = e / G16, gq = e % G16;
       if constexpr (kDown) return (size_t)(c0 + row) * tokO + gq * EG;
-      return (size_t)(c0 + (row >> lgR)) * tokO + rank_of(row) * P + gq * EG;
+      return (size_t)(c0 + (row >> lgR)) * tokO + (padr ? rank_of(row) : (row & (RP - 1))) * P + gq * EG;
     };
     float gwr[EG];
     uint4 zr[KZ];
@@ -830,10 +831,18 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     };
     auto store_y = [&](int jy) {
       const int c0 = jy * Q, ng = chunk_len(jy) * RP * G16;
-      for (int e = ct; e < ng; e += kCT) {
-        const int row = e / G16, gq = e % G16;
-        if (real_row(row))
-          *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG);
+      if (R == RP) {  // no padded ranks (uniform branch): every tile row is stored, no rank checks
+        for (int e = ct; e < ng; e += kCT) {
+          const int row = e / G16, gq = e % G16;
+          *reinterpret_cast<uint4*>(Yg + (size_t)(c0 + (row >> lgR)) * tokX + (row & (RP - 1)) * P + gq * EG) =
+              *reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG);
+        }
+      } else {
+        for (int e = ct; e < ng; e += kCT) {
+          const int row = e / G16, gq = e % G16;
+          if (real_row(row))
+            *reinterpret_cast<uint4*>(Yg + gran_off(c0, e)) = *reinterpret_cast<const uint4*>(sY + row * ldy + gq * EG);
+        }
       }
     };
     uint4 gres[KZ];
@@ -876,7 +885,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
 #pragma unroll
       for (int k = 0; k < KZ; ++k) {
         const int e = ct + k * kCT;
-        if (e < ng && (kDown || real_row(e / G16))) *reinterpret_cast<uint4*>(Og + out_off(c0, e)) = gres[k];
+        if (e < ng && (kDown || !padr || real_row(e / G16))) *reinterpret_cast<uint4*>(Og + out_off(c0, e)) = gres[k];
       }
     };
     for (int i = ck0; i <= ck1; ++i) {
