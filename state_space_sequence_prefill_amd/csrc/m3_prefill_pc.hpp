@@ -1000,33 +1000,54 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             Frag<IO> Xf[KSM];  // K = keys in natural order, as the score rows below
 #pragma unroll
             for (int ks = 0; ks < KSM; ++ks) Xf[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
+            // every row block's products first, then the y stores: a store to
+            // the output tile between them would keep the next block's LDS
+            // reads (which the compiler cannot tell apart from it) from being
+            // issued ahead, and each product would wait a full LDS round trip
+            f32x4 yacc[RBM];
+            // C~ rows of the next row block are read while this block's
+            // products run (two register sets)
+            Frag<IO> Cf2[2][NS];
+            auto load_cf = [&](int rb, Frag<IO> (&cf)[NS]) {
+#pragma unroll
+              for (int ns = 0; ns < NS; ++ns) {
+                const IO* cr = bf.sC + (16 * rb + c) * LDN + 32 * ns + 4 * g;
+                cf[ns].load44(cr, cr + 16);
+              }
+            };
+            load_cf(0, Cf2[0]);
 #pragma unroll
             for (int rb = 0; rb < RBM; ++rb) {
               const int rho = 16 * rb + c;
               f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-              {
-                Frag<IO> Cf[NS];
+              // (LDS reads return in order: the row's decay first, so that
+              // waiting for it does not wait for the tiles)
+              const int tq = rho >> lgR;
+              const float lqs = co.sTok[tq < Q ? tq : Q - 1].z;
+              Frag<IO> SMf[KSM];
 #pragma unroll
-                for (int ns = 0; ns < NS; ++ns) {
-                  const IO* cr = bf.sC + rho * LDN + 32 * ns + 4 * g;
-                  Cf[ns].load44(cr, cr + 16);
-                }
+              for (int ks = 0; ks < KSM; ++ks)
+                if (2 * ks <= rb) SMf[ks].load8(sSM + rho * ldr + 32 * ks + 8 * g);
+              if (rb + 1 < RBM) load_cf(rb + 1, Cf2[(rb + 1) & 1]);
+              // the reads above stay ahead of this block's products
+              __builtin_amdgcn_sched_barrier(0);
+              {
+                Frag<IO>(&Cf)[NS] = Cf2[rb & 1];
 #pragma unroll
                 for (int ns = 0; ns < NS; ++ns) mma(acc, Hf[ns], Cf[ns]);
-                const int tq = rho >> lgR;
-                acc = acc * __builtin_amdgcn_exp2f(co.sTok[tq < Q ? tq : Q - 1].z);
+                acc = acc * __builtin_amdgcn_exp2f(lqs);
               }
 #pragma unroll
-              for (int ks = 0; ks < KSM; ++ks) {
-                if (2 * ks <= rb) {
-                  Frag<IO> SMf;
-                  SMf.load8(sSM + rho * ldr + 32 * ks + 8 * g);
-                  mma(acc, Xf[ks], SMf);
-                }
-              }
+              for (int ks = 0; ks < KSM; ++ks)
+                if (2 * ks <= rb) mma(acc, Xf[ks], SMf[ks]);
+              yacc[rb] = acc;
+            }
+#pragma unroll
+            for (int rb = 0; rb < RBM; ++rb) {
               // y (row rho, columns 16pb + 4g .. +3) into the output tile
               // (down-projection: scaled by the weights of rank rho % R)
-              float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+              const int rho = 16 * rb + c;
+              float v[4] = {yacc[rb][0], yacc[rb][1], yacc[rb][2], yacc[rb][3]};
               if constexpr (kDown) {
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) v[i4] *= dwr[u][i4];
