@@ -208,7 +208,8 @@ int mamba3_prefill(const m3_dims* dims, int32_t seqlen, const void* x, const voi
  * shares that GPU's scratch: calls that overlap on one GPU (other streams,
  * other threads) race and must be serialised by the caller.  The scratch
  * needs no clearing between calls (a call writes everything it reads), and
- * results are identical to mamba3_prefill's.  ABI version 6. */
+ * results are identical to mamba3_prefill's.  The scratch is the current
+ * device's, so `stream` must belong to the current device.  ABI version 6. */
 int mamba3_prefill_noalloc(const m3_dims* dims, int32_t seqlen, const void* x, const void* B,
                            const void* C, const float* dt, const float* lam, const float* theta,
                            const float* A, const float* D, m3_state* state, void* y, void* stream);
