@@ -621,8 +621,13 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // consumers' shared score tile of chunk i-1 (other buffers); the first
     // barrier ends both, and the coefficient work and the next loads then
     // overlap the consumers' outputs and state update.
+    // Wave priorities (issue arbitration on a SIMD, where one producer and
+    // one consumer wave share the issue slots): the tile build is the longer
+    // side of the first phase, so it runs at raised priority.
     auto step = [&](int i, PcRaw<IO, MI, MX>& rs, const PcRaw<IO, MI, MX>& rsn) {
+      __builtin_amdgcn_s_setprio(2);
       build_tiles(i, rs);
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       const int n1 = i + 1 < ck1 ? i + 1 : i;  // clamped: past the end the data is reloaded, not used
       const int n2 = i + 2 < ck1 ? i + 2 : n1;
@@ -670,7 +675,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       if (i < ck1) step(i, rsA, rsB);
     } else {
       for (int i = ck0; i < ck1; ++i) {
+        __builtin_amdgcn_s_setprio(2);
         build_tiles(i, rsA);
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         const int n1 = i + 1 < ck1 ? i + 1 : i;
         const int n2 = i + 2 < ck1 ? i + 2 : n1;
@@ -977,6 +984,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
       }
       __syncthreads();
       // ---- phase 2: outputs and state update for this wave's p-blocks ----
+      // Their work grows with the state size (the carried-state product and
+      // the state update); from N = 128 on they are the longer side of the
+      // second phase and run at raised priority.  Measured on the 1.5B-scale
+      // shapes: N = 128 SISO 0.2826 -> 0.2770 ms with it; N = 64 MIMO R = 4,
+      // whose producers' second phase is as long, 0.686 -> 0.696 ms with it.
+      if constexpr (N >= 128) __builtin_amdgcn_s_setprio(2);
       if (i > ck0) {
         const int j = i - 1;
         const int c0 = j * Q, Lc = chunk_len(j);
@@ -1103,6 +1116,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
     }
     if (gated && ck1 > ck0) {
