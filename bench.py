@@ -521,8 +521,9 @@ def profile_decode(steps, name):
 
 def profile_copy(steps):
     """Copies of a known size through the library's copy kernel (m3_state_load
-    of a 256 x 32 x 64 x 128 fp32 state, 256 MiB read + 256 MiB written per
-    launch): the calibration for rocprofv3's FETCH_SIZE / WRITE_SIZE."""
+    of a 256 x 32 x 64 x 128 state: the fp32 h of 256 MiB and the bf16 pending
+    pair of 3 MiB, read and written in one launch): the calibration for
+    rocprofv3's FETCH_SIZE / WRITE_SIZE."""
     import torch
     import state_space_sequence_prefill_amd as m3
     d = m3.make_dims(256, 32, 64, 128, 1, 64, "bf16")
@@ -534,7 +535,7 @@ def profile_copy(steps):
     for _ in range(steps):
         m3.m3_state_load(d, dst, src.h, src.B_prev, src.x_prev)
     torch.cuda.synchronize()
-    log(f"bench: {steps} state copies of {dst.h.numel() * 4} bytes done")
+    log(f"bench: {steps} state copies of {dst.h.numel() * 4 + dst.B_prev.numel() * 2 + dst.x_prev.numel() * 2} bytes done")
 
 
 def measured_copy_gbs(steps=20):
@@ -654,10 +655,10 @@ def record_traffic(base, name, steps):
     """Write profiles/traffic_<workload>.json from four rocprofv3 counter
     runs under `base`: <workload>_fetch, <workload>_write (FETCH_SIZE /
     WRITE_SIZE over `steps` profiled steps of the workload) and copy_fetch,
-    copy_write (the same counters for the 256 MiB copy).  Counters are KiB
+    copy_write (the same counters for the 259 MiB state copy).  Counters are KiB
     per dispatch; each is scaled by known copy bytes / the copy's reading.
     Per step: the sum over every dispatch of the step's kernels / steps."""
-    copy_bytes = 256 * 32 * 64 * 128 * 4
+    copy_bytes = 256 * 32 * (64 * 128 * 4 + 128 * 2 + 64 * 2)  # h, B_prev, x_prev of the calibration copy
     cf = _counter_per_dispatch(os.path.join(base, "copy_fetch"), "FETCH_SIZE", "copy_kernel", largest=True) * 1024
     cw = _counter_per_dispatch(os.path.join(base, "copy_write"), "WRITE_SIZE", "copy_kernel", largest=True) * 1024
     kind = workload_kind(name)

@@ -162,9 +162,9 @@ int m3_state_zero(const m3_dims* dims, m3_state* state, void* stream) {
   size_t hb, bb, xb;
   state_sizes(dims, &hb, &bb, &xb);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = m3::launch_fill_zero(state->h, hb, s);
-  if (e == hipSuccess) e = m3::launch_fill_zero(state->B_prev, bb, s);
-  if (e == hipSuccess) e = m3::launch_fill_zero(state->x_prev, xb, s);
+  void* const p[3] = {state->h, state->B_prev, state->x_prev};
+  const size_t n[3] = {hb, bb, xb};
+  const hipError_t e = m3::launch_fill_zero3(p, n, s);
   return hip_status(e, "m3_state_zero");
 }
 
@@ -180,9 +180,10 @@ int m3_state_load(const m3_dims* dims, m3_state* dst, const float* h, const void
   size_t hb, bb, xb;
   state_sizes(dims, &hb, &bb, &xb);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = m3::launch_copy(dst->h, h, hb, s);
-  if (e == hipSuccess) e = m3::launch_copy(dst->B_prev, B_prev, bb, s);
-  if (e == hipSuccess) e = m3::launch_copy(dst->x_prev, x_prev, xb, s);
+  void* const d[3] = {dst->h, dst->B_prev, dst->x_prev};
+  const void* const from[3] = {h, B_prev, x_prev};
+  const size_t n[3] = {hb, bb, xb};
+  const hipError_t e = m3::launch_copy3(d, from, n, s);
   return hip_status(e, "m3_state_load");
 }
 
@@ -198,9 +199,10 @@ int m3_state_readout(const m3_dims* dims, const m3_state* src, float* h, void* B
   size_t hb, bb, xb;
   state_sizes(dims, &hb, &bb, &xb);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = m3::launch_copy(h, src->h, hb, s);
-  if (e == hipSuccess) e = m3::launch_copy(B_prev, src->B_prev, bb, s);
-  if (e == hipSuccess) e = m3::launch_copy(x_prev, src->x_prev, xb, s);
+  void* const d[3] = {h, B_prev, x_prev};
+  const void* const from[3] = {src->h, src->B_prev, src->x_prev};
+  const size_t n[3] = {hb, bb, xb};
+  const hipError_t e = m3::launch_copy3(d, from, n, s);
   return hip_status(e, "m3_state_readout");
 }
 

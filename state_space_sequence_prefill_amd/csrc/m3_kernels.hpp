@@ -112,8 +112,9 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const Dims& d, const PrefillArgs& a, hipStream_t s);
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+// Zero three buffers, or copy three, in one launch (16-byte aligned pointers).
+hipError_t launch_fill_zero3(void* const p[3], const size_t bytes[3], hipStream_t s);
+hipError_t launch_copy3(void* const dst[3], const void* const src[3], const size_t bytes[3], hipStream_t s);
 
 bool decode_supported(const Dims& d);
 // Rank >= 2 decode on the matrix cores (m3_decode_mimo.hip).

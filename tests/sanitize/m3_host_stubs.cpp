@@ -29,8 +29,8 @@ size_t backward_workspace_bytes(const Dims& d, int seqlen) {
 }
 hipError_t launch_decode(const Dims&, const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_prefill(const Dims&, const PrefillArgs&, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_fill_zero(void*, size_t, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_copy(void*, const void*, size_t, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_fill_zero3(void* const*, const size_t*, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_copy3(void* const*, const void* const*, const size_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_backward(const Dims&, const BackwardArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t noalloc_scratch(void**) { return hipErrorNoDevice; }
 
