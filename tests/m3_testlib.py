@@ -115,15 +115,23 @@ def to_gpu(arr, io_dtype, key):
 
 
 def inputs_on_gpu(w, seed, long_memory=False, seqlen=None, zero_D=False, dt_scale=1.0, a_scale=1.0,
-                  resets=(), big_angles=0.0):
+                  resets=(), big_angles=0.0, degenerate=False):
     """Returns (exact fp64 dict, torch dict) for workload w.  dt_scale and
     a_scale stretch dt (and the dt-scaled angles) and A, e.g. for strong decay.
     resets: (token, log_decay) pairs; that token's dt is set so that dt * A
     equals log_decay in every chain (a state reset; its angle is left as
     drawn).  big_angles > 0 adds a one-signed angle of big_angles * U(1, 2)
     radians per (token, pair), so chunk-local angle sums run to thousands of
-    radians."""
+    radians.  degenerate: the method's boundary cases in one input: no
+    rotation at all in the even heads (theta = 0), every 7th token without
+    step (dt = 0: no decay and zero input weights), and the trapezoid weight
+    at its ends (lam = 0 on every 5th token, lam = 1 on every 3rd)."""
     raw = syn.draw(w, seed, long_memory=long_memory, seqlen=seqlen)
+    if degenerate:
+        raw["theta"][:, :, 0::2, :] = 0.0
+        raw["dt"][:, 0::7, :] = 0.0
+        raw["lam"][:, 0::5, :] = 0.0
+        raw["lam"][:, 0::3, :] = 1.0
     if zero_D:
         raw["D"] = np.zeros_like(raw["D"])
     if dt_scale != 1.0:

@@ -57,9 +57,9 @@ def make_state(w, st=None):
 
 
 def check_prefill(w, seed, pairs=None, st=None, long_memory=False, zero_D=False, tol=None, dt_scale=1.0,
-                  a_scale=1.0, disc=0, resets=(), big_angles=0.0, token_factor=None):
+                  a_scale=1.0, disc=0, resets=(), big_angles=0.0, token_factor=None, degenerate=False):
     ex, tt = inputs_on_gpu(w, seed, long_memory=long_memory, zero_D=zero_D, dt_scale=dt_scale, a_scale=a_scale,
-                           resets=resets, big_angles=big_angles)
+                           resets=resets, big_angles=big_angles, degenerate=degenerate)
     s = make_state(w, st)
     y = run_prefill(w, tt, s, disc=disc)
     if pairs is None:
@@ -85,7 +85,7 @@ def check_prefill(w, seed, pairs=None, st=None, long_memory=False, zero_D=False,
 # decode
 # ---------------------------------------------------------------------------
 
-def check_decode(w, seed, steps=3, pairs=None, tol=None, disc=0, resets=(), big_angles=0.0):
+def check_decode(w, seed, steps=3, pairs=None, tol=None, disc=0, resets=(), big_angles=0.0, degenerate=False):
     d = dims_of(w, disc)
     rng_state = syn.draw_state(w, seed + 500)
     s = make_state(w, rng_state)
@@ -96,7 +96,7 @@ def check_decode(w, seed, steps=3, pairs=None, tol=None, disc=0, resets=(), big_
     hs = np.array([p[1] for p in pairs])
     cur = state_slice(cur, pairs)
     tol_arg = tol
-    ex, tt = inputs_on_gpu(w, seed, seqlen=steps, resets=resets, big_angles=big_angles)
+    ex, tt = inputs_on_gpu(w, seed, seqlen=steps, resets=resets, big_angles=big_angles, degenerate=degenerate)
     for k in range(steps):
         tok = {key: (v[:, k].contiguous() if v.dim() >= 3 else v) for key, v in tt.items()}
         y = torch.empty((w.batch, w.heads, w.rank, w.headdim), dtype=tt["x"].dtype, device="cuda")
@@ -301,6 +301,40 @@ def test_prefill_large_angles_segment_path():
 def test_decode_large_angles(io, R, N):
     w = W("tiny_siso_f32", batch=2, heads=3, headdim=64, dstate=N, rank=R, io_dtype=io, seqlen=1)
     check_decode(w, seed=4700 + R, steps=2, big_angles=20.0)
+
+
+# ---------------------------------------------------------------------------
+# degenerate inputs: no rotation (theta = 0), tokens without step (dt = 0: no
+# decay, zero input weights, so the mask's exponents are infinite and its
+# terms must come out as exact zeros), trapezoid weight at both ends
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("disc", [0, 2])
+@pytest.mark.parametrize("io,P,N,R,Q", [
+    ("bf16", 64, 128, 1, 64),   # the headline family
+    ("bf16", 64, 64, 4, 64),    # MIMO rank 4
+    ("bf16", 32, 64, 3, 32),    # padded ranks
+    ("f32", 32, 32, 2, 32),
+    ("f32", 128, 128, 1, 64),   # single-role kernel
+])
+def test_prefill_degenerate_inputs(io, P, N, R, Q, disc):
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=P, dstate=N, rank=R, seqlen=3 * Q + 11, chunk=Q,
+          io_dtype=io)
+    check_prefill(w, seed=9100 + P + N + R + disc, st=syn.draw_state(w, 9101), disc=disc, degenerate=True)
+
+
+def test_prefill_degenerate_inputs_segment_path():
+    w = W("tiny_siso_f32", batch=1, heads=2, headdim=32, dstate=64, rank=1, seqlen=64 * 24 + 9, chunk=64,
+          io_dtype="bf16")
+    assert m3.mamba3_prefill_workspace_bytes(dims_of(w), w.seqlen) > 0, "expected the segment path"
+    check_prefill(w, seed=9200, st=syn.draw_state(w, 9201), degenerate=True)
+
+
+@pytest.mark.parametrize("io,R,N", [("bf16", 1, 128), ("bf16", 4, 64), ("f32", 2, 32), ("bf16", 3, 256)])
+def test_decode_degenerate_inputs(io, R, N):
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=64, dstate=N, rank=R, seqlen=1, chunk=64, io_dtype=io)
+    # 8 steps: steps 0 and 7 have dt = 0, steps 0, 3, 6 lam = 1, step 5 lam = 0
+    check_decode(w, seed=9300 + R + N, steps=8, degenerate=True)
 
 
 @pytest.mark.parametrize("disc", [1, 2])
