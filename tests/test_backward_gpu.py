@@ -31,10 +31,10 @@ def W(name, **kw):
     return syn.WORKLOADS[name].with_(**kw)
 
 
-def run_backward(w, seed, disc=0, st=None, with_dh=True, resets=()):
+def run_backward(w, seed, disc=0, st=None, with_dh=True, resets=(), degenerate=False):
     d = m3.make_dims(w.batch, w.heads, w.headdim, w.dstate, w.rank, w.chunk, w.io_dtype, disc)
     T = w.seqlen
-    ex, tt = inputs_on_gpu(w, seed, resets=resets)
+    ex, tt = inputs_on_gpu(w, seed, resets=resets, degenerate=degenerate)
     rng = np.random.default_rng(seed + 31)
     dy = syn.round_io(rng.standard_normal((w.batch, T, w.heads, w.rank, w.headdim)), w.io_dtype)
     dh = syn.round_io(rng.standard_normal((w.batch, w.heads, w.headdim, w.dstate)), "f32") if with_dh else None
@@ -55,8 +55,8 @@ def run_backward(w, seed, disc=0, st=None, with_dh=True, resets=()):
     return ex, st_ex, dy, dh, {k: to_np(v) for k, v in grads.items()}
 
 
-def check_backward(w, seed, disc=0, st=None, with_dh=True, resets=()):
-    ex, st_ex, dy, dh, g = run_backward(w, seed, disc, st, with_dh, resets)
+def check_backward(w, seed, disc=0, st=None, with_dh=True, resets=(), degenerate=False):
+    ex, st_ex, dy, dh, g = run_backward(w, seed, disc, st, with_dh, resets, degenerate)
     ref = oracle.prefill_backward(ex["x"], ex["B"], ex["C"], ex["dt"], ex["lam"], ex["theta"], ex["A"], ex["D"],
                                   st_ex, dy, dh_final=dh, disc=disc)
     errs = {k: relerr(g[k], ref[k]) for k in NAMES if np.linalg.norm(ref[k]) > 0}
@@ -81,6 +81,16 @@ def test_backward_state_reset(io, P, N, R, T, ld):
     qu = 64 // R
     resets = [(t, ld) for t in sorted({16 // R, qu, qu + 3 * (16 // R), T - 1})]
     check_backward(w, seed=2300 + R, st=syn.draw_state(w, 2301), resets=resets)
+
+
+@pytest.mark.parametrize("disc", [0, 2])
+@pytest.mark.parametrize("io,P,N,R,T", [("f32", 32, 64, 1, 150), ("bf16", 64, 64, 4, 70), ("f32", 32, 32, 2, 90)])
+def test_backward_degenerate_inputs(io, P, N, R, T, disc):
+    """No rotation in half the heads, tokens with dt = 0 (no decay, zero
+    input weights), the trapezoid weight at 0 and 1: every gradient finite
+    and at the fp32 bar."""
+    w = W("tiny_siso_f32", batch=2, heads=2, headdim=P, dstate=N, rank=R, io_dtype=io, seqlen=T)
+    check_backward(w, seed=2400 + R + disc, st=syn.draw_state(w, 2401), disc=disc, degenerate=True)
 
 
 @pytest.mark.parametrize("io,P,N,R,T", [
