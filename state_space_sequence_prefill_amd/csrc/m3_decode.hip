@@ -224,7 +224,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
   DecodeGate<IO, R> gate;
   if (gated)
     gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * (a.gdown ? 1 : R) * P, a.gw + (size_t)hh * P,
-                  a.gdown != nullptr, P, wave, nthr / kWave, lane);
+                  a.gdown ? a.gdown + (size_t)hh * R * P : nullptr, P, wave, nthr / kWave, lane);
   // KG granules per thread (the launch picks KG with KG * threads >= total);
   // every load is unconditional (clamped duplicates are not stored).  KG = 0:
   // more granules than a register array holds, staged by a plain loop first.
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a, int heads, i
   if (gated) {
     __syncthreads();
     gate.apply(sYg, static_cast<IO*>(a.y) + (size_t)head * (a.gdown ? 1 : R) * P,
-               a.gdown ? a.gdown + (size_t)hh * R * P : nullptr, a.geps, P, wave, nthr / kWave, lane);
+               a.gdown != nullptr, a.geps, P, wave, nthr / kWave, lane);
   }
 }
 

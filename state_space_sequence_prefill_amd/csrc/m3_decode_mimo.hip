@@ -102,7 +102,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   DecodeGate<IO, R> gate;
   if (gated)
     gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * (a.gdown ? 1 : R) * P, a.gw + (size_t)hh * P,
-                  a.gdown != nullptr, P, wave, nthr / kWave, lane);
+                  a.gdown ? a.gdown + (size_t)hh * R * P : nullptr, P, wave, nthr / kWave, lane);
   // KG granules per thread in registers; KG = 0: more granules than a
   // register array holds, staged by a plain loop first
   auto granule_src = [&](int e) {
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   if (gated) {
     __syncthreads();
     gate.apply(sYg, static_cast<IO*>(a.y) + (size_t)head * (a.gdown ? 1 : R) * P,
-               a.gdown ? a.gdown + (size_t)hh * R * P : nullptr, a.geps, P, wave, nthr / kWave, lane);
+               a.gdown != nullptr, a.geps, P, wave, nthr / kWave, lane);
   }
 }
 

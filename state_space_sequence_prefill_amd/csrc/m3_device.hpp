@@ -214,16 +214,19 @@ __device__ __forceinline__ float gate_out(float s, float inv_rms, float w, float
 // by the head's weights and gated.  Wave w of nw handles rows w, w + nw, ...;
 // lane l channels l and l + 64 (P <= 128).  With the rank down-projection
 // (weights dg (R, P) of this head) the R rows are first folded into one row of
-// P channels, which wave 0 normalises and gates.  The gate and weight values
-// are fetched ahead, before the step's own loads (every array element is
-// assigned unconditionally, with selects around masked loads, so the arrays
-// stay in registers); the few projection weights are read at the end.
+// P channels, which wave 0 normalises and gates.  The gate, weight and
+// down-projection values are fetched ahead, before the step's own loads
+// (every array element is assigned unconditionally, with selects around
+// masked loads, so the arrays stay in registers): read at the end, the
+// projection weights' load latency was exposed once per head.
 template <typename IO, int R>
 struct DecodeGate {
   float z[R][2];
   float w[2];
-  __device__ __forceinline__ void prefetch(const IO* zg, const float* wg, bool down, int P, int wave, int nw,
+  float dw[R][2];  // down-projection weights of this lane's channels (wave 0)
+  __device__ __forceinline__ void prefetch(const IO* zg, const float* wg, const float* dg, int P, int wave, int nw,
                                            int lane) {
+    const bool down = dg != nullptr;
 #pragma unroll
     for (int k = 0; k < 2; ++k) w[k] = lane + 64 * k < P ? wg[lane + 64 * k] : 0.f;
 #pragma unroll
@@ -234,6 +237,7 @@ struct DecodeGate {
         const int r = down ? 0 : wave + i * nw;
         const bool ok = p < P && (down ? (i == 0 && wave == 0) : r < R);
         z[i][k] = ok ? to_f32(zg[r * P + p]) : 0.f;
+        dw[i][k] = (down && wave == 0 && p < P) ? dg[i * P + p] : 0.f;
       }
     }
   }
@@ -244,15 +248,15 @@ struct DecodeGate {
     if (lane < P) yr[lane] = from_f32<IO>(gate_out(v0, inv, w[0], z0));
     if (lane + 64 < P) yr[lane + 64] = from_f32<IO>(gate_out(v1, inv, w[1], z1));
   }
-  __device__ __forceinline__ void apply(const float* sy, IO* y, const float* dg, float eps, int P, int wave, int nw,
+  __device__ __forceinline__ void apply(const float* sy, IO* y, bool down, float eps, int P, int wave, int nw,
                                         int lane) const {
-    if (dg) {
+    if (down) {
       if (wave == 0) {
         float v0 = 0.f, v1 = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          v0 += lane < P ? dg[r * P + lane] * sy[r * P + lane] : 0.f;
-          v1 += lane + 64 < P ? dg[r * P + lane + 64] * sy[r * P + lane + 64] : 0.f;
+          v0 += lane < P ? dw[r][0] * sy[r * P + lane] : 0.f;
+          v1 += lane + 64 < P ? dw[r][1] * sy[r * P + lane + 64] : 0.f;
         }
         row(v0, v1, y, eps, P, lane, z[0][0], z[0][1]);
       }
