@@ -200,6 +200,31 @@ __device__ __forceinline__ float lane_group_sum(float v, int width) {
   return v;
 }
 
+// The same for a width known only at run time, up to MAXW (<= 16): every
+// step is computed and kept or dropped by a select, so the sum compiles
+// without branches (a branch per step costs more than the step).
+template <int MAXW>
+__device__ __forceinline__ float lane_group_sum_upto(float v, int width) {
+  static_assert(MAXW <= 16, "DPP steps only");
+  if (MAXW >= 2) {
+    const float t = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, true));
+    v = width >= 2 ? v + t : v;
+  }
+  if (MAXW >= 4) {
+    const float t = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, true));
+    v = width >= 4 ? v + t : v;
+  }
+  if (MAXW >= 8) {
+    const float t = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, true));
+    v = width >= 8 ? v + t : v;
+  }
+  if (MAXW >= 16) {
+    const float t = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, true));
+    v = width >= 16 ? v + t : v;
+  }
+  return v;
+}
+
 // The output epilogue's per-element map: weight * s * inv_rms * silu(z), with
 // silu(z) = z / (1 + exp(-z)) from the hardware exp2 and reciprocal (a correctly
 // rounded division would cost ten instructions per element).  Both limits are

@@ -358,7 +358,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
     // pieces of the chunk held in `rs`, summed over the GW lanes that share
     // the rows, into sPart (one float4 of 4 rows per lane group).  The other
     // half reads them back while building the chunk's tiles.
+    // (GW <= 8: rows_pad >= 32 gives RG >= 8; the sums take no branches)
     const int NG = npg / GW;  // lane groups per row
+    constexpr int kGWMax = (N / 8) < 8 ? (N / 8) : 8;
     auto norm_partials = [&](const PcRaw<IO, MI, MX>& rs) {
       if constexpr (BCN) {
 #pragma unroll
@@ -366,9 +368,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           float pb[4], pc[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            pb[k] = lane_group_sum(rs.b[m][k].sumsq(), GW);
-            // segment summaries never read C
-            pc[k] = (has_y && !kSplit) ? lane_group_sum(rs.c[m][k].sumsq(), GW) : 0.f;
+            pb[k] = lane_group_sum_upto<kGWMax>(rs.b[m][k].sumsq(), GW);
+            // (a segment summary holds B in the C registers and uses no C sums)
+            pc[k] = kSplit ? 0.f : lane_group_sum_upto<kGWMax>(rs.c[m][k].sumsq(), GW);
           }
           if (kSplit && ist[m] && (lane & (GW - 1)) == 0) {  // this role's matrix only
             const int grp = ipg[m] / GW + (crole ? NG : 0);
@@ -490,13 +492,17 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
                        (kq >= 3 ? th[3][j] : 0.f);
         }
         // BC normalisation, second half: this item's 4 row scales and 8
-        // column weights of B and C
+        // column weights of B and C.  The GW lanes that share the item's rows
+        // split the NG group partials between them (lane j reads groups j,
+        // j + GW, ...: one LDS round trip instead of NG) and sum the rest
+        // across the lanes.
         float sclB[4] = {1.f, 1.f, 1.f, 1.f}, sclC[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (BCN) {
           float4 tb = make_float4(0.f, 0.f, 0.f, 0.f), tc = tb;
-          for (int grp = crole ? NG : 0; grp < (crole ? 2 * NG : NG); ++grp) {  // split: this role's rows
-            if (kSplit) {
-              const float4 u = *reinterpret_cast<const float4*>(sPart + (size_t)grp * rows_pad + 4 * rg);
+          for (int grp = lane & (GW - 1); grp < NG; grp += GW) {
+            if (kSplit) {  // this role's rows
+              const float4 u =
+                  *reinterpret_cast<const float4*>(sPart + (size_t)(grp + (crole ? NG : 0)) * rows_pad + 4 * rg);
               tb.x += u.x; tb.y += u.y; tb.z += u.z; tb.w += u.w;
               continue;
             }
@@ -504,6 +510,12 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             const float4 w = *reinterpret_cast<const float4*>(sPart + (size_t)(NG + grp) * rows_pad + 4 * rg);
             tb.x += u.x; tb.y += u.y; tb.z += u.z; tb.w += u.w;
             tc.x += w.x; tc.y += w.y; tc.z += w.z; tc.w += w.w;
+          }
+          tb.x = lane_group_sum_upto<kGWMax>(tb.x, GW); tb.y = lane_group_sum_upto<kGWMax>(tb.y, GW);
+          tb.z = lane_group_sum_upto<kGWMax>(tb.z, GW); tb.w = lane_group_sum_upto<kGWMax>(tb.w, GW);
+          if (!kSplit) {
+            tc.x = lane_group_sum_upto<kGWMax>(tc.x, GW); tc.y = lane_group_sum_upto<kGWMax>(tc.y, GW);
+            tc.z = lane_group_sum_upto<kGWMax>(tc.z, GW); tc.w = lane_group_sum_upto<kGWMax>(tc.w, GW);
           }
           const float inN = 1.0f / N;
           sclB[0] = rsqrtf(tb.x * inN + a.neps); sclB[1] = rsqrtf(tb.y * inN + a.neps);
