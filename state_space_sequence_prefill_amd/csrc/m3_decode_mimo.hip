@@ -103,6 +103,20 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
   if (gated)
     gate.prefetch(static_cast<const IO*>(a.gz) + (size_t)head * (a.gdown ? 1 : R) * P, a.gw + (size_t)hh * P,
                   a.gdown ? a.gdown + (size_t)hh * R * P : nullptr, P, wave, nthr / kWave, lane);
+  // BC normalisation: when N divides the thread count every element a thread
+  // derives in step 2 has column tid % N, so its three weights (the rotation
+  // pair of B and the C column) are fetched here, ahead of the barriers
+  const bool bcn = a.nbw != nullptr;
+  const bool wpre = bcn && nthr % N == 0;
+  float wb0, wb1, wc;
+  {
+    const int n = tid % N;
+    const float* nb = wpre ? a.nbw + (size_t)hh * N : a.A;  // (a valid dummy address otherwise)
+    const float* nc = wpre ? a.ncw + (size_t)hh * N : a.A;
+    wb0 = nb[wpre ? (n & ~1) : 0];
+    wb1 = nb[wpre ? (n | 1) : 0];
+    wc = nc[wpre ? n : 0];
+  }
   // KG granules per thread in registers; KG = 0: more granules than a
   // register array holds, staged by a plain loop first
   auto granule_src = [&](int e) {
@@ -154,7 +168,6 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
 
   // ---- 1b. BC normalisation: RMS scales of the 3R rows B_prev, B, C (wave w
   //          takes rows w, w + waves, ...; lane l columns l and l + 64)
-  const bool bcn = a.nbw != nullptr;
   float* const sScl = reinterpret_cast<float*>(dsm + L::bytes(P));  // [3R], in kSclBytes
   if (bcn) {
     const int nw = nthr / kWave;
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
         const float v = to_f32(row[n]);
         ss += v * v;
       }
-      ss = lane_group_sum(ss, kWave);
+      ss = wave_sum(ss);
       if (lane == 0) sScl[j] = rsqrtf(ss * (1.0f / N) + a.neps);
     }
     __syncthreads();
@@ -196,12 +209,12 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
         sincosf(sTh[j], &s, &co);
         float b0 = to_f32(sBp[k * N + 2 * j]), b1 = to_f32(sBp[k * N + 2 * j + 1]);
         if (bcn) {
-          b0 *= nwB[2 * j] * sScl[k];
-          b1 *= nwB[2 * j + 1] * sScl[k];
+          b0 *= (wpre ? wb0 : nwB[2 * j]) * sScl[k];
+          b1 *= (wpre ? wb1 : nwB[2 * j + 1]) * sScl[k];
         }
         v = beta * ((n & 1) ? (s * b0 + co * b1) : (co * b0 - s * b1));
       } else if (k < 2 * R) {
-        v = gamma * to_f32(sBc[(k - R) * N + n]) * (bcn ? nwB[n] * sScl[k] : 1.f);
+        v = gamma * to_f32(sBc[(k - R) * N + n]) * (bcn ? (wpre ? ((n & 1) ? wb1 : wb0) : nwB[n]) * sScl[k] : 1.f);
       }
       sBk[e] = v;
     }
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(512) void decode_mimo_kernel(DecodeArgs a, int head
       sXk[e] = k < R ? to_f32(sXp[k * P + p]) : (k < 2 * R ? to_f32(sXc[(k - R) * P + p]) : 0.f);
     }
     for (int e = tid; e < R * N; e += nthr)
-      sCf[e] = to_f32(sCc[e]) * (bcn ? nwC[e % N] * sScl[2 * R + e / N] : 1.f);
+      sCf[e] = to_f32(sCc[e]) * (bcn ? (wpre ? wc : nwC[e % N]) * sScl[2 * R + e / N] : 1.f);
   }
   __syncthreads();
 

@@ -200,6 +200,21 @@ __device__ __forceinline__ float lane_group_sum(float v, int width) {
   return v;
 }
 
+// Sum over the whole wave, in every lane: the four row sums from DPP, then
+// their total from four lane reads (no LDS round trip, unlike the two
+// cross-row shuffles).  (r0 + r1) + (r2 + r3) is the value lane_group_sum(v,
+// 64) gives every lane (a + b and b + a round alike).  Needs the whole wave
+// active.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = lane_group_sum(v, 16);
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // The same for a width known only at run time, up to MAXW (<= 16): every
 // step is computed and kept or dropped by a select, so the sum compiles
 // without branches (a branch per step costs more than the step).
@@ -268,7 +283,7 @@ struct DecodeGate {
   }
   __device__ __forceinline__ void row(float v0, float v1, IO* yr, float eps, int P, int lane, float z0,
                                       float z1) const {
-    const float ss = lane_group_sum(v0 * v0 + v1 * v1, kWave);
+    const float ss = wave_sum(v0 * v0 + v1 * v1);
     const float inv = rsqrtf(ss / (float)P + eps);
     if (lane < P) yr[lane] = from_f32<IO>(gate_out(v0, inv, w[0], z0));
     if (lane + 64 < P) yr[lane + 64] = from_f32<IO>(gate_out(v1, inv, w[1], z1));
