@@ -76,7 +76,7 @@ struct PcLds {
     return (size_t)rows * LDN * E * 2            // sB, sC
            + (size_t)N * (rows + PAD) * E        // sBt
            + (size_t)P * (rows + PAD) * E        // sXt
-           + (size_t)(N / 2) * 16;               // sEnd {cos, sin, phi, 0}
+           + (size_t)(N / 2) * 16;               // sEnd: {cos, sin} of pair pairs, then the angles
   }
   // masked score tile (S.M) shared by the consumer waves: rows = queries,
   // columns = keys
@@ -101,6 +101,8 @@ struct PcLds {
 template <typename IO, int N, int P>
 struct PcBuf {
   IO *sB, *sC, *sBt, *sXt;
+  // end rotations: float4 q = {cos, sin} of pairs 2q and 2q + 1 (q < N/4),
+  // then the N/2 angles as floats (float4 N/4 on)
   float4* sEnd;
 };
 struct PcCoef {
@@ -141,7 +143,10 @@ enum PcEpi : int {
 // BCN: B and C rows are RMS-normalised and scaled per channel (a.nbw, a.ncw,
 // a.neps) as the producers build the tiles; the pending B_prev of the entry
 // state likewise.
-template <typename IO, int N, int P, int EPI, bool BCN>
+// LGR >= 0 fixes log2 of the padded rank at compile time (0: rank 1; 2:
+// ranks 3 and 4), so the row -> (token, rank) arithmetic folds away; -1 takes
+// it from kp.
+template <typename IO, int N, int P, int EPI, bool BCN, int LGR>
 __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) {
   using L = PcLds<IO, N, P, BCN>;
   using Lim = PcLimits<IO, N, P>;
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   extern __shared__ __align__(16) char smem[];
 
   const PrefillArgs& a = kp.a;
-  const int Q = kp.Q, R = kp.R, lgR = kp.lgR, H = kp.heads;
+  const int Q = kp.Q, R = LGR == 0 ? 1 : kp.R, lgR = LGR >= 0 ? LGR : kp.lgR, H = kp.heads;
   const int RP = 1 << lgR;  // tile rows per token (R padded to a power of two)
   const int T = a.seqlen;
   const int mode = kp.mode;
@@ -566,9 +571,9 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           }
           if (ist[m] && !crole) {
             if (valid && t == te && (rho & (RP - 1)) == 0) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                bf.sEnd[4 * pg + j] = make_float4(cs4[j], sn4[j], ph[k][j], 0.f);
+              bf.sEnd[2 * pg] = make_float4(cs4[0], sn4[0], cs4[1], sn4[1]);
+              bf.sEnd[2 * pg + 1] = make_float4(cs4[2], sn4[2], cs4[3], sn4[3]);
+              bf.sEnd[N / 4 + pg] = make_float4(ph[k][0], ph[k][1], ph[k][2], ph[k][3]);
             }
           }
         }
@@ -1012,6 +1017,11 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         for (int u = 0; u < PBW; ++u) {
           const int pb = cw + kConsWaves * u;
           if (pb >= PB) continue;
+          // X^T rows p, K = keys in natural order: the B operand of the
+          // outputs' (S.M) product and of the state update
+          Frag<IO> Xs[KSM];
+#pragma unroll
+          for (int ks = 0; ks < KSM; ++ks) Xs[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
           if (has_y) {
             // carried-state operand: E^T rows p, K = n in the accumulator order
             Frag<IO> Hf[NS];
@@ -1022,9 +1032,6 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
                 Hf[ns].set(i4, Hreg[u][2 * ns][i4]);
                 Hf[ns].set(4 + i4, (2 * ns + 1 < NB) ? Hreg[u][(2 * ns + 1 < NB) ? 2 * ns + 1 : 0][i4] : 0.f);
               }
-            Frag<IO> Xf[KSM];  // K = keys in natural order, as the score rows below
-#pragma unroll
-            for (int ks = 0; ks < KSM; ++ks) Xf[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
             // every row block's products first, then the y stores: a store to
             // the output tile between them would keep the next block's LDS
             // reads (which the compiler cannot tell apart from it) from being
@@ -1064,7 +1071,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
               }
 #pragma unroll
               for (int ks = 0; ks < KSM; ++ks)
-                if (2 * ks <= rb) mma(acc, Xf[ks], SMf[ks]);
+                if (2 * ks <= rb) mma(acc, Xs[ks], SMf[ks]);
               yacc[rb] = acc;
             }
 #pragma unroll
@@ -1083,19 +1090,16 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           // state update and rotation into the next chunk's frame
           const float decE = expf(co.sMisc[0]);
           // all operands first (independent LDS reads), then the MFMA chains
-          Frag<IO> Xs[KSM];
           Frag<IO> Bs[NB][KSM];
           float2 r0[NB], r1[NB];
-#pragma unroll
-          for (int ks = 0; ks < KSM; ++ks) Xs[ks].load8(bf.sXt + (16 * pb + c) * ldr + 32 * ks + 8 * g);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
             for (int ks = 0; ks < KSM; ++ks) Bs[nb][ks].load8(bf.sBt + (16 * nb + c) * ldr + 32 * ks + 8 * g);
-            const float4 e0 = bf.sEnd[8 * nb + 2 * g];
-            const float4 e1 = bf.sEnd[8 * nb + 2 * g + 1];
-            r0[nb] = make_float2(e0.x, e0.y);
-            r1[nb] = make_float2(e1.x, e1.y);
+            // this lane's pairs 8 nb + 2 g and 8 nb + 2 g + 1: one 16-byte read
+            const float4 e = bf.sEnd[4 * nb + g];
+            r0[nb] = make_float2(e.x, e.y);
+            r1[nb] = make_float2(e.z, e.w);
           }
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
@@ -1118,7 +1122,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
         if (mode == kPcSummary) {
           const int ct = tid - kProdThreads;
           if (ct < N / 2) {
-            const float tot = reduce_angle(sSeg[ct] + bf.sEnd[ct].z);
+            const float tot = reduce_angle(sSeg[ct] + reinterpret_cast<const float*>(bf.sEnd + N / 4)[ct]);
             sSeg[ct] = tot;
             if (last_chunk) a.seg_angle[((size_t)seg * kp.batch * H + chain) * (N / 2) + ct] = tot;
           }
@@ -1149,6 +1153,19 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   }
 }
 
+template <typename IO, int N, int P, int EPI, bool BCN, int LGR>
+hipError_t launch_pc_k(const PcParams& kp, size_t lds, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI, BCN, LGR>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI, BCN, LGR>), dim3(kp.nblocks), dim3(kPcThreads), lds, st, kp);
+  return hipGetLastError();
+}
+
 template <typename IO, int N, int P, int EPI, bool BCN>
 hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int mode, int nblocks) {
   // instances whose tiles fit at no height are never launched (the host
@@ -1158,13 +1175,6 @@ hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int 
   } else {
     const size_t lds = PcLds<IO, N, P, BCN>::bytes(PcLimits<IO, N, P>::kMaxRows);
     if (lds > 160 * 1024) return hipErrorInvalidValue;  // (the host checks this first)
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI, BCN>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
     PcParams kp;
     kp.a = a;
     kp.batch = d.batch;
@@ -1174,8 +1184,17 @@ hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int 
     kp.Q = d.Q;
     kp.mode = mode;
     kp.nblocks = nblocks;
-    hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI, BCN>), dim3(nblocks), dim3(kPcThreads), lds, st, kp);
-    return hipGetLastError();
+    // bf16 I/O: ranks 3-4 have an instance of their own, and so does rank 1
+    // in the segment passes.  Measured against the instance that takes the
+    // rank from kp: MIMO R = 4 prefill 0.689 -> 0.594 ms; the 16K-token
+    // SISO path (segment passes) 0.2745 -> 0.267 ms; but the fused SISO
+    // pass 0.2787 -> 0.284 ms (with the compile-time rank in either role),
+    // so the fused pass of rank 1 keeps the general instance.
+    if constexpr (sizeof(IO) == 2) {
+      if (kp.lgR == 0 && mode != kPcFused) return launch_pc_k<IO, N, P, EPI, BCN, 0>(kp, lds, st);
+      if (kp.lgR == 2) return launch_pc_k<IO, N, P, EPI, BCN, 2>(kp, lds, st);
+    }
+    return launch_pc_k<IO, N, P, EPI, BCN, -1>(kp, lds, st);
   }
 }
 
