@@ -342,8 +342,9 @@ __device__ __forceinline__ void rank_sum4(float (&v)[4], int rs) {
 // ============================ local ============================
 // Two workgroups per unit: which = 0 forms U_u from x and B (and stores the
 // unit's end decay and angle), which = 1 forms V_u from dy and C.
-template <typename IO, int PB, int NB>
-__global__ __launch_bounds__(kBT) void local_kernel(BackwardArgs a, BwdWs ws, int H, int rs, int nu) {
+template <typename IO, int PB, int NB, int RS>
+__global__ __launch_bounds__(kBT) void local_kernel(BackwardArgs a, BwdWs ws, int H, int nu) {
+  constexpr int rs = RS;  // log2 of the rank (1, 2, 4 -> 0, 1, 2)
   constexpr int P = 16 * PB, N = 16 * NB, NH = N / 2, LDX = P + 4, LDB = N + 4, LDPH = NH + 1;
   extern __shared__ __align__(16) float sm[];
   const int R = 1 << rs, Qu = kU >> rs;
@@ -481,8 +482,9 @@ struct ColsIn {
   }
 };
 
-template <int PB, int NB>
-__global__ __launch_bounds__(kBT) void local_bf_kernel(BackwardArgs a, BwdWs ws, int H, int rs, int nu) {
+template <int PB, int NB, int RS>
+__global__ __launch_bounds__(kBT) void local_bf_kernel(BackwardArgs a, BwdWs ws, int H, int nu) {
+  constexpr int rs = RS;  // log2 of the rank
   constexpr int P = 16 * PB, N = 16 * NB, NH = N / 2, LDPH = NH + 1;
   using XC = ColsIn<P>;
   using BC = ColsIn<N>;
@@ -1116,8 +1118,9 @@ __device__ __forceinline__ void grad_body(const BackwardArgs& a, const float* Eg
 
 // One workgroup per CU (its LDS), one wave per SIMD: the whole register file
 // is this wave's.
-template <typename IO, int PB, int NB>
-__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) void grad_kernel(BackwardArgs a, BwdWs ws, int H, int rs, int nu) {
+template <typename IO, int PB, int NB, int RS>
+__global__ __launch_bounds__(kBT) __attribute__((amdgpu_waves_per_eu(1, 1))) void grad_kernel(BackwardArgs a, BwdWs ws, int H, int nu) {
+  constexpr int rs = RS;  // log2 of the rank
   constexpr int P = 16 * PB, N = 16 * NB, NH = N / 2, LDX = P + 4, LDB = N + 4, LDPH = NH + 1;
   extern __shared__ __align__(16) float sm[];
   const int R = 1 << rs;
@@ -1326,23 +1329,24 @@ __global__ __launch_bounds__(256) void finish_kernel(BackwardArgs a, BwdWs ws, i
 }
 
 // The unit kernels of one (P / 16, N / 16), then scan and finish.
-template <typename IO, int PB, int NB>
-hipError_t launch_io_pn(const Dims& d, const BackwardArgs& a, const BwdWs& w, hipStream_t s) {
+// The local and grad kernels are compiled per rank (1, 2, 4: RS = 0, 1, 2),
+// so their row -> (token, rank) arithmetic folds away.
+template <typename IO, int PB, int NB, int RS>
+hipError_t launch_io_pnr(const Dims& d, const BackwardArgs& a, const BwdWs& w, hipStream_t s) {
   constexpr int P = 16 * PB, N = 16 * NB;
   static bool attr_set = false;
   if (!attr_set) {
     const void* local;
     if constexpr (sizeof(IO) == 2)
-      local = reinterpret_cast<const void*>(&local_bf_kernel<PB, NB>);
+      local = reinterpret_cast<const void*>(&local_bf_kernel<PB, NB, RS>);
     else
-      local = reinterpret_cast<const void*>(&local_kernel<IO, PB, NB>);
-    for (const void* f : {local, reinterpret_cast<const void*>(&grad_kernel<IO, PB, NB>)}) {
+      local = reinterpret_cast<const void*>(&local_kernel<IO, PB, NB, RS>);
+    for (const void* f : {local, reinterpret_cast<const void*>(&grad_kernel<IO, PB, NB, RS>)}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
     }
     attr_set = true;
   }
-  const int rs = d.R == 1 ? 0 : d.R == 2 ? 1 : 2;
   const int chains = d.batch * d.heads;
   const int nu = (a.seqlen + kU / d.R - 1) / (kU / d.R);
   const int bpc = (P * N / 8 + kScanT - 1) / kScanT;
@@ -1351,14 +1355,24 @@ hipError_t launch_io_pn(const Dims& d, const BackwardArgs& a, const BwdWs& w, hi
   const dim3 units((unsigned)chains * nu), blk(kBT);
   if constexpr (sizeof(IO) == 2) {
     const size_t lds_bf = (size_t)(P + 3 * N) * 128 + (size_t)((kU / d.R) * (N / 2 + 1) + kSmall) * 4;
-    hipLaunchKernelGGL((local_bf_kernel<PB, NB>), dim3(2 * units.x), blk, lds_bf, s, a, w, d.heads, rs, nu);
+    hipLaunchKernelGGL((local_bf_kernel<PB, NB, RS>), dim3(2 * units.x), blk, lds_bf, s, a, w, d.heads, nu);
   } else {
-    hipLaunchKernelGGL((local_kernel<IO, PB, NB>), dim3(2 * units.x), blk, lds_local, s, a, w, d.heads, rs, nu);
+    hipLaunchKernelGGL((local_kernel<IO, PB, NB, RS>), dim3(2 * units.x), blk, lds_local, s, a, w, d.heads, nu);
   }
   hipLaunchKernelGGL(scan_kernel<IO>, dim3(chains * bpc), dim3(kScanT), 0, s, a, w, d.heads, P, N, d.R, nu, bpc);
-  hipLaunchKernelGGL((grad_kernel<IO, PB, NB>), units, blk, lds_grad, s, a, w, d.heads, rs, nu);
+  hipLaunchKernelGGL((grad_kernel<IO, PB, NB, RS>), units, blk, lds_grad, s, a, w, d.heads, nu);
   hipLaunchKernelGGL(finish_kernel<IO>, dim3(chains), dim3(256), 0, s, a, w, d.heads, P, N, d.R, nu);
   return hipGetLastError();
+}
+
+template <typename IO, int PB, int NB>
+hipError_t launch_io_pn(const Dims& d, const BackwardArgs& a, const BwdWs& w, hipStream_t s) {
+  switch (d.R) {  // (the host accepts ranks 1, 2 and 4 only)
+    case 1: return launch_io_pnr<IO, PB, NB, 0>(d, a, w, s);
+    case 2: return launch_io_pnr<IO, PB, NB, 1>(d, a, w, s);
+    case 4: return launch_io_pnr<IO, PB, NB, 2>(d, a, w, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Dispatch over the supported tile counts (P, N in {16, 32, 64, 128}, P N <= 8192).
