@@ -1184,15 +1184,18 @@ hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int 
     kp.Q = d.Q;
     kp.mode = mode;
     kp.nblocks = nblocks;
-    // bf16 I/O: ranks 3-4 have an instance of their own, and so does rank 1
-    // in the segment passes.  Measured against the instance that takes the
-    // rank from kp: MIMO R = 4 prefill 0.689 -> 0.594 ms; the 16K-token
-    // SISO path (segment passes) 0.2745 -> 0.267 ms; but the fused SISO
-    // pass 0.2787 -> 0.284 ms (with the compile-time rank in either role),
-    // so the fused pass of rank 1 keeps the general instance.
+    // Instances with the rank fixed at compile time, where they measured
+    // faster than the one that takes it from kp (A/B on one box): bf16 ranks
+    // 3-4 (MIMO R = 4 prefill 0.689 -> 0.594 ms); bf16 rank 1 in the segment
+    // passes (16K-token SISO path 0.2745 -> 0.267 ms) and with the BC
+    // normalisation (0.336 -> 0.318 ms); fp32 rank 1 (0.881 -> 0.828 ms).
+    // The fused bf16 rank-1 pass without the BC normalisation keeps the
+    // general instance: 0.2787 -> 0.284 ms plain, 0.313 -> 0.317 gated.
     if constexpr (sizeof(IO) == 2) {
-      if (kp.lgR == 0 && mode != kPcFused) return launch_pc_k<IO, N, P, EPI, BCN, 0>(kp, lds, st);
+      if (kp.lgR == 0 && (mode != kPcFused || BCN)) return launch_pc_k<IO, N, P, EPI, BCN, 0>(kp, lds, st);
       if (kp.lgR == 2) return launch_pc_k<IO, N, P, EPI, BCN, 2>(kp, lds, st);
+    } else {
+      if (kp.lgR == 0) return launch_pc_k<IO, N, P, EPI, BCN, 0>(kp, lds, st);
     }
     return launch_pc_k<IO, N, P, EPI, BCN, -1>(kp, lds, st);
   }
