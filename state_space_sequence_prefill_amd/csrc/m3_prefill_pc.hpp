@@ -148,7 +148,8 @@ enum PcEpi : int {
 // largest that fits (kMaxRows rows, kMaxRows >> LGR tokens; such an instance
 // is launched only for calls at that height), so the row -> (token, rank)
 // arithmetic and the chunk-sized bounds fold away.  -1 takes both from kp.
-template <typename IO, int N, int P, int EPI, bool BCN, int LGR>
+// SUMM fixes the segment-summary mode: no C loads, scores, outputs or y.
+template <typename IO, int N, int P, int EPI, bool BCN, int LGR, bool SUMM = false>
 __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) {
   using L = PcLds<IO, N, P, BCN>;
   using Lim = PcLimits<IO, N, P>;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   const int R = LGR == 0 ? 1 : kp.R, lgR = LGR >= 0 ? LGR : kp.lgR, H = kp.heads;
   const int RP = 1 << lgR;  // tile rows per token (R padded to a power of two)
   const int T = a.seqlen;
-  const int mode = kp.mode;
+  const int mode = SUMM ? (int)kPcSummary : kp.mode;
   const int nseg_grid = (mode == kPcFused) ? 1 : (mode == kPcSummary ? a.nseg - 1 : a.nseg);
   const int bid = pc_remap_block(blockIdx.x, kp.nblocks);
   const int chain = bid / nseg_grid;
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
             rs.b[m][k].load((crole ? Cc : Bc) + o);  // this role's matrix
           } else {
             rs.b[m][k].load(Bc + o);
-            rs.c[m][k].load(Cc + o);
+            if constexpr (!SUMM) rs.c[m][k].load(Cc + o);  // (a summary reads no C)
           }
         }
 #pragma unroll
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
           for (int k = 0; k < 4; ++k) {
             pb[k] = lane_group_sum_upto<kGWMax>(rs.b[m][k].sumsq(), GW);
             // (a segment summary holds B in the C registers and uses no C sums)
-            pc[k] = kSplit ? 0.f : lane_group_sum_upto<kGWMax>(rs.c[m][k].sumsq(), GW);
+            pc[k] = (kSplit || SUMM) ? 0.f : lane_group_sum_upto<kGWMax>(rs.c[m][k].sumsq(), GW);
           }
           if (kSplit && ist[m] && (lane & (GW - 1)) == 0) {  // this role's matrix only
             const int grp = ipg[m] / GW + (crole ? NG : 0);
@@ -1156,16 +1157,18 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   }
 }
 
-template <typename IO, int N, int P, int EPI, bool BCN, int LGR>
+template <typename IO, int N, int P, int EPI, bool BCN, int LGR, bool SUMM = false>
 hipError_t launch_pc_k(const PcParams& kp, size_t lds, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI, BCN, LGR>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<IO, N, P, EPI, BCN, LGR, SUMM>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI, BCN, LGR>), dim3(kp.nblocks), dim3(kPcThreads), lds, st, kp);
+  hipLaunchKernelGGL((prefill_pc_kernel<IO, N, P, EPI, BCN, LGR, SUMM>), dim3(kp.nblocks), dim3(kPcThreads), lds, st,
+                     kp);
   return hipGetLastError();
 }
 
@@ -1199,6 +1202,13 @@ hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int 
     // general instance: 0.2787 -> 0.284 ms plain, 0.313 -> 0.317 gated, and
     // 0.280 -> 0.286 ms with only the tile height fixed.
     const bool full = EPI != kEpiPlain || kp.Q == (PcLimits<IO, N, P>::kMaxRows >> kp.lgR);
+    // segment summaries (always the plain output) in instances of their own
+    if constexpr (EPI == kEpiPlain) {
+      if (mode == kPcSummary && full && kp.lgR == 0) return launch_pc_k<IO, N, P, EPI, BCN, 0, true>(kp, lds, st);
+      if constexpr (sizeof(IO) == 2) {
+        if (mode == kPcSummary && full && kp.lgR == 2) return launch_pc_k<IO, N, P, EPI, BCN, 2, true>(kp, lds, st);
+      }
+    }
     if constexpr (sizeof(IO) == 2) {
       if (full && kp.lgR == 0 && (mode != kPcFused || BCN)) return launch_pc_k<IO, N, P, EPI, BCN, 0>(kp, lds, st);
       if (full && kp.lgR == 2) return launch_pc_k<IO, N, P, EPI, BCN, 2>(kp, lds, st);
