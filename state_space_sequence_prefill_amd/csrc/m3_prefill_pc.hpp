@@ -144,8 +144,8 @@ enum PcEpi : int {
 // a.neps) as the producers build the tiles; the pending B_prev of the entry
 // state likewise.
 // LGR >= 0 fixes log2 of the padded rank at compile time (0: rank 1; 2:
-// ranks 3 and 4), and with the plain output also the tile height at the
-// largest that fits (kMaxRows rows, kMaxRows >> LGR tokens; such an instance
+// ranks 3 and 4), and except with the gated per-rank epilogue also the tile
+// height at the largest that fits (kMaxRows rows, kMaxRows >> LGR tokens; such an instance
 // is launched only for calls at that height), so the row -> (token, rank)
 // arithmetic and the chunk-sized bounds fold away.  -1 takes both from kp.
 // SUMM fixes the segment-summary mode: no C loads, scores, outputs or y.
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kPcThreads, 1) void prefill_pc_kernel(PcParams kp) 
   extern __shared__ __align__(16) char smem[];
 
   const PrefillArgs& a = kp.a;
-  const int Q = (LGR >= 0 && EPI == kEpiPlain) ? (Lim::kMaxRows > 0 ? Lim::kMaxRows : 32) >> LGR : kp.Q;
+  const int Q = (LGR >= 0 && EPI != kEpiGate) ? (Lim::kMaxRows > 0 ? Lim::kMaxRows : 32) >> LGR : kp.Q;
   const int R = LGR == 0 ? 1 : kp.R, lgR = LGR >= 0 ? LGR : kp.lgR, H = kp.heads;
   const int RP = 1 << lgR;  // tile rows per token (R padded to a power of two)
   const int T = a.seqlen;
@@ -1190,18 +1190,19 @@ hipError_t launch_pc_t(const Dims& d, const PrefillArgs& a, hipStream_t st, int 
     kp.Q = d.Q;
     kp.mode = mode;
     kp.nblocks = nblocks;
-    // Instances with the rank (and, plain output, the tile height) fixed at
-    // compile time, where they measured faster than the one that takes both
-    // from kp (A/B on one box; the second figure adds the fixed tile height):
-    // bf16 ranks 3-4 (MIMO R = 4 prefill 0.689 -> 0.594 -> 0.573 ms, with the
-    // BC normalisation 0.861 -> 0.739 -> 0.621 ms, gated 0.830 -> 0.713 ms
-    // but 0.739 ms with the fixed height); bf16 rank 1 in the segment passes
+    // Instances with the rank (and, but for the gated per-rank epilogue, the
+    // tile height) fixed at compile time, where they measured faster than the
+    // one that takes both from kp (A/B on one box; the second figure adds the
+    // fixed tile height): bf16 ranks 3-4 (MIMO R = 4 prefill 0.689 -> 0.594
+    // -> 0.573 ms, with the BC normalisation 0.861 -> 0.739 -> 0.621 ms,
+    // down-projected and gated 0.850 -> 0.700 -> 0.665 ms, gated 0.830 ->
+    // 0.713 ms but 0.739 ms with the fixed height); bf16 rank 1 in the segment passes
     // (16K-token SISO path 0.2745 -> 0.267 ms) and with the BC normalisation
     // (0.336 -> 0.318 -> 0.301 ms); fp32 rank 1 (0.881 -> 0.828 -> 0.810 ms).
     // The fused bf16 rank-1 pass without the BC normalisation keeps the
     // general instance: 0.2787 -> 0.284 ms plain, 0.313 -> 0.317 gated, and
     // 0.280 -> 0.286 ms with only the tile height fixed.
-    const bool full = EPI != kEpiPlain || kp.Q == (PcLimits<IO, N, P>::kMaxRows >> kp.lgR);
+    const bool full = EPI == kEpiGate || kp.Q == (PcLimits<IO, N, P>::kMaxRows >> kp.lgR);
     // segment summaries (always the plain output) in instances of their own
     if constexpr (EPI == kEpiPlain) {
       if (mode == kPcSummary && full && kp.lgR == 0) return launch_pc_k<IO, N, P, EPI, BCN, 0, true>(kp, lds, st);
